@@ -1,0 +1,56 @@
+"""Plant plausible mistakes in a copy of the oracle (on the CPU) and show that
+at least one pin catches each.  The real oracle is never modified."""
+import os
+import types
+
+import pytest
+
+from tests import oracle_pins
+
+SRC_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle", "lora_oracle.py")
+
+# (description, text in the oracle, replacement)
+MUTATIONS = [
+    ("adapter term dropped", "Y = Z @ W.T + s * (T @ B.T)", "Y = Z @ W.T"),
+    ("scale applied twice", "Y = Z @ W.T + s * (T @ B.T)", "Y = Z @ W.T + s * s * (T @ B.T)"),
+    ("side product uses W", "T = Z @ A.T\n    Y", "T = Z @ W[: A.shape[0]].T\n    Y"),
+    ("dT missing scale", "dT = s * (dY @ B)", "dT = dY @ B"),
+    ("dB missing scale", "dB = s * (dY.T @ T)", "dB = dY.T @ T"),
+    ("dA halved", "dA = dT.T @ Z", "dA = dT.T @ Z * 0.5"),
+    ("dA drops dT", "dA = dT.T @ Z", "dA = (dY @ B).T @ Z"),
+    ("dZ drops adapter", "dZ = dY @ W + dT @ A", "dZ = dY @ W"),
+    ("silu' drops term", "return sg * (1.0 + g * (1.0 - sg))", "return sg"),
+    ("silu is sigmoid", "return g * _sigmoid(g)", "return _sigmoid(g)"),
+    ("gelu_tanh cubic sign", "(g + _GELU_CUBIC * g ** 3)))", "(g - _GELU_CUBIC * g ** 3)))"),
+    ("gelu_tanh' drops 1-t^2", "0.5 * g * (1.0 - t * t) * _SQRT_2_OVER_PI", "0.5 * g * _SQRT_2_OVER_PI"),
+    ("GLU backward drops U", "dG = dH * f[\"U\"] * dphi(f[\"G\"])", "dG = dH * dphi(f[\"G\"])"),
+    ("GLU backward swaps phi", "dU = dH * phi(f[\"G\"])", "dU = dH * dphi(f[\"G\"])"),
+    ("dX drops up branch", "return {\"dX\": dXg + dXu,", "return {\"dX\": dXg,"),
+    ("rope frequency exponent", "inv_freq = theta ** (-2.0 * j / head_dim)", "inv_freq = theta ** (-1.0 * j / head_dim)"),
+    ("rope sign", "x1 * c - x2 * s, x2 * c + x1 * s", "x1 * c + x2 * s, x2 * c - x1 * s"),
+    ("rope adjacent pairs", "x1, x2 = x[..., :h], x[..., h:]", "x1, x2 = x[..., 0::2], x[..., 1::2]"),
+    ("rope transpose not inverted", "y1 * c + y2 * s, y2 * c - y1 * s", "y1 * c - y2 * s, y2 * c + y1 * s"),
+    ("head split order", ".transpose(0, 2, 1, 3).copy()\n\n\ndef head_unsplit", ".transpose(0, 2, 1, 3)[:, ::-1].copy()\n\n\ndef head_unsplit"),
+    ("rope on V", "if name != \"v\":\n            Z = rope_rotate", "if True:\n            Z = rope_rotate"),
+    ("no RoPE adjoint in backward", "grads = {\"q\": rope_rotate_transpose(dQ, ang)", "grads = {\"q\": dQ"),
+]
+
+
+def _mutant(old, new):
+    src = open(SRC_PATH).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    mod = types.ModuleType("lora_oracle_mutant")
+    exec(compile(src.replace(old, new), "lora_oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("desc,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(desc, old, new):
+    mod = _mutant(old, new)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(mod)
+        except Exception:  # an assertion or a shape error both count as caught
+            caught.append(check.__name__)
+    assert caught, f"no pin caught: {desc}"
