@@ -1,0 +1,262 @@
+"""Thin ctypes binding over the C ABI in include/lora_mi355x.h.
+
+Argument marshalling only: tensors become device pointers, the stream becomes
+the current torch stream's hipStream_t, status codes become exceptions.  Every
+step of the computation runs in the HIP library; there is no fallback.  If the
+library has not been built, loading fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
+
+LORA_F32, LORA_BF16 = 0, 1
+LORA_SWIGLU, LORA_GEGLU_TANH = 0, 1
+LORA_MAX_RANK = 16
+DTYPE_CODES = {"f32": LORA_F32, "bf16": LORA_BF16, torch.float32: LORA_F32, torch.bfloat16: LORA_BF16}
+ACT_CODES = {"swiglu": LORA_SWIGLU, "geglu_tanh": LORA_GEGLU_TANH}
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"status {status}: {message}")
+        self.status = status
+
+
+class MlpDesc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("hidden", ctypes.c_int32), ("inter", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("act", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class QkvDesc(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("seq", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_q", ctypes.c_int32), ("n_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double)]
+
+
+class Proj(ctypes.Structure):
+    _fields_ = [("W", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("scale", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "lora_mlp_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MlpDesc), ctypes.c_int]),
+    "lora_qkv_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(QkvDesc), ctypes.c_int]),
+    "lora_mlp_fwd": (ctypes.c_int, [ctypes.POINTER(MlpDesc), _P, ctypes.POINTER(Proj), ctypes.POINTER(Proj),
+                                    ctypes.POINTER(Proj), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "lora_mlp_bwd": (ctypes.c_int, [ctypes.POINTER(MlpDesc), _P, _P, _P, _P, _P, ctypes.POINTER(Proj),
+                                    ctypes.POINTER(Proj), ctypes.POINTER(Proj), _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
+    "lora_qkv_fwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, ctypes.POINTER(Proj), ctypes.POINTER(Proj),
+                                    ctypes.POINTER(Proj), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "lora_qkv_bwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, _P, _P, _P, _P, ctypes.POINTER(Proj),
+                                    ctypes.POINTER(Proj), ctypes.POINTER(Proj), _P, _P, _P, _P, _P, _P, _P, _P,
+                                    ctypes.c_size_t, _P]),
+    "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "lora_last_error_message": (ctypes.c_char_p, []),
+    "lora_version": (ctypes.c_char_p, []),
+    "lora_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "lora_timing_reset": (ctypes.c_int, []),
+    "lora_timing_query": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),
+                                         ctypes.POINTER(ctypes.c_int)]),
+    "lora_kernel_names": (ctypes.c_char_p, []),
+}
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise LoraError(status, lib().lora_last_error_message().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the LoRA library must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def proj(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, scale: float) -> Proj:
+    return Proj(_ptr(W), _ptr(A), _ptr(B), float(scale))
+
+
+def mlp_desc(n_tokens, hidden, inter, rank, dtype, act) -> MlpDesc:
+    return MlpDesc(int(n_tokens), int(hidden), int(inter), int(rank), DTYPE_CODES[dtype], ACT_CODES.get(act, act), 0)
+
+
+def qkv_desc(batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta) -> QkvDesc:
+    return QkvDesc(int(batch), int(seq), int(hidden), int(n_q), int(n_kv), int(head_dim), int(rank),
+                   DTYPE_CODES[dtype], float(theta))
+
+
+# ---- raw entry points (same names as the C ABI) ------------------------------
+
+def lora_mlp_workspace_bytes(desc: MlpDesc, pass_: int) -> int:
+    return int(lib().lora_mlp_workspace_bytes(ctypes.byref(desc), int(pass_)))
+
+
+def lora_qkv_workspace_bytes(desc: QkvDesc, pass_: int) -> int:
+    return int(lib().lora_qkv_workspace_bytes(ctypes.byref(desc), int(pass_)))
+
+
+def lora_mlp_fwd(desc, X, gate: Proj, up: Proj, down: Proj, Y, G, U, T, workspace, stream=None):
+    _check(lib().lora_mlp_fwd(ctypes.byref(desc), _ptr(X), ctypes.byref(gate), ctypes.byref(up), ctypes.byref(down),
+                              _ptr(Y), _ptr(G), _ptr(U), _ptr(T), _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+
+
+def lora_mlp_bwd(desc, dY, X, G, U, T, gate: Proj, up: Proj, down: Proj, dX, dA_gate, dB_gate, dA_up, dB_up,
+                 dA_down, dB_down, workspace, stream=None):
+    _check(lib().lora_mlp_bwd(ctypes.byref(desc), _ptr(dY), _ptr(X), _ptr(G), _ptr(U), _ptr(T), ctypes.byref(gate),
+                              ctypes.byref(up), ctypes.byref(down), _ptr(dX), _ptr(dA_gate), _ptr(dB_gate),
+                              _ptr(dA_up), _ptr(dB_up), _ptr(dA_down), _ptr(dB_down), _ptr(workspace),
+                              workspace.numel(), _stream(stream)))
+
+
+def lora_qkv_fwd(desc, X, q: Proj, k: Proj, v: Proj, Q, K, V, T, workspace, stream=None):
+    _check(lib().lora_qkv_fwd(ctypes.byref(desc), _ptr(X), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                              _ptr(Q), _ptr(K), _ptr(V), _ptr(T), _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+
+
+def lora_qkv_bwd(desc, dQ, dK, dV, X, T, q: Proj, k: Proj, v: Proj, dX, dA_q, dB_q, dA_k, dB_k, dA_v, dB_v,
+                 workspace, stream=None):
+    _check(lib().lora_qkv_bwd(ctypes.byref(desc), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(X), _ptr(T), ctypes.byref(q),
+                              ctypes.byref(k), ctypes.byref(v), _ptr(dX), _ptr(dA_q), _ptr(dB_q), _ptr(dA_k),
+                              _ptr(dB_k), _ptr(dA_v), _ptr(dB_v), _ptr(workspace), workspace.numel(),
+                              _stream(stream)))
+
+
+# ---- timing -------------------------------------------------------------------
+
+def timing_enable(on: bool = True) -> None:
+    _check(lib().lora_timing_enable(1 if on else 0))
+
+
+def timing_reset() -> None:
+    _check(lib().lora_timing_reset())
+
+
+def timing_query(kernel: str):
+    """(total milliseconds, launches) of one kernel since the last reset."""
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    _check(lib().lora_timing_query(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def kernel_names():
+    return lib().lora_kernel_names().decode().split(",")
+
+
+# ---- plumbing: allocate outputs / workspace with torch, then call the ABI -----
+
+class MLP:
+    """LoRA MLP weights on the device plus the buffers one fwd+bwd needs."""
+
+    def __init__(self, t: Dict[str, torch.Tensor], n_tokens, hidden, inter, rank, dtype, act,
+                 scales=(2.0, 2.0, 2.0)):
+        self.t = t
+        self.desc = mlp_desc(n_tokens, hidden, inter, rank, dtype, act)
+        self.dtype = t["X"].dtype
+        dev = t["X"].device
+        self.N, self.h, self.i, self.r = int(n_tokens), int(hidden), int(inter), int(rank)
+        self.gate = proj(t["W_gate"], t["A_gate"], t["B_gate"], scales[0])
+        self.up = proj(t["W_up"], t["A_up"], t["B_up"], scales[1])
+        self.down = proj(t["W_down"], t["A_down"], t["B_down"], scales[2])
+        e = dict(device=dev, dtype=self.dtype)
+        self.Y = torch.empty(self.N, self.h, **e)
+        self.G = torch.empty(self.N, self.i, **e)
+        self.U = torch.empty(self.N, self.i, **e)
+        self.T = torch.empty(3, self.N, self.r, device=dev, dtype=torch.float32)
+        self.dX = torch.empty(self.N, self.h, **e)
+        self.grads = {
+            "dA_gate": torch.empty(self.r, self.h, **e), "dB_gate": torch.empty(self.i, self.r, **e),
+            "dA_up": torch.empty(self.r, self.h, **e), "dB_up": torch.empty(self.i, self.r, **e),
+            "dA_down": torch.empty(self.r, self.i, **e), "dB_down": torch.empty(self.h, self.r, **e),
+        }
+        self.ws_fwd = torch.empty(max(1, lora_mlp_workspace_bytes(self.desc, 0)), device=dev, dtype=torch.uint8)
+        self.ws_bwd = torch.empty(max(1, lora_mlp_workspace_bytes(self.desc, 1)), device=dev, dtype=torch.uint8)
+
+    def forward(self, stream=None):
+        lora_mlp_fwd(self.desc, self.t["X"], self.gate, self.up, self.down, self.Y, self.G, self.U, self.T,
+                     self.ws_fwd, stream)
+        return self.Y
+
+    def backward(self, dY, stream=None):
+        g = self.grads
+        lora_mlp_bwd(self.desc, dY, self.t["X"], self.G, self.U, self.T, self.gate, self.up, self.down, self.dX,
+                     g["dA_gate"], g["dB_gate"], g["dA_up"], g["dB_up"], g["dA_down"], g["dB_down"], self.ws_bwd,
+                     stream)
+        return self.dX
+
+
+class QKV:
+    """LoRA QKV weights on the device plus the buffers one fwd+bwd needs."""
+
+    def __init__(self, t: Dict[str, torch.Tensor], batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta,
+                 scales=(2.0, 2.0, 2.0)):
+        self.t = t
+        self.desc = qkv_desc(batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta)
+        self.dtype = t["X"].dtype
+        dev = t["X"].device
+        self.B, self.S, self.h, self.r, self.d = int(batch), int(seq), int(hidden), int(rank), int(head_dim)
+        self.nq, self.nkv = int(n_q), int(n_kv)
+        N = self.B * self.S
+        self.q = proj(t["W_q"], t["A_q"], t["B_q"], scales[0])
+        self.k = proj(t["W_k"], t["A_k"], t["B_k"], scales[1])
+        self.v = proj(t["W_v"], t["A_v"], t["B_v"], scales[2])
+        e = dict(device=dev, dtype=self.dtype)
+        self.Q = torch.empty(self.B, self.nq, self.S, self.d, **e)
+        self.K = torch.empty(self.B, self.nkv, self.S, self.d, **e)
+        self.V = torch.empty(self.B, self.nkv, self.S, self.d, **e)
+        self.T = torch.empty(3, N, self.r, device=dev, dtype=torch.float32)
+        self.dX = torch.empty(N, self.h, **e)
+        Oq, Ok = self.nq * self.d, self.nkv * self.d
+        self.grads = {
+            "dA_q": torch.empty(self.r, self.h, **e), "dB_q": torch.empty(Oq, self.r, **e),
+            "dA_k": torch.empty(self.r, self.h, **e), "dB_k": torch.empty(Ok, self.r, **e),
+            "dA_v": torch.empty(self.r, self.h, **e), "dB_v": torch.empty(Ok, self.r, **e),
+        }
+        self.ws_fwd = torch.empty(max(1, lora_qkv_workspace_bytes(self.desc, 0)), device=dev, dtype=torch.uint8)
+        self.ws_bwd = torch.empty(max(1, lora_qkv_workspace_bytes(self.desc, 1)), device=dev, dtype=torch.uint8)
+
+    def forward(self, stream=None):
+        lora_qkv_fwd(self.desc, self.t["X"], self.q, self.k, self.v, self.Q, self.K, self.V, self.T, self.ws_fwd,
+                     stream)
+        return self.Q, self.K, self.V
+
+    def backward(self, dQ, dK, dV, stream=None):
+        g = self.grads
+        lora_qkv_bwd(self.desc, dQ, dK, dV, self.t["X"], self.T, self.q, self.k, self.v, self.dX, g["dA_q"],
+                     g["dB_q"], g["dA_k"], g["dB_k"], g["dA_v"], g["dB_v"], self.ws_bwd, stream)
+        return self.dX

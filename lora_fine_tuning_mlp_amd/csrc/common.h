@@ -1,0 +1,247 @@
+// Device-side building blocks shared by every kernel of the LoRA library
+// (gfx950 / CDNA4, wave64).
+//
+// Tiles live in LDS as rows of 128 bytes (64 bf16 or 32 fp32 along K), split
+// into eight 16-byte chunks.  The chunk index is XOR-swizzled with
+// (row ^ row>>3) & 7 so that the 16 consecutive rows an MFMA fragment read
+// touches fall on distinct bank groups (both for 32- and 64-bank LDS).
+//
+// MFMA: v_mfma_f32_16x16x32_bf16 for bf16 and v_mfma_f32_16x16x4_f32 for
+// fp32.  A "fragment" is 8 consecutive K values of one row (A operand) or one
+// column (B operand) held by a lane: lane l covers row/column (l & 15) and K
+// slots 8*(l>>4) .. 8*(l>>4)+7.  Because A and B use the same slot <-> K map,
+// the products pair up correctly whatever order the hardware sums the slots
+// in.  The 16x16 fp32 result is held as C[4*(l>>4) + j][l & 15], j = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;       // 4 waves of 64
+constexpr int kBM = 256;            // tile rows (tokens)
+constexpr int kBN = 256;            // tile columns
+constexpr int kRowBytes = 128;      // one LDS tile row
+constexpr int kMaxSide = 3;         // adapters whose rank-r product a GEMM carries
+constexpr int kSlot = 16;           // K width reserved per adapter in a fold (rank <= 16)
+
+template <class T> struct ET;
+template <> struct ET<bf16> {
+  static constexpr int VEC = 8;     // elements per 16-byte chunk
+  static constexpr int BK = 64;     // K per LDS tile row
+  static constexpr int KSUB = 2;    // MFMA K-steps (32 each) per tile
+  static constexpr int BYTES = 2;
+};
+template <> struct ET<float> {
+  static constexpr int VEC = 4;
+  static constexpr int BK = 32;
+  static constexpr int KSUB = 1;
+  static constexpr int BYTES = 4;
+};
+
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int lds_off(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ swz(row)) << 4);
+}
+
+__device__ __forceinline__ u32x4 zero4() { u32x4 z = {0u, 0u, 0u, 0u}; return z; }
+
+// ---- bf16 <-> fp32 ---------------------------------------------------------
+__device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ unsigned pack_bf2(float lo, float hi) {
+  bf16x2 v;
+  v.x = (bf16)lo;   // round to nearest even (v_cvt_pk_bf16_f32)
+  v.y = (bf16)hi;
+  return __builtin_bit_cast(unsigned, v);
+}
+
+// A 16-byte chunk as VEC floats and back.
+__device__ __forceinline__ void unpack(u32x4 c, float (&v)[8]) {
+  v[0] = bf_lo(c.x); v[1] = bf_hi(c.x); v[2] = bf_lo(c.y); v[3] = bf_hi(c.y);
+  v[4] = bf_lo(c.z); v[5] = bf_hi(c.z); v[6] = bf_lo(c.w); v[7] = bf_hi(c.w);
+}
+__device__ __forceinline__ void unpack(u32x4 c, float (&v)[4]) {
+  v[0] = __uint_as_float(c.x); v[1] = __uint_as_float(c.y);
+  v[2] = __uint_as_float(c.z); v[3] = __uint_as_float(c.w);
+}
+__device__ __forceinline__ u32x4 pack(const float (&v)[8]) {
+  u32x4 c;
+  c.x = pack_bf2(v[0], v[1]); c.y = pack_bf2(v[2], v[3]);
+  c.z = pack_bf2(v[4], v[5]); c.w = pack_bf2(v[6], v[7]);
+  return c;
+}
+__device__ __forceinline__ u32x4 pack(const float (&v)[4]) {
+  u32x4 c;
+  c.x = __float_as_uint(v[0]); c.y = __float_as_uint(v[1]);
+  c.z = __float_as_uint(v[2]); c.w = __float_as_uint(v[3]);
+  return c;
+}
+
+template <class T> __device__ __forceinline__ float to_f(T x);
+template <> __device__ __forceinline__ float to_f<bf16>(bf16 x) { return (float)x; }
+template <> __device__ __forceinline__ float to_f<float>(float x) { return x; }
+template <class T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+
+// ---- global 16-byte chunk loads with bounds --------------------------------
+// Elements [k, k+VEC) of a row; zero past `len` or when row == nullptr.
+// `vec` means the row is 16-byte aligned and len % VEC == 0.
+template <class T>
+__device__ __forceinline__ u32x4 gload(const T* row, long k, long len, bool vec) {
+  constexpr int VEC = ET<T>::VEC;
+  if (row == nullptr || k >= len) return zero4();
+  if (vec) return *reinterpret_cast<const u32x4*>(row + k);
+  float v[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) v[e] = (k + e < len) ? to_f<T>(row[k + e]) : 0.0f;
+  return pack(v);
+}
+
+// Store `n` (<= VEC) leading elements of v at p (vector store when full and aligned).
+template <class T, int NV>
+__device__ __forceinline__ void gstore(T* p, const float (&v)[NV], int n, bool vec) {
+  if (n <= 0) return;
+  if (vec && n == NV) {
+    if constexpr (sizeof(T) * NV == 16) {
+      *reinterpret_cast<u32x4*>(p) = pack(v);
+      return;
+    } else if constexpr (sizeof(T) * NV == 8) {
+      u32x2 c;
+      if constexpr (sizeof(T) == 2) { c.x = pack_bf2(v[0], v[1]); c.y = pack_bf2(v[2], v[3]); }
+      else { c.x = __float_as_uint(v[0]); c.y = __float_as_uint(v[1]); }
+      *reinterpret_cast<u32x2*>(p) = c;
+      return;
+    } else if constexpr (sizeof(T) * NV == 4) {
+      if constexpr (sizeof(T) == 2) *reinterpret_cast<unsigned*>(p) = pack_bf2(v[0], v[1]);
+      else *reinterpret_cast<unsigned*>(p) = __float_as_uint(v[0]);
+      return;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < NV; ++e)
+    if (e < n) p[e] = from_f<T>(v[e]);
+}
+
+// ---- MFMA fragments ----------------------------------------------------------
+template <class T> struct Frag;
+template <> struct Frag<bf16> { u32x4 v; };
+template <> struct Frag<float> { u32x4 v0, v1; };
+
+__device__ __forceinline__ f32x4 mma(f32x4 c, const Frag<bf16>& a, const Frag<bf16>& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.v),
+                                                 __builtin_bit_cast(bf16x8, b.v), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma(f32x4 c, const Frag<float>& a, const Frag<float>& b) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v0.x), __uint_as_float(b.v0.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v0.y), __uint_as_float(b.v0.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v0.z), __uint_as_float(b.v0.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v0.w), __uint_as_float(b.v0.w), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.x), __uint_as_float(b.v1.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.y), __uint_as_float(b.v1.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.z), __uint_as_float(b.v1.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.w), __uint_as_float(b.v1.w), c, 0, 0, 0);
+  return c;
+}
+
+// Fragment of LDS tile row `row`, K-step ks, lane group g (= lane >> 4).
+template <class T> __device__ __forceinline__ Frag<T> lds_frag(const char* buf, int row, int ks, int g);
+template <> __device__ __forceinline__ Frag<bf16> lds_frag<bf16>(const char* buf, int row, int ks, int g) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const u32x4*>(buf + lds_off(row, ks * 4 + g));
+  return f;
+}
+template <> __device__ __forceinline__ Frag<float> lds_frag<float>(const char* buf, int row, int ks, int g) {
+  Frag<float> f;
+  f.v0 = *reinterpret_cast<const u32x4*>(buf + lds_off(row, 2 * g));
+  f.v1 = *reinterpret_cast<const u32x4*>(buf + lds_off(row, 2 * g + 1));
+  return f;
+}
+
+// Fragment built from 8 floats (slot order), e.g. from registers in C layout.
+template <class T> __device__ __forceinline__ Frag<T> make_frag(const float (&v)[8]);
+template <> __device__ __forceinline__ Frag<bf16> make_frag<bf16>(const float (&v)[8]) {
+  Frag<bf16> f; f.v = pack(v); return f;
+}
+template <> __device__ __forceinline__ Frag<float> make_frag<float>(const float (&v)[8]) {
+  Frag<float> f;
+  f.v0.x = __float_as_uint(v[0]); f.v0.y = __float_as_uint(v[1]);
+  f.v0.z = __float_as_uint(v[2]); f.v0.w = __float_as_uint(v[3]);
+  f.v1.x = __float_as_uint(v[4]); f.v1.y = __float_as_uint(v[5]);
+  f.v1.z = __float_as_uint(v[6]); f.v1.w = __float_as_uint(v[7]);
+  return f;
+}
+
+// ---- column permutation of a 128-column wave window ---------------------------
+// A wave owns 8 MFMA column blocks of 16.  Loading B rows into LDS in a
+// permuted order decides which output column each lane holds: with G groups,
+// lane c holds, in block b = gg*(8/G) + e, window column gg*(128/G) + c*(8/G) + e.
+// G = 1 gives every lane 8 consecutive columns (16-byte stores); G = 2 puts
+// columns w and w+64 in the same lane (GLU gate/up pairs, RoPE pairs for
+// head_dim 128); G = 4 pairs w and w+32 (RoPE, head_dim 64).
+__device__ __forceinline__ int perm_col(int lg, int c, int b) {   // lg = log2(G)
+  const int cw = 8 >> lg, gw = 128 >> lg;
+  return (b / cw) * gw + c * cw + (b % cw);
+}
+__device__ __forceinline__ int perm_row(int lg, int w) {
+  const int cw = 8 >> lg, gw = 128 >> lg;
+  const int gg = w / gw, rem = w % gw;
+  return ((gg * cw + rem % cw) << 4) + rem / cw;
+}
+
+// ---- activations (fp32) --------------------------------------------------------
+#define LORA_ACT_SWIGLU 0
+#define LORA_ACT_GEGLU_TANH 1
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+template <int ACT> __device__ __forceinline__ float act_fwd(float g) {
+  if constexpr (ACT == LORA_ACT_SWIGLU) {
+    return g * sigmoidf_(g);
+  } else {
+    const float k0 = 0.7978845608028654f, k1 = 0.044715f;   // sqrt(2/pi), cubic coefficient
+    return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+  }
+}
+// phi(g) and phi'(g) together.
+template <int ACT> __device__ __forceinline__ void act_both(float g, float& phi, float& dphi) {
+  if constexpr (ACT == LORA_ACT_SWIGLU) {
+    const float s = sigmoidf_(g);
+    phi = g * s;
+    dphi = s * (1.0f + g * (1.0f - s));
+  } else {
+    const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+    const float t = tanhf(k0 * (g + k1 * g * g * g));
+    phi = 0.5f * g * (1.0f + t);
+    dphi = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * k0 * (1.0f + 3.0f * k1 * g * g);
+  }
+}
+
+// ---- tile scheduling -------------------------------------------------------------
+// blockIdx.x -> (row block, column block).  Consecutive blocks go round-robin
+// to the 8 XCDs; remap so each XCD gets a contiguous range of logical tiles,
+// then walk that range in groups of `gm` row blocks so CTAs resident on one
+// XCD share A row blocks and B column tiles in its L2.
+__device__ __forceinline__ void tile_coords(int ntiles, int R, int NC, int gm, int& rb, int& cb) {
+  const int b = blockIdx.x;
+  const int per = ntiles >> 3, rem = ntiles & 7, x = b & 7, i = b >> 3;
+  const int L = (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+  const int gsz = gm * NC;
+  const int grp = L / gsz;
+  const int first = grp * gm;
+  const int g = min(gm, R - first);
+  const int w = L - grp * gsz;
+  rb = first + w % g;
+  cb = w / g;
+}
+
+}  // namespace lora

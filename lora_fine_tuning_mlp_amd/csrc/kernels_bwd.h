@@ -1,0 +1,623 @@
+// Backward kernels (base weights frozen: no dW anywhere).
+//
+// LoRA linear backward for the loss <dY, Y> (Opake "Model Patches and
+// Kernels", "Fused LoRA operations"; frozen weights get no gradient per
+// "Fused linear cross-entropy", key design decisions):
+//   dT = s dY B,  dB = s dY^T T,  dA = dT^T Z,  dZ = dY W + dT A.
+// GLU backward ("Activation functions": reads dH, G, U; writes dG, dU):
+//   dG = dH * U * phi'(G),  dU = dH * phi(G).
+// RoPE backward: the adjoint rotation R^T (rotation by -angle) applied to dQ, dK.
+//
+// Kernels:
+//   k_bwd_prologue  one pass over the upstream gradient P (dY, or dQ/dK/dV
+//                   un-rotated and un-split into token-major dP):
+//                   dT_p = s_p P_p B_p (partials over column ranges) and
+//                   dB_p = s_p P_p^T T_p (partials over row blocks), MFMA.
+//   k_down_bwd      dH = dY W_d + dT_d A_d (K = h), GLU backward in the
+//                   epilogue, plus row-block partials of dA_d, dB_g, dB_u.
+//   k_mlp_dx_bwd    dX = [dG|dU] [W_g; W_u] + dT_g A_g + dT_u A_u (K = 2i);
+//                   dT_g, dT_u ride the K-loop; partials of dA_g, dA_u.
+//   k_qkv_dx_bwd    dX = dP [W_q; W_k; W_v] + sum_p dT_p A_p; partials of dA_p.
+//   k_reduce        fixed-order sum of partials -> dA / dB in the call dtype.
+#pragma once
+
+#include "gemm.h"
+
+namespace lora {
+
+// ===========================================================================
+// Prologue
+// ===========================================================================
+struct ProArgs {
+  int qkv;                      // 0: P = dY [N][O];  1: P gathered from dQ/dK/dV
+  const void* P;
+  const void* src[3];           // dQ, dK, dV as [B][heads][S][d]
+  const float* cs; const float* sn;
+  int S, d;
+  int nh[3];
+  void* dP;                     // qkv: token-major dP [N][O]
+  const void* Bp[3];            // [O_p][r]
+  const float* Tp[3];           // saved T_p [N][r]
+  float s[3];
+  int off[4];                   // adapter column ranges
+  int nadp;
+  float* dT_part;               // [NCR][3][N][16]
+  float* dB_part;               // [R][O][16]
+  long N; int O, r;
+  int NCH, CPC, NCR;
+  int vecP, vecB;
+};
+
+constexpr int kProPr = 0;                       // [256 rows][BK]   row-major P tile
+constexpr int kProPc = 32768;                   // tiles [BK cols][BK tokens] x (256 / BK)
+constexpr int kProBt = 65536;                   // [16 t][BK]       B_p^T chunk
+constexpr int kProTT = 65536 + 2048;            // per adapter tiles [16 t][BK tokens] x (256/BK)
+constexpr int kProLds = kProTT + 3 * 16384;     // 116736
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
+  constexpr int VEC = ET<T>::VEC, BK = ET<T>::BK, KSUB = ET<T>::KSUB, HW = BK / 2;
+  constexpr int NKB = kBM / BK;                 // token tiles per 256 rows
+  constexpr int TTB = 16 * kRowBytes * NKB;     // bytes of one adapter's T^T
+  __shared__ __align__(16) char smem[kProLds];
+  const WaveId q = wave_id();
+  const int rb = blockIdx.x, cr = blockIdx.y;
+  const long m0 = (long)rb * kBM;
+  char* Pr = smem + kProPr;
+  char* Pc = smem + kProPc;
+  char* Bt = smem + kProBt;
+  char* TT = smem + kProTT;
+
+  // (s_p T_p)^T for this row block, once: TT_p tile kb, row t, element row % BK.
+  for (int p = 0; p < a.nadp; ++p) {
+    const int row = q.tid;
+    const long n = m0 + row;
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const float v = (n < a.N && t < a.r) ? a.s[p] * a.Tp[p][n * a.r + t] : 0.f;
+      char* dst = TT + p * TTB + (row / BK) * (16 * kRowBytes) + lds_off(t, (row % BK) / VEC) + (row % VEC) * ET<T>::BYTES;
+      *reinterpret_cast<T*>(dst) = from_f<T>(v);
+    }
+  }
+
+  f32x4 dT[3][4];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dT[p][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int pc = q.tid & 3, rg4 = q.tid >> 2;   // chunk pair (pc, pc+4), rows 4*rg4 .. +3
+  const int ch_end = min(a.NCH, (cr + 1) * a.CPC);
+  for (int ch = cr * a.CPC; ch < ch_end; ++ch) {
+    // Column map of this chunk: kk < HW -> base_lo + kk, kk >= HW -> base_hi + kk - HW.
+    int p = 0, hd = 0;
+    long base_lo, base_hi;
+    if (a.qkv) {
+      const int cph = a.d / BK;                 // chunks per head
+      const int gh = ch / cph, qq = ch % cph;
+      p = (gh < a.nh[0]) ? 0 : ((gh < a.nh[0] + a.nh[1]) ? 1 : 2);
+      hd = gh - ((p == 0) ? 0 : ((p == 1) ? a.nh[0] : a.nh[0] + a.nh[1]));
+      base_lo = a.off[p] + (long)hd * a.d + qq * HW;
+      base_hi = base_lo + a.d / 2;
+    } else {
+      base_lo = (long)ch * BK;
+      base_hi = base_lo + HW;
+    }
+    const T* Bsrc = static_cast<const T*>(a.Bp[p]);
+
+    // 1. P tile: 4 rows x (chunk pc, chunk pc+4) per thread.
+    u32x4 lo[4], hi[4];
+    const long clo = base_lo + pc * VEC, chi = base_hi + pc * VEC;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long n = m0 + 4 * rg4 + i;
+      if (n >= a.N) { lo[i] = zero4(); hi[i] = zero4(); continue; }
+      if (a.qkv) {
+        const int s = (int)(n % a.S);
+        const long b = n / a.S;
+        const int jlo = (int)(clo - a.off[p] - (long)hd * a.d);   // index within the head, < d/2
+        const T* src = static_cast<const T*>(a.src[p]) + ((b * a.nh[p] + hd) * a.S + s) * (long)a.d;
+        const u32x4 xl = gload<T>(src, jlo, a.d, a.vecP);
+        const u32x4 xh = gload<T>(src, jlo + a.d / 2, a.d, a.vecP);
+        if (p < 2) {
+          float vl[VEC], vh[VEC], yl[VEC], yh[VEC];
+          unpack(xl, vl);
+          unpack(xh, vh);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float c = a.cs[(long)s * (a.d / 2) + jlo + e], sn = a.sn[(long)s * (a.d / 2) + jlo + e];
+            yl[e] = vl[e] * c + vh[e] * sn;      // R^T: rotate by -angle
+            yh[e] = vh[e] * c - vl[e] * sn;
+          }
+          lo[i] = pack(yl);
+          hi[i] = pack(yh);
+        } else {
+          lo[i] = xl;
+          hi[i] = xh;
+        }
+        T* dp = static_cast<T*>(a.dP) + n * a.O;
+        *reinterpret_cast<u32x4*>(dp + clo) = lo[i];
+        *reinterpret_cast<u32x4*>(dp + chi) = hi[i];
+      } else {
+        const T* row = static_cast<const T*>(a.P) + n * a.O;
+        lo[i] = gload<T>(row, clo, a.O, a.vecP);
+        hi[i] = gload<T>(row, chi, a.O, a.vecP);
+      }
+    }
+    // 2. Row-major copy for dT, column-major copy for dB.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<u32x4*>(Pr + lds_off(4 * rg4 + i, pc)) = lo[i];
+      *reinterpret_cast<u32x4*>(Pr + lds_off(4 * rg4 + i, pc + 4)) = hi[i];
+    }
+    {
+      const int r0 = 4 * rg4;                     // 4 tokens: tile kb, chunk (r0 % BK) / VEC
+      char* tile = Pc + (r0 / BK) * (BK * kRowBytes);
+      const int kc = (r0 % BK) / VEC, sub = (r0 % VEC) * ET<T>::BYTES;
+      if constexpr (sizeof(T) == 2) {
+        const unsigned* wl = reinterpret_cast<const unsigned*>(lo);
+        const unsigned* wh = reinterpret_cast<const unsigned*>(hi);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          const int sh = (c & 1) * 16;
+          const unsigned l0 = (wl[0 * 4 + c / 2] >> sh) & 0xffffu, l1 = (wl[1 * 4 + c / 2] >> sh) & 0xffffu;
+          const unsigned l2 = (wl[2 * 4 + c / 2] >> sh) & 0xffffu, l3 = (wl[3 * 4 + c / 2] >> sh) & 0xffffu;
+          const unsigned h0 = (wh[0 * 4 + c / 2] >> sh) & 0xffffu, h1 = (wh[1 * 4 + c / 2] >> sh) & 0xffffu;
+          const unsigned h2 = (wh[2 * 4 + c / 2] >> sh) & 0xffffu, h3 = (wh[3 * 4 + c / 2] >> sh) & 0xffffu;
+          *reinterpret_cast<u32x2*>(tile + lds_off(pc * VEC + c, kc) + sub) = (u32x2){l0 | (l1 << 16), l2 | (l3 << 16)};
+          *reinterpret_cast<u32x2*>(tile + lds_off(HW + pc * VEC + c, kc) + sub) = (u32x2){h0 | (h1 << 16), h2 | (h3 << 16)};
+        }
+      } else {
+        u32x4 tl[4], th[4];
+        transpose4x4_f32(lo, tl);
+        transpose4x4_f32(hi, th);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          *reinterpret_cast<u32x4*>(tile + lds_off(pc * VEC + c, kc)) = tl[c];
+          *reinterpret_cast<u32x4*>(tile + lds_off(HW + pc * VEC + c, kc)) = th[c];
+        }
+      }
+    }
+    // 3. B_p^T chunk: row t, element kk = B_p[col(kk) - off_p][t].
+    if (q.tid < 128) {
+      const int tpr = (sizeof(T) == 2) ? 2 : 4;   // threads per kk
+      const int kk = q.tid / tpr, t0 = (q.tid % tpr) * VEC;
+      const long col = (kk < HW) ? base_lo + kk : base_hi + (kk - HW);
+      const long lim = a.qkv ? (long)a.off[p + 1] : (long)a.O;
+      const T* brow = (col < lim) ? Bsrc + (col - a.off[p]) * a.r : nullptr;
+      const u32x4 v = gload<T>(brow, t0, a.r, a.vecB);
+      const unsigned* wv = reinterpret_cast<const unsigned*>(&v);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        char* dst = Bt + lds_off(t0 + e, kk / VEC) + (kk % VEC) * ET<T>::BYTES;
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<unsigned short*>(dst) = (unsigned short)((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu));
+        else
+          *reinterpret_cast<unsigned*>(dst) = wv[e];
+      }
+    }
+    __syncthreads();
+
+    // 4. dT_p[rows][t] += P[rows][chunk] . B_p[chunk][t]   (wave w: rows 64w .. 64w+63)
+#pragma unroll
+    for (int ks = 0; ks < KSUB; ++ks) {
+      const Frag<T> bf = lds_frag<T>(Bt, q.r16, ks, q.g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const Frag<T> af = lds_frag<T>(Pr, (4 * q.w + i) * 16 + q.r16, ks, q.g);
+        if (p == 0) dT[0][i] = mma(dT[0][i], af, bf);
+        else if (p == 1) dT[1][i] = mma(dT[1][i], af, bf);
+        else dT[2][i] = mma(dT[2][i], af, bf);
+      }
+    }
+    // 5. dB_p[col][t] (row-block partial) = P[rows][col]^T . (s_p T_p)[rows][t]
+    if (q.w * 16 < BK) {
+      f32x4 db = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < KSUB; ++ks) {
+          const Frag<T> af = lds_frag<T>(Pc + kb * (BK * kRowBytes), q.w * 16 + q.r16, ks, q.g);
+          const Frag<T> bf = lds_frag<T>(TT + p * TTB + kb * (16 * kRowBytes), q.r16, ks, q.g);
+          db = mma(db, af, bf);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = q.w * 16 + 4 * q.g + j;
+        const long col = (kk < HW) ? base_lo + kk : base_hi + (kk - HW);
+        if (col < a.O) a.dB_part[((long)rb * a.O + col) * 16 + q.r16] = db[j];
+      }
+    }
+    __syncthreads();
+  }
+
+  // dT partial of this column range (zeros for adapters it did not touch).
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long n = m0 + (4 * q.w + i) * 16 + 4 * q.g + j;
+        if (n < a.N) a.dT_part[(((long)cr * 3 + p) * a.N + n) * 16 + q.r16] = a.s[p] * dT[p][i][j];
+      }
+}
+
+// Fill Ts[slot][m][t] = sum over column ranges of the prologue's dT partials.
+__device__ __forceinline__ void load_dT(char* smem, const float* dT_part, int NCR, long N, long m0, int nslot) {
+  float* Ts = ts_ptr(smem);
+  const int m = threadIdx.x;
+  const long n = m0 + m;
+  for (int sl = 0; sl < nslot; ++sl)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float v = 0.f;
+      if (n < N)
+        for (int c = 0; c < NCR; ++c) v += dT_part[(((long)c * 3 + sl) * N + n) * 16 + t];
+      Ts[ts_idx(sl, m, t)] = v;
+    }
+  __syncthreads();
+}
+
+// ===========================================================================
+// Down projection backward + GLU backward
+// ===========================================================================
+struct DownBwdArgs {
+  const void* dY; const void* Wd; const void* Ad;
+  const void* G; const void* U;
+  const float* Tg; const float* Tu;
+  const float* dT_part; int NCR;
+  float sg, su;
+  void* dG; void* dU;
+  float* pA_d; float* pB_g; float* pB_u;     // [R][i][16]
+  long N; int h, i, r;
+  int vecA, vecW, vecO;
+  int R, NC;
+};
+
+template <class T, int ACT>
+__global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  const WaveId q = wave_id();
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const long n0 = (long)cb * kBN;
+  const T* dY = static_cast<const T*>(a.dY);
+  const T* Wd = static_cast<const T*>(a.Wd);
+  const long h = a.h, ni = a.i;
+
+  KNLoader<T, RowsA<T>, 0, KRow1<T>, SRowNone<T>, SMaskNone> ld;
+  ld.a.init(dY, h, a.N, m0, h, a.vecA);
+  ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
+  ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+
+  f32x4 acc[8][8];
+  f32x4 sacc[1][8];
+  zero_acc(acc);
+  const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
+  kloop<T, 0>(smem, nkt, ld, acc, sacc);
+
+  load_dT(smem, a.dT_part, a.NCR, a.N, m0, 1);
+  const T* Ad = static_cast<const T*>(a.Ad);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const long n = n0 + lds_row_col(0, R);
+    if (slot != 0 || n >= ni) return;
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(Ad[(long)(t0 + e) * ni + n]);
+  };
+  const float fs[kMaxSide] = {1.f, 0.f, 0.f};
+  fold<T>(smem, acc, 1, fs, fb);
+
+  // Epilogue: lane holds dH[row][c0 + nb], nb = 0..7.
+  const T* Gs = static_cast<const T*>(a.G);
+  const T* Us = static_cast<const T*>(a.U);
+  T* dGo = static_cast<T*>(a.dG);
+  T* dUo = static_cast<T*>(a.dU);
+  const float* Ts = ts_ptr(smem);
+  const long c0 = n0 + q.wn * 128 + 8 * q.r16;
+  const int nvalid = (int)min(8L, ni - c0);
+  f32x4 pacc[3][8];
+#pragma unroll
+  for (int o = 0; o < 3; ++o)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int mp = 0; mp < 4; ++mp) {
+    float hv[8][8], gv[8][8], uv[8][8];    // [slot = mbl*4 + j][nb]
+#pragma unroll
+    for (int mbl = 0; mbl < 2; ++mbl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mb = 2 * mp + mbl, sl = mbl * 4 + j;
+        const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+        float G8[8], U8[8];
+        if (row < a.N && nvalid > 0) {
+          const u32x4 g0 = gload<T>(Gs + row * ni, c0, ni, a.vecO);
+          const u32x4 u0 = gload<T>(Us + row * ni, c0, ni, a.vecO);
+          if constexpr (sizeof(T) == 2) {
+            unpack(g0, G8);
+            unpack(u0, U8);
+          } else {
+            const u32x4 g1 = gload<T>(Gs + row * ni, c0 + 4, ni, a.vecO);
+            const u32x4 u1 = gload<T>(Us + row * ni, c0 + 4, ni, a.vecO);
+            float t4[4];
+            unpack(g0, t4); for (int e = 0; e < 4; ++e) G8[e] = t4[e];
+            unpack(g1, t4); for (int e = 0; e < 4; ++e) G8[4 + e] = t4[e];
+            unpack(u0, t4); for (int e = 0; e < 4; ++e) U8[e] = t4[e];
+            unpack(u1, t4); for (int e = 0; e < 4; ++e) U8[4 + e] = t4[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { G8[e] = 0.f; U8[e] = 0.f; }
+        }
+        float dg8[8], du8[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          float ph, dph;
+          act_both<ACT>(G8[nb], ph, dph);
+          const float dh = acc[mb][nb][j];
+          dg8[nb] = dh * U8[nb] * dph;
+          du8[nb] = dh * ph;
+          hv[sl][nb] = ph * U8[nb];
+          gv[sl][nb] = dg8[nb];
+          uv[sl][nb] = du8[nb];
+        }
+        if (row < a.N && nvalid > 0) {
+          store_row8<T>(dGo + row * ni + c0, dg8, nvalid, a.vecO);
+          store_row8<T>(dUo + row * ni + c0, du8, nvalid, a.vecO);
+        }
+      }
+    // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
+    // (s T_g), (s T_u) and dG, dU.  K = the 8 rows of this lane group.
+    const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q.wm, mp, q.g, q.r16);
+    float tg[8], tu[8];
+#pragma unroll
+    for (int mbl = 0; mbl < 2; ++mbl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long row = m0 + q.wm * 128 + (2 * mp + mbl) * 16 + 4 * q.g + j;
+        const bool ok = row < a.N && q.r16 < a.r;
+        tg[mbl * 4 + j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
+        tu[mbl * 4 + j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
+      }
+    const Frag<T> aTg = make_frag<T>(tg);
+    const Frag<T> aTu = make_frag<T>(tu);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      float b0[8], b1[8], b2[8];
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) { b0[sl] = hv[sl][nb]; b1[sl] = gv[sl][nb]; b2[sl] = uv[sl][nb]; }
+      pacc[0][nb] = mma(pacc[0][nb], adT, make_frag<T>(b0));
+      pacc[1][nb] = mma(pacc[1][nb], aTg, make_frag<T>(b1));
+      pacc[2][nb] = mma(pacc[2][nb], aTu, make_frag<T>(b2));
+    }
+  }
+  float* const parts[3] = {a.pA_d + (long)rb * ni * 16, a.pB_g + (long)rb * ni * 16, a.pB_u + (long)rb * ni * 16};
+  reduce_store_partials<3>(smem, pacc, parts, n0, ni);
+}
+
+// ===========================================================================
+// Shared dX epilogue: store dX, then dA_p partials = (scale_p Ts_p)^T . X.
+// ===========================================================================
+template <class T, int NA>
+__device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[8][8], const float (&escale)[kMaxSide],
+                                            const T* X, T* dX, float* const (&parts)[NA], long N, long h, long m0,
+                                            long n0, bool vecO) {
+  const WaveId q = wave_id();
+  const float* Ts = ts_ptr(smem);
+  const long c0 = n0 + q.wn * 128 + 8 * q.r16;
+  const int nvalid = (int)min(8L, h - c0);
+  f32x4 pacc[NA][8];
+#pragma unroll
+  for (int o = 0; o < NA; ++o)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mp = 0; mp < 4; ++mp) {
+    float xv[8][8];   // [slot][nb]
+#pragma unroll
+    for (int mbl = 0; mbl < 2; ++mbl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int mb = 2 * mp + mbl, sl = mbl * 4 + j;
+        const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+        float X8[8];
+        if (row < N && nvalid > 0) {
+          float v[8];
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
+          store_row8<T>(dX + row * h + c0, v, nvalid, vecO);
+          const u32x4 x0 = gload<T>(X + row * h, c0, h, vecO);
+          if constexpr (sizeof(T) == 2) {
+            unpack(x0, X8);
+          } else {
+            const u32x4 x1 = gload<T>(X + row * h, c0 + 4, h, vecO);
+            float t4[4];
+            unpack(x0, t4); for (int e = 0; e < 4; ++e) X8[e] = t4[e];
+            unpack(x1, t4); for (int e = 0; e < 4; ++e) X8[4 + e] = t4[e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) X8[e] = 0.f;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) xv[sl][nb] = X8[nb];
+      }
+    Frag<T> adT[NA];
+#pragma unroll
+    for (int o = 0; o < NA; ++o) adT[o] = ts_frag<T>(Ts, o, escale[o], q.wm, mp, q.g, q.r16);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      float b[8];
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) b[sl] = xv[sl][nb];
+      const Frag<T> bf = make_frag<T>(b);
+#pragma unroll
+      for (int o = 0; o < NA; ++o) pacc[o][nb] = mma(pacc[o][nb], adT[o], bf);
+    }
+  }
+  reduce_store_partials<NA>(smem, pacc, parts, n0, h);
+}
+
+// ===========================================================================
+// MLP dX
+// ===========================================================================
+struct MlpDxArgs {
+  const void* dG; const void* dU;
+  const void* Wg; const void* Wu;
+  const void* Bg; const void* Bu;
+  const void* Ag; const void* Au;
+  const void* X;
+  float sg, su;
+  void* dX;
+  float* pA_g; float* pA_u;       // [R][h][16]
+  long N; int h, i, r;
+  int vecA, vecW, vecS, vecO;
+  int R, NC;
+};
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const long n0 = (long)cb * kBN;
+  const long h = a.h, ni = a.i, r = a.r;
+  const T* Wg = static_cast<const T*>(a.Wg);
+  const T* Wu = static_cast<const T*>(a.Wu);
+  const T* Bg = static_cast<const T*>(a.Bg);
+  const T* Bu = static_cast<const T*>(a.Bu);
+  constexpr int BK = ET<T>::BK;
+
+  KNLoader<T, SplitRowsA<T>, 2, KRow2<T>, SRow2<T>, SMask2> ld;
+  ld.a.init(static_cast<const T*>(a.dG), ni, ni, static_cast<const T*>(a.dU), ni, ni, a.N, m0, a.vecA);
+  ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
+  ld.srow.B0 = Bg; ld.srow.B1 = Bu; ld.srow.K0 = ni; ld.srow.K1 = ni; ld.srow.ld = r;
+  ld.smask_of.K0 = ni; ld.smask_of.BK = BK;
+  ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
+
+  f32x4 acc[8][8];
+  f32x4 sacc[2][8];
+  zero_acc(acc);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int nkt = (int)((2 * ni + BK - 1) / BK);
+  kloop<T, 2>(smem, nkt, ld, acc, sacc);
+  side_reduce<T, 2>(smem, sacc);
+
+  const T* Ag = static_cast<const T*>(a.Ag);
+  const T* Au = static_cast<const T*>(a.Au);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const long n = n0 + lds_row_col(0, R);
+    if (n >= h) return;
+    const T* src = (slot == 0) ? Ag : Au;
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(src[(long)(t0 + e) * h + n]);
+  };
+  const float fs[kMaxSide] = {a.sg, a.su, 0.f};
+  fold<T>(smem, acc, 2, fs, fb);
+
+  float* const parts[2] = {a.pA_g + (long)rb * h * 16, a.pA_u + (long)rb * h * 16};
+  dx_epilogue<T, 2>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                    a.vecO);
+}
+
+// ===========================================================================
+// QKV dX
+// ===========================================================================
+struct QkvDxArgs {
+  const void* dP;
+  const void* W[3]; const void* A[3];
+  const float* dT_part; int NCR;
+  const void* X;
+  void* dX;
+  float* pA[3];                   // [R][h][16]
+  long N; int h, O, r;
+  int off[4];
+  int vecA, vecW, vecO;
+  int R, NC;
+};
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const long n0 = (long)cb * kBN;
+  const long h = a.h;
+  const T* W0 = static_cast<const T*>(a.W[0]);
+  const T* W1 = static_cast<const T*>(a.W[1]);
+  const T* W2 = static_cast<const T*>(a.W[2]);
+  const long o1 = a.off[1], o2 = a.off[2], o3 = a.off[3];
+
+  KNLoader<T, RowsA<T>, 0, KRow3<T>, SRowNone<T>, SMaskNone> ld;
+  ld.a.init(static_cast<const T*>(a.dP), a.O, a.N, m0, a.O, a.vecA);
+  ld.krow.W0 = W0; ld.krow.W1 = W1; ld.krow.W2 = W2;
+  ld.krow.o1 = o1; ld.krow.o2 = o2; ld.krow.o3 = o3; ld.krow.ld = h;
+  ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+
+  f32x4 acc[8][8];
+  f32x4 sacc[1][8];
+  zero_acc(acc);
+  const int nkt = (a.O + ET<T>::BK - 1) / ET<T>::BK;
+  kloop<T, 0>(smem, nkt, ld, acc, sacc);
+
+  load_dT(smem, a.dT_part, a.NCR, a.N, m0, 3);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const long n = n0 + lds_row_col(0, R);
+    if (n >= h) return;
+    const T* src = static_cast<const T*>(a.A[0]);
+    if (slot == 1) src = static_cast<const T*>(a.A[1]);
+    if (slot == 2) src = static_cast<const T*>(a.A[2]);
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(src[(long)(t0 + e) * h + n]);
+  };
+  const float fs[kMaxSide] = {1.f, 1.f, 1.f};
+  fold<T>(smem, acc, 3, fs, fb);
+
+  float* const parts[3] = {a.pA[0] + (long)rb * h * 16, a.pA[1] + (long)rb * h * 16, a.pA[2] + (long)rb * h * 16};
+  dx_epilogue<T, 3>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                    a.vecO);
+}
+
+// ===========================================================================
+// Fixed-order reduction of [nslice][cols][16] partials.
+//   transpose = 1: out[t][col] (dA, [r, cols]);  0: out[col][t] (dB, [cols, r]).
+// ===========================================================================
+struct RedJob {
+  const float* part;
+  long stride;                   // elements between consecutive slices
+  long count;                    // elements per slice (cols * 16)
+  int nslice;
+  int cols;
+  int transpose;
+  void* out;
+};
+struct RedArgs {
+  RedJob job[6];
+  int njobs;
+  int r;
+};
+
+template <class T>
+__global__ __launch_bounds__(256) void k_reduce(RedArgs a) {
+  const RedJob& jb = a.job[blockIdx.y];
+  const long e = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= jb.count) return;
+  const int t = (int)(e & 15);
+  const long col = e >> 4;
+  if (t >= a.r) return;
+  float v = 0.f;
+  for (int x = 0; x < jb.nslice; ++x) v += jb.part[(long)x * jb.stride + e];
+  T* out = static_cast<T*>(jb.out);
+  if (jb.transpose) out[(long)t * jb.cols + col] = from_f<T>(v);
+  else out[col * a.r + t] = from_f<T>(v);
+}
+
+}  // namespace lora

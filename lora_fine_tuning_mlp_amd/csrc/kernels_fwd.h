@@ -1,0 +1,371 @@
+// Forward kernels: LoRA gate/up + GLU, LoRA down, LoRA QKV + RoPE + GQA split,
+// and the RoPE angle table.
+//
+// Math (Opake "Model Patches and Kernels": "Fused LoRA operations",
+// "Activation functions", "Rotary position embeddings (RoPE)"):
+//   G = X W_g^T + s_g (X A_g^T) B_g^T,  U likewise,  H = phi(G) * U,
+//   Y = H W_d^T + s_d (H A_d^T) B_d^T,
+//   P_p = X W_p^T + s_p (X A_p^T) B_p^T for p in {q, k, v}; Q, K rotated.
+#pragma once
+
+#include "gemm.h"
+
+namespace lora {
+
+// ===========================================================================
+// gate/up: one tile = 256 tokens x (128 gate columns + the same 128 up columns)
+// ===========================================================================
+struct GateUpArgs {
+  const void* X; const void* Wg; const void* Ag; const void* Bg;
+  const void* Wu; const void* Au; const void* Bu;
+  float sg, su;
+  void* G; void* U; void* H;
+  float* Tg; float* Tu;
+  long N; int h, i, r;
+  int vecA, vecW, vecS, vecO;
+  int R, NC;
+};
+
+// LDS row R of the B tile -> (is_up, intermediate column index j).
+__device__ __forceinline__ void gateup_row(int R, int j0, int& is_up, int& j) {
+  const int w = perm_col(1, R & 15, (R >> 4) & 7);   // G = 2: [gate 64 | up 64] per wave window
+  is_up = w >> 6;
+  j = j0 + (R >> 7) * 64 + (w & 63);
+}
+
+template <class T, int ACT>
+__global__ __launch_bounds__(kThreads, 1) void k_gateup_fwd(GateUpArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  const WaveId q = wave_id();
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const int j0 = cb * 128;
+  const T* X = static_cast<const T*>(a.X);
+  const T* Wg = static_cast<const T*>(a.Wg);
+  const T* Wu = static_cast<const T*>(a.Wu);
+  const T* Ag = static_cast<const T*>(a.Ag);
+  const T* Au = static_cast<const T*>(a.Au);
+
+  NKLoader<T, RowsA<T>, 2> ld;
+  ld.a.init(X, a.h, a.N, m0, a.h, a.vecA);
+  ld.K = a.h;
+  ld.vecB = a.vecW;
+  ld.vecS = a.vecS;
+  ld.smask = 3u;
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) {
+    int up, j;
+    gateup_row((q.tid >> 3) + 32 * qq, j0, up, j);
+    ld.brow[qq] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
+  }
+  {
+    const int sr = q.tid >> 3;          // side rows 0..31: A_g rows 0..15, A_u rows 0..15
+    const int t = sr & 15;
+    ld.srow[0] = (t < a.r) ? ((sr < 16) ? Ag : Au) + (long)t * a.h : nullptr;
+  }
+
+  f32x4 acc[8][8];
+  f32x4 sacc[2][8];
+  zero_acc(acc);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
+  kloop<T, 2>(smem, nkt, ld, acc, sacc);
+  side_reduce<T, 2>(smem, sacc);
+
+  // The row block's T_g, T_u are saved once (by column block 0).
+  if (cb == 0) {
+    const float* Ts = ts_ptr(smem);
+    const long row = m0 + q.tid;
+    if (row < a.N)
+      for (int t = 0; t < a.r; ++t) {
+        a.Tg[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
+        a.Tu[row * a.r + t] = Ts[ts_idx(1, q.tid, t)];
+      }
+  }
+
+  const T* Bg = static_cast<const T*>(a.Bg);
+  const T* Bu = static_cast<const T*>(a.Bu);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    int up, j;
+    gateup_row(R, j0, up, j);
+    if (slot != up || j >= a.i) return;
+    const T* src = (up ? Bu : Bg) + (long)j * a.r;
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(src[t0 + e]);
+  };
+  const float fs[kMaxSide] = {a.sg, a.su, 0.f};
+  fold<T>(smem, acc, 2, fs, fb);
+
+  // GLU epilogue: lane holds gate (blocks 0..3) and up (blocks 4..7) of the
+  // same 4 consecutive intermediate columns.
+  T* Go = static_cast<T*>(a.G);
+  T* Uo = static_cast<T*>(a.U);
+  T* Ho = static_cast<T*>(a.H);
+  const int jj = j0 + q.wn * 64 + 4 * q.r16;
+  const int nvalid = min(4, a.i - jj);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      if (row >= a.N || nvalid <= 0) continue;
+      float gv[4], uv[4], hv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        gv[e] = acc[mb][e][j];
+        uv[e] = acc[mb][4 + e][j];
+        hv[e] = act_fwd<ACT>(gv[e]) * uv[e];
+      }
+      const long off = row * a.i + jj;
+      gstore<T, 4>(Go + off, gv, nvalid, a.vecO);
+      gstore<T, 4>(Uo + off, uv, nvalid, a.vecO);
+      gstore<T, 4>(Ho + off, hv, nvalid, a.vecO);
+    }
+}
+
+// ===========================================================================
+// Plain LoRA linear with a row-major output (down projection: Y = L_d(H)).
+// ===========================================================================
+struct LinearArgs {
+  const void* Z; const void* W; const void* A; const void* B;
+  float s;
+  void* Y; float* T;
+  long N; int K, O, r;
+  int vecA, vecW, vecS, vecO;
+  int R, NC;
+};
+
+template <class T>
+__global__ __launch_bounds__(kThreads, 1) void k_linear_fwd(LinearArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  const WaveId q = wave_id();
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const long n0 = (long)cb * kBN;
+  const T* Z = static_cast<const T*>(a.Z);
+  const T* W = static_cast<const T*>(a.W);
+  const T* A = static_cast<const T*>(a.A);
+
+  NKLoader<T, RowsA<T>, 1> ld;
+  ld.a.init(Z, a.K, a.N, m0, a.K, a.vecA);
+  ld.K = a.K;
+  ld.vecB = a.vecW;
+  ld.vecS = a.vecS;
+  ld.smask = 1u;
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) {
+    const long n = n0 + lds_row_col(0, (q.tid >> 3) + 32 * qq);
+    ld.brow[qq] = (n < a.O) ? W + n * a.K : nullptr;
+  }
+  {
+    const int sr = q.tid >> 3;
+    ld.srow[0] = (sr < 16 && sr < a.r) ? A + (long)sr * a.K : nullptr;
+  }
+
+  f32x4 acc[8][8];
+  f32x4 sacc[1][8];
+  zero_acc(acc);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) sacc[0][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int nkt = (a.K + ET<T>::BK - 1) / ET<T>::BK;
+  kloop<T, 1>(smem, nkt, ld, acc, sacc);
+  side_reduce<T, 1>(smem, sacc);
+
+  if (cb == 0) {
+    const float* Ts = ts_ptr(smem);
+    const long row = m0 + q.tid;
+    if (row < a.N)
+      for (int t = 0; t < a.r; ++t) a.T[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
+  }
+
+  const T* B = static_cast<const T*>(a.B);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const long n = n0 + lds_row_col(0, R);
+    if (slot != 0 || n >= a.O) return;
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(B[n * a.r + t0 + e]);
+  };
+  const float fs[kMaxSide] = {a.s, 0.f, 0.f};
+  fold<T>(smem, acc, 1, fs, fb);
+
+  T* Y = static_cast<T*>(a.Y);
+  const long c0 = n0 + q.wn * 128 + 8 * q.r16;
+  const int nvalid = (int)min(8L, a.O - c0);
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      if (row >= a.N || nvalid <= 0) continue;
+      float v[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
+      store_row8<T>(Y + row * a.O + c0, v, nvalid, a.vecO);
+    }
+}
+
+// ===========================================================================
+// RoPE angle table: cos/sin of s * theta^(-2j/d), evaluated in double.
+// ===========================================================================
+__global__ void k_rope_table(float* cs, float* sn, int S, int half, double theta) {
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)S * half) return;
+  const int s = (int)(idx / half), j = (int)(idx % half);
+  const double ang = (double)s * pow(theta, -2.0 * (double)j / (double)(2 * half));
+  cs[idx] = (float)cos(ang);
+  sn[idx] = (float)sin(ang);
+}
+
+// ===========================================================================
+// QKV: [P_q | P_k | P_v] tile = X . [W_q; W_k; W_v]^T + fold, then RoPE on
+// q/k columns and the head split into [B, heads, S, d].
+// ===========================================================================
+struct QKVFwdArgs {
+  const void* X;
+  const void* W[3]; const void* A[3]; const void* B[3];
+  float s[3];
+  void* out[3];        // Q, K, V
+  float* T[3];
+  const float* cs; const float* sn;
+  long N; int h, S, d, r;
+  int nh[3];           // heads per projection
+  int off[4];          // column offsets: 0, Oq, Oq+Ok, O
+  int vecA, vecW, vecS, vecO;
+  int R, NC;
+};
+
+// LG = log2(256 / head_dim): 1 for d = 128, 2 for d = 64 (RoPE pairs share a lane).
+template <class T, int LG>
+__global__ __launch_bounds__(kThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  const WaveId q = wave_id();
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const int n0 = cb * kBN;
+  const int O = a.off[3];
+  const T* X = static_cast<const T*>(a.X);
+
+  // Projections overlapping this tile, in q, k, v order -> fold / side slots.
+  int plist[3] = {0, 0, 0};
+  int nslot = 0;
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+    if (a.off[p] < min(n0 + kBN, O) && a.off[p + 1] > n0) plist[nslot++] = p;
+  auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
+  auto slot_of = [&](int p) { return (plist[0] == p) ? 0 : ((plist[1] == p) ? 1 : 2); };
+
+  NKLoader<T, RowsA<T>, 3> ld;
+  ld.a.init(X, a.h, a.N, m0, a.h, a.vecA);
+  ld.K = a.h;
+  ld.vecB = a.vecW;
+  ld.vecS = a.vecS;
+  ld.smask = (1u << nslot) - 1u;
+#pragma unroll
+  for (int qq = 0; qq < 8; ++qq) {
+    const int o = n0 + lds_row_col(LG, (q.tid >> 3) + 32 * qq);
+    if (o < O) {
+      const int p = proj_of(o);
+      ld.brow[qq] = static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
+    } else {
+      ld.brow[qq] = nullptr;
+    }
+  }
+#pragma unroll
+  for (int qq = 0; qq < NKLoader<T, RowsA<T>, 3>::NSQ; ++qq) {
+    const int sr = (q.tid >> 3) + 32 * qq;     // side row: slot sr/16, rank sr%16
+    const int sl = sr >> 4, t = sr & 15;
+    const T* p = nullptr;
+    if (sr < 48 && sl < nslot && t < a.r) {
+      const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+      p = static_cast<const T*>(a.A[pj]) + (long)t * a.h;
+    }
+    ld.srow[qq] = p;
+  }
+
+  f32x4 acc[8][8];
+  f32x4 sacc[3][8];
+  zero_acc(acc);
+#pragma unroll
+  for (int s = 0; s < 3; ++s)
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
+  kloop<T, 3>(smem, nkt, ld, acc, sacc);
+  side_reduce<T, 3>(smem, sacc);
+
+  // T_p is saved by the tile holding projection p's first column.
+  {
+    const float* Ts = ts_ptr(smem);
+    const long row = m0 + q.tid;
+    for (int sl = 0; sl < nslot; ++sl) {
+      const int p = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+      if (a.off[p] >= n0 && a.off[p] < n0 + kBN && row < a.N)
+        for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, q.tid, t)];
+    }
+  }
+
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const int o = n0 + lds_row_col(LG, R);
+    if (o >= O) return;
+    const int p = proj_of(o);
+    if (slot_of(p) != slot) return;
+    const T* src = static_cast<const T*>(a.B[p]) + (long)(o - a.off[p]) * a.r;
+    for (int e = 0; e < ET<T>::VEC; ++e)
+      if (t0 + e < a.r) v[e] = to_f<T>(src[t0 + e]);
+  };
+  float fs[kMaxSide];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSide; ++sl) {
+    const int p = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+    fs[sl] = (p == 0) ? a.s[0] : ((p == 1) ? a.s[1] : a.s[2]);
+  }
+  fold<T>(smem, acc, nslot, fs, fb);
+
+  // RoPE + split.  Groups alternate first half / second half of a head, so
+  // block b (first half) pairs with block b + cw in the same lane.
+  constexpr int cw = 8 >> LG;
+  const int half = a.d >> 1;
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      if (row >= a.N) continue;
+      const int s = (int)(row % a.S);
+      const long bidx = row / a.S;
+#pragma unroll
+      for (int b1 = 0; b1 < 8; b1 += 2 * cw) {       // first block of each head-half pair group
+        const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, b1);
+        if (o1 >= O) continue;
+        const int p = proj_of(o1);
+        const int oo = o1 - a.off[p];
+        const int hd = oo / a.d, jj = oo % a.d;      // jj < d/2, jj .. jj+cw-1 consecutive
+        float y1[cw], y2[cw];
+#pragma unroll
+        for (int e = 0; e < cw; ++e) {
+          const float x1 = acc[mb][b1 + e][j];
+          const float x2 = acc[mb][b1 + cw + e][j];
+          if (p < 2) {
+            const float c = a.cs[(long)s * half + jj + e], sn = a.sn[(long)s * half + jj + e];
+            y1[e] = x1 * c - x2 * sn;
+            y2[e] = x2 * c + x1 * sn;
+          } else {
+            y1[e] = x1;
+            y2[e] = x2;
+          }
+        }
+        T* dst = static_cast<T*>(a.out[p]) + ((bidx * a.nh[p] + hd) * a.S + s) * (long)a.d + jj;
+        gstore<T, cw>(dst, y1, cw, a.vecO);
+        gstore<T, cw>(dst + half, y2, cw, a.vecO);
+      }
+    }
+}
+
+}  // namespace lora

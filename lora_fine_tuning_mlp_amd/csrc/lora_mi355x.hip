@@ -1,0 +1,621 @@
+// Host orchestration and C ABI of the fused LoRA MLP / QKV library (gfx950).
+//
+// Each entry point validates its arguments on the host (nothing is enqueued
+// on an error), carves the caller's workspace, and enqueues its kernels on
+// the caller's stream.  No allocation, no synchronisation, no global state
+// besides the optional timing recorder and the thread-local error message.
+#include "lora_mi355x.h"
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "kernels_bwd.h"
+#include "kernels_fwd.h"
+
+using namespace lora;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+int ok() {
+  g_err[0] = '\0';
+  return LORA_OK;
+}
+
+// ---- timing ---------------------------------------------------------------
+const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
+                        "k_down_bwd",   "k_mlp_dx_bwd", "k_qkv_dx_bwd", "k_reduce"};
+constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
+
+struct Rec {
+  int kernel;
+  hipEvent_t e0, e1;
+};
+std::mutex g_tm;
+bool g_timing = false;
+std::vector<Rec> g_recs;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+int kernel_id(const char* name) {
+  for (int i = 0; i < kNumNames; ++i)
+    if (strcmp(kNames[i], name) == 0) return i;
+  return -1;
+}
+
+template <class Kern, class... Args>
+int launch(int kid, Kern kern, dim3 grid, dim3 block, hipStream_t st, Args... args) {
+  if (grid.x == 0 || grid.y == 0 || grid.z == 0) return LORA_OK;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tm);
+    if (g_timing) {
+      e0 = take_event();
+      e1 = take_event();
+      timed = e0 && e1;
+    }
+  }
+  if (timed) (void)hipEventRecord(e0, st);
+  hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
+  const hipError_t err = hipGetLastError();
+  if (timed) {
+    (void)hipEventRecord(e1, st);
+    std::lock_guard<std::mutex> lk(g_tm);
+    g_recs.push_back(Rec{kid, e0, e1});
+  }
+  if (err != hipSuccess) return fail(LORA_ERR_HIP, "%s launch failed: %s", kNames[kid], hipGetErrorString(err));
+  return LORA_OK;
+}
+
+// ---- helpers ----------------------------------------------------------------
+bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+int vecw(int dtype) { return dtype == LORA_BF16 ? 8 : 4; }
+size_t esz(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
+size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
+long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class P> P* take(size_t bytes) {
+    P* p = reinterpret_cast<P*>(base ? base + off : nullptr);
+    off += up256(bytes);
+    return p;
+  }
+};
+
+// MLP workspace.
+struct MlpWs {
+  void* H;
+  void *dG, *dU;
+  float *dT_part, *pA_d, *pB_g, *pB_u, *pA_g, *pA_u, *pB_d;
+  int NCR, NCH, CPC;
+  size_t bytes;
+};
+MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
+  MlpWs w{};
+  Carver c(base);
+  const long N = d.n_tokens, h = d.hidden, i = d.inter;
+  const long R = cdiv(N, kBM);
+  const size_t es = esz(d.dtype);
+  const int BK = d.dtype == LORA_BF16 ? ET<bf16>::BK : ET<float>::BK;
+  w.NCH = (int)cdiv(h, BK);
+  w.NCR = w.NCH < 8 ? w.NCH : 8;
+  w.CPC = (int)cdiv(w.NCH, w.NCR);
+  if (pass == 0) {
+    w.H = c.take<void>(N * i * es);
+  } else {
+    w.dG = c.take<void>(N * i * es);
+    w.dU = c.take<void>(N * i * es);
+    w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    w.pA_d = c.take<float>(R * i * 16 * 4);
+    w.pB_g = c.take<float>(R * i * 16 * 4);
+    w.pB_u = c.take<float>(R * i * 16 * 4);
+    w.pA_g = c.take<float>(R * h * 16 * 4);
+    w.pA_u = c.take<float>(R * h * 16 * 4);
+    w.pB_d = c.take<float>(R * h * 16 * 4);
+  }
+  w.bytes = c.off;
+  return w;
+}
+
+struct QkvWs {
+  float *cs, *sn;
+  void* dP;
+  float *dT_part, *pA[3], *dB_part;
+  int NCR, NCH, CPC;
+  size_t bytes;
+};
+QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
+  QkvWs w{};
+  Carver c(base);
+  const long N = (long)d.batch * d.seq, h = d.hidden;
+  const long O = (long)(d.n_q + 2 * d.n_kv) * d.head_dim;
+  const long R = cdiv(N, kBM);
+  const size_t es = esz(d.dtype);
+  const int BK = d.dtype == LORA_BF16 ? ET<bf16>::BK : ET<float>::BK;
+  w.cs = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
+  w.sn = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
+  w.NCH = (int)(O / BK);
+  w.NCR = w.NCH < 8 ? w.NCH : 8;
+  w.CPC = w.NCR > 0 ? (int)cdiv(w.NCH, w.NCR) : 0;
+  if (pass == 1) {
+    w.dP = c.take<void>(N * O * es);
+    w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    for (int p = 0; p < 3; ++p) w.pA[p] = c.take<float>(R * h * 16 * 4);
+    w.dB_part = c.take<float>(R * O * 16 * 4);
+  }
+  w.bytes = c.off;
+  return w;
+}
+
+// ---- validation ---------------------------------------------------------------
+int check_mlp(const lora_mlp_desc_t* d) {
+  if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
+  if (d->n_tokens <= 0 || d->hidden <= 0 || d->inter <= 0 || d->rank <= 0)
+    return fail(LORA_ERR_SHAPE, "sizes must be positive (n_tokens=%lld hidden=%d inter=%d rank=%d)",
+                (long long)d->n_tokens, d->hidden, d->inter, d->rank);
+  if (d->reserved != 0) return fail(LORA_ERR_SHAPE, "reserved field must be 0");
+  if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (d->act != LORA_SWIGLU && d->act != LORA_GEGLU_TANH)
+    return fail(LORA_ERR_UNSUPPORTED, "unsupported activation %d", d->act);
+  if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
+  if (d->n_tokens > (1L << 30) || (long)d->hidden * d->inter > (1L << 31))
+    return fail(LORA_ERR_UNSUPPORTED, "sizes beyond the 32-bit tile index range");
+  return LORA_OK;
+}
+int check_proj(const lora_proj_t* p, const char* name) {
+  if (!p || !p->W || !p->A || !p->B) return fail(LORA_ERR_NULL, "projection %s has a NULL pointer", name);
+  return LORA_OK;
+}
+int check_qkv(const lora_qkv_desc_t* d) {
+  if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
+  if (d->batch <= 0 || d->seq <= 0 || d->hidden <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->head_dim <= 0 ||
+      d->rank <= 0)
+    return fail(LORA_ERR_SHAPE, "sizes must be positive");
+  if (d->head_dim % 2) return fail(LORA_ERR_SHAPE, "head_dim %d is odd", d->head_dim);
+  if (d->n_q % d->n_kv) return fail(LORA_ERR_SHAPE, "n_q %% n_kv != 0 (%d, %d)", d->n_q, d->n_kv);
+  if (!(d->rope_theta > 0.0)) return fail(LORA_ERR_SHAPE, "rope_theta must be > 0");
+  if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (d->head_dim != 64 && d->head_dim != 128)
+    return fail(LORA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
+  if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
+  if ((long)d->batch * d->seq > (1L << 30)) return fail(LORA_ERR_UNSUPPORTED, "too many tokens");
+  return LORA_OK;
+}
+
+template <class T>
+struct DT;
+template <>
+struct DT<float> {
+  static constexpr int code = LORA_F32;
+};
+template <>
+struct DT<bf16> {
+  static constexpr int code = LORA_BF16;
+};
+
+// ---- MLP ----------------------------------------------------------------------
+template <class T, int ACT>
+int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, const lora_proj_t& u,
+                 const lora_proj_t& dn, void* Y, void* G, void* U, void* Tsv, const MlpWs& w, hipStream_t st) {
+  const long N = d.n_tokens;
+  const int h = d.hidden, i = d.inter, r = d.rank, V = vecw(DT<T>::code);
+  const int R = (int)cdiv(N, kBM);
+  float* T3 = static_cast<float*>(Tsv);
+  {
+    GateUpArgs a{};
+    a.X = X; a.Wg = g.W; a.Ag = g.A; a.Bg = g.B; a.Wu = u.W; a.Au = u.A; a.Bu = u.B;
+    a.sg = g.scale; a.su = u.scale;
+    a.G = G; a.U = U; a.H = w.H;
+    a.Tg = T3; a.Tu = T3 + N * r;
+    a.N = N; a.h = h; a.i = i; a.r = r;
+    a.vecA = (h % V == 0) && al16(X);
+    a.vecW = (h % V == 0) && al16(g.W) && al16(u.W);
+    a.vecS = (h % V == 0) && al16(g.A) && al16(u.A);
+    a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
+    a.R = R; a.NC = (int)cdiv(i, 128);
+    const int rc = launch(0, k_gateup_fwd<T, ACT>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    LinearArgs a{};
+    a.Z = w.H; a.W = dn.W; a.A = dn.A; a.B = dn.B; a.s = dn.scale;
+    a.Y = Y; a.T = T3 + 2 * N * r;
+    a.N = N; a.K = i; a.O = h; a.r = r;
+    a.vecA = (i % V == 0) && al16(w.H);
+    a.vecW = (i % V == 0) && al16(dn.W);
+    a.vecS = (i % V == 0) && al16(dn.A);
+    a.vecO = (h % 8 == 0) && al16(Y);
+    a.R = R; a.NC = (int)cdiv(h, kBN);
+    const int rc = launch(1, k_linear_fwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+template <class T, int ACT>
+int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const void* G, const void* U,
+                 const void* Tsv, const lora_proj_t& g, const lora_proj_t& u, const lora_proj_t& dn, void* dX,
+                 void* dAg, void* dBg, void* dAu, void* dBu, void* dAd, void* dBd, const MlpWs& w, hipStream_t st) {
+  const long N = d.n_tokens;
+  const int h = d.hidden, i = d.inter, r = d.rank, V = vecw(DT<T>::code);
+  const int R = (int)cdiv(N, kBM);
+  const float* T3 = static_cast<const float*>(Tsv);
+  {
+    ProArgs a{};
+    a.qkv = 0;
+    a.P = dY;
+    a.Bp[0] = dn.B; a.Tp[0] = T3 + 2 * N * r; a.s[0] = dn.scale;
+    a.off[0] = 0; a.off[1] = h; a.off[2] = h; a.off[3] = h;
+    a.nadp = 1;
+    a.dT_part = w.dT_part; a.dB_part = w.pB_d;
+    a.N = N; a.O = h; a.r = r;
+    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+    a.vecP = (h % V == 0) && al16(dY);
+    a.vecB = (r % V == 0) && al16(dn.B);
+    const int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    DownBwdArgs a{};
+    a.dY = dY; a.Wd = dn.W; a.Ad = dn.A; a.G = G; a.U = U;
+    a.Tg = T3; a.Tu = T3 + N * r;
+    a.dT_part = w.dT_part; a.NCR = w.NCR;
+    a.sg = g.scale; a.su = u.scale;
+    a.dG = w.dG; a.dU = w.dU;
+    a.pA_d = w.pA_d; a.pB_g = w.pB_g; a.pB_u = w.pB_u;
+    a.N = N; a.h = h; a.i = i; a.r = r;
+    a.vecA = (h % V == 0) && al16(dY);
+    a.vecW = (i % V == 0) && al16(dn.W);
+    a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
+    a.R = R; a.NC = (int)cdiv(i, kBN);
+    const int rc = launch(5, k_down_bwd<T, ACT>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    MlpDxArgs a{};
+    a.dG = w.dG; a.dU = w.dU; a.Wg = g.W; a.Wu = u.W; a.Bg = g.B; a.Bu = u.B; a.Ag = g.A; a.Au = u.A;
+    a.X = X; a.sg = g.scale; a.su = u.scale;
+    a.dX = dX; a.pA_g = w.pA_g; a.pA_u = w.pA_u;
+    a.N = N; a.h = h; a.i = i; a.r = r;
+    a.vecA = (i % V == 0) && al16(w.dG) && al16(w.dU);
+    a.vecW = (h % V == 0) && al16(g.W) && al16(u.W);
+    a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
+    a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
+    a.R = R; a.NC = (int)cdiv(h, kBN);
+    const int rc = launch(6, k_mlp_dx_bwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    RedArgs a{};
+    a.r = r;
+    a.njobs = 6;
+    const long si = (long)i * 16, sh = (long)h * 16;
+    a.job[0] = RedJob{w.pA_d, si, si, R, i, 1, dAd};
+    a.job[1] = RedJob{w.pB_g, si, si, R, i, 0, dBg};
+    a.job[2] = RedJob{w.pB_u, si, si, R, i, 0, dBu};
+    a.job[3] = RedJob{w.pA_g, sh, sh, R, h, 1, dAg};
+    a.job[4] = RedJob{w.pA_u, sh, sh, R, h, 1, dAu};
+    a.job[5] = RedJob{w.pB_d, sh, sh, R, h, 0, dBd};
+    const long mx = si > sh ? si : sh;
+    const int rc = launch(8, k_reduce<T>, dim3((unsigned)cdiv(mx, 256), 6), dim3(256), st, a);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+// ---- QKV -----------------------------------------------------------------------
+void qkv_offsets(const lora_qkv_desc_t& d, int (&off)[4], int (&nh)[3]) {
+  nh[0] = d.n_q; nh[1] = d.n_kv; nh[2] = d.n_kv;
+  off[0] = 0;
+  off[1] = d.n_q * d.head_dim;
+  off[2] = off[1] + d.n_kv * d.head_dim;
+  off[3] = off[2] + d.n_kv * d.head_dim;
+}
+
+int rope_table(const lora_qkv_desc_t& d, const QkvWs& w, hipStream_t st) {
+  const long n = (long)d.seq * (d.head_dim / 2);
+  return launch(2, k_rope_table, dim3((unsigned)cdiv(n, 256)), dim3(256), st, w.cs, w.sn, d.seq, d.head_dim / 2,
+                d.rope_theta);
+}
+
+template <class T>
+int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* const (&pr)[3], void* const (&out)[3],
+                 void* Tsv, const QkvWs& w, hipStream_t st) {
+  const long N = (long)d.batch * d.seq;
+  const int h = d.hidden, r = d.rank, V = vecw(DT<T>::code);
+  int rc = rope_table(d, w, st);
+  if (rc) return rc;
+  QKVFwdArgs a{};
+  a.X = X;
+  bool wal = true, aal = true, oal = true;
+  for (int p = 0; p < 3; ++p) {
+    a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.B[p] = pr[p]->B; a.s[p] = pr[p]->scale;
+    a.out[p] = out[p];
+    a.T[p] = static_cast<float*>(Tsv) + p * N * r;
+    wal = wal && al16(pr[p]->W);
+    aal = aal && al16(pr[p]->A);
+    oal = oal && al16(out[p]);
+  }
+  a.cs = w.cs; a.sn = w.sn;
+  a.N = N; a.h = h; a.S = d.seq; a.d = d.head_dim; a.r = r;
+  qkv_offsets(d, a.off, a.nh);
+  a.vecA = (h % V == 0) && al16(X);
+  a.vecW = (h % V == 0) && wal;
+  a.vecS = (h % V == 0) && aal;
+  a.vecO = oal;
+  a.R = (int)cdiv(N, kBM);
+  a.NC = (int)cdiv(a.off[3], kBN);
+  if (d.head_dim == 128) rc = launch(3, k_qkv_fwd<T, 1>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+  else rc = launch(3, k_qkv_fwd<T, 2>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+  if (rc) return rc;
+  return ok();
+}
+
+template <class T>
+int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const void* X, const void* Tsv,
+                 const lora_proj_t* const (&pr)[3], void* dX, void* const (&dA)[3], void* const (&dB)[3],
+                 const QkvWs& w, hipStream_t st) {
+  const long N = (long)d.batch * d.seq;
+  const int h = d.hidden, r = d.rank, V = vecw(DT<T>::code);
+  const int R = (int)cdiv(N, kBM);
+  int off[4], nh[3];
+  qkv_offsets(d, off, nh);
+  const int O = off[3];
+  int rc = rope_table(d, w, st);
+  if (rc) return rc;
+  {
+    ProArgs a{};
+    a.qkv = 1;
+    bool sal = true, bal = true;
+    for (int p = 0; p < 3; ++p) {
+      a.src[p] = dO[p];
+      a.nh[p] = nh[p];
+      a.Bp[p] = pr[p]->B;
+      a.Tp[p] = static_cast<const float*>(Tsv) + p * N * r;
+      a.s[p] = pr[p]->scale;
+      sal = sal && al16(dO[p]);
+      bal = bal && al16(pr[p]->B);
+    }
+    a.cs = w.cs; a.sn = w.sn; a.S = d.seq; a.d = d.head_dim;
+    a.dP = w.dP;
+    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+    a.nadp = 3;
+    a.dT_part = w.dT_part; a.dB_part = w.dB_part;
+    a.N = N; a.O = O; a.r = r;
+    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+    a.vecP = sal;
+    a.vecB = (r % V == 0) && bal;
+    rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    QkvDxArgs a{};
+    a.dP = w.dP;
+    bool wal = true;
+    for (int p = 0; p < 3; ++p) {
+      a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.pA[p] = w.pA[p];
+      wal = wal && al16(pr[p]->W);
+    }
+    a.dT_part = w.dT_part; a.NCR = w.NCR;
+    a.X = X; a.dX = dX;
+    a.N = N; a.h = h; a.O = O; a.r = r;
+    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+    a.vecA = (O % V == 0);
+    a.vecW = (h % V == 0) && wal;
+    a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
+    a.R = R; a.NC = (int)cdiv(h, kBN);
+    rc = launch(7, k_qkv_dx_bwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    RedArgs a{};
+    a.r = r;
+    a.njobs = 6;
+    const long sh = (long)h * 16, so = (long)O * 16;
+    long mx = sh;
+    for (int p = 0; p < 3; ++p) {
+      a.job[p] = RedJob{w.pA[p], sh, sh, R, h, 1, dA[p]};
+      const long cnt = (long)(off[p + 1] - off[p]) * 16;
+      a.job[3 + p] = RedJob{w.dB_part + (long)off[p] * 16, so, cnt, R, off[p + 1] - off[p], 0, dB[p]};
+      if (cnt > mx) mx = cnt;
+    }
+    rc = launch(8, k_reduce<T>, dim3((unsigned)cdiv(mx, 256), 6), dim3(256), st, a);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
+}  // namespace
+
+// =============================================================================
+// C ABI
+// =============================================================================
+extern "C" {
+
+size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass) {
+  if (check_mlp(desc) != LORA_OK || (pass != 0 && pass != 1)) return 0;
+  return mlp_ws(*desc, pass, nullptr).bytes;
+}
+
+size_t lora_qkv_workspace_bytes(const lora_qkv_desc_t* desc, int pass) {
+  if (check_qkv(desc) != LORA_OK || (pass != 0 && pass != 1)) return 0;
+  return qkv_ws(*desc, pass, nullptr).bytes;
+}
+
+int lora_mlp_fwd(const lora_mlp_desc_t* desc, const void* X, const lora_proj_t* gate, const lora_proj_t* up,
+                 const lora_proj_t* down, void* Y, void* G, void* U, void* T, void* workspace,
+                 size_t workspace_bytes, void* hip_stream) {
+  int rc = check_mlp(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(gate, "gate")) || (rc = check_proj(up, "up")) || (rc = check_proj(down, "down"))) return rc;
+  if (!X || !Y || !G || !U || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const MlpWs probe = mlp_ws(*desc, 0, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const MlpWs w = mlp_ws(*desc, 0, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (desc->dtype == LORA_BF16) {
+    if (desc->act == LORA_SWIGLU) return mlp_fwd_impl<bf16, 0>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+    return mlp_fwd_impl<bf16, 1>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+  }
+  if (desc->act == LORA_SWIGLU) return mlp_fwd_impl<float, 0>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+  return mlp_fwd_impl<float, 1>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+}
+
+int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X, const void* G, const void* U,
+                 const void* T, const lora_proj_t* gate, const lora_proj_t* up, const lora_proj_t* down, void* dX,
+                 void* dA_gate, void* dB_gate, void* dA_up, void* dB_up, void* dA_down, void* dB_down,
+                 void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_mlp(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(gate, "gate")) || (rc = check_proj(up, "up")) || (rc = check_proj(down, "down"))) return rc;
+  if (!dY || !X || !G || !U || !T || !dX || !dA_gate || !dB_gate || !dA_up || !dB_up || !dA_down || !dB_down)
+    return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const MlpWs probe = mlp_ws(*desc, 1, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const MlpWs w = mlp_ws(*desc, 1, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+#define LORA_MLP_BWD(TT, AA)                                                                                    \
+  return mlp_bwd_impl<TT, AA>(*desc, dY, X, G, U, T, *gate, *up, *down, dX, dA_gate, dB_gate, dA_up, dB_up, \
+                              dA_down, dB_down, w, st)
+  if (desc->dtype == LORA_BF16) {
+    if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(bf16, 0);
+    LORA_MLP_BWD(bf16, 1);
+  }
+  if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(float, 0);
+  LORA_MLP_BWD(float, 1);
+#undef LORA_MLP_BWD
+}
+
+int lora_qkv_fwd(const lora_qkv_desc_t* desc, const void* X, const lora_proj_t* q, const lora_proj_t* k,
+                 const lora_proj_t* v, void* Q, void* K, void* V, void* T, void* workspace, size_t workspace_bytes,
+                 void* hip_stream) {
+  int rc = check_qkv(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
+  if (!X || !Q || !K || !V || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const QkvWs probe = qkv_ws(*desc, 0, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const QkvWs w = qkv_ws(*desc, 0, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const lora_proj_t* const pr[3] = {q, k, v};
+  void* const out[3] = {Q, K, V};
+  if (desc->dtype == LORA_BF16) return qkv_fwd_impl<bf16>(*desc, X, pr, out, T, w, st);
+  return qkv_fwd_impl<float>(*desc, X, pr, out, T, w, st);
+}
+
+int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, const void* dV, const void* X,
+                 const void* T, const lora_proj_t* q, const lora_proj_t* k, const lora_proj_t* v, void* dX,
+                 void* dA_q, void* dB_q, void* dA_k, void* dB_k, void* dA_v, void* dB_v, void* workspace,
+                 size_t workspace_bytes, void* hip_stream) {
+  int rc = check_qkv(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
+  if (!dQ || !dK || !dV || !X || !T || !dX || !dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v)
+    return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const QkvWs probe = qkv_ws(*desc, 1, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const QkvWs w = qkv_ws(*desc, 1, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const lora_proj_t* const pr[3] = {q, k, v};
+  const void* const dO[3] = {dQ, dK, dV};
+  void* const dA[3] = {dA_q, dA_k, dA_v};
+  void* const dB[3] = {dB_q, dB_k, dB_v};
+  if (desc->dtype == LORA_BF16) return qkv_bwd_impl<bf16>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
+  return qkv_bwd_impl<float>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
+}
+
+const char* lora_status_string(int status) {
+  switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL: return "null pointer";
+    case LORA_ERR_SHAPE: return "bad shape";
+    case LORA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case LORA_ERR_WORKSPACE: return "workspace too small";
+    case LORA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* lora_last_error_message(void) { return g_err; }
+
+const char* lora_version(void) { return "lora_mi355x 0.1 (gfx950)"; }
+
+int lora_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tm);
+  g_timing = on != 0;
+  return LORA_OK;
+}
+
+int lora_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tm);
+  for (auto& r : g_recs) {
+    g_pool.push_back(r.e0);
+    g_pool.push_back(r.e1);
+  }
+  g_recs.clear();
+  return LORA_OK;
+}
+
+int lora_timing_query(const char* kernel, double* total_ms, int* launches) {
+  if (!kernel || !total_ms || !launches) return fail(LORA_ERR_NULL, "NULL argument");
+  const int kid = kernel_id(kernel);
+  if (kid < 0) return fail(LORA_ERR_SHAPE, "unknown kernel name %s", kernel);
+  std::lock_guard<std::mutex> lk(g_tm);
+  double tot = 0.0;
+  int n = 0;
+  for (auto& r : g_recs) {
+    if (r.kernel != kid) continue;
+    if (hipEventSynchronize(r.e1) != hipSuccess) return fail(LORA_ERR_HIP, "event synchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) return fail(LORA_ERR_HIP, "event elapsed failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return ok();
+}
+
+const char* lora_kernel_names(void) {
+  static std::string s;
+  static std::once_flag once;
+  std::call_once(once, [] {
+    for (int i = 0; i < kNumNames; ++i) {
+      if (i) s += ",";
+      s += kNames[i];
+    }
+  });
+  return s.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+"""Shared helpers for the GPU parity tests: run the HIP path through the C ABI
+binding on seeded inputs and the CPU oracle on the same values, and compare.
+
+Tolerance (per output tensor): max|gpu - ref| / max|ref| <= 2e-2 in bf16 mode
+and <= 1e-5 in fp32 mode.
+"""
+from __future__ import annotations
+
+import dataclasses
+import sys
+
+import numpy as np
+import torch
+
+from lora_fine_tuning_mlp_amd import binding as B
+from lora_fine_tuning_mlp_amd import synthetic as S
+from oracle import lora_oracle as orc
+
+TOL = {"bf16": 2e-2, "f32": 1e-5}
+
+
+def say(msg: str) -> None:
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def rel_err(gpu: np.ndarray, ref: np.ndarray) -> float:
+    den = float(np.max(np.abs(ref)))
+    num = float(np.max(np.abs(gpu - ref)))
+    if den == 0.0:
+        return num
+    return num / den
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------
+# Small parity configurations: several tiles and a ragged tail in every
+# dimension the kernels tile (tokens 256, columns 256 or 128, K 64 or 32).
+# ---------------------------------------------------------------------------
+MLP_CASES = [
+    S.C0,
+    S.MLPConfig("mlp_bf16_ragged", 600, 384, 640, 16, 2.0, "swiglu", "bf16"),
+    S.MLPConfig("mlp_bf16_geglu_unaligned", 300, 196, 300, 5, 2.0, "geglu_tanh", "bf16"),
+    S.MLPConfig("mlp_f32_mid", 520, 256, 384, 8, 2.0, "swiglu", "f32"),
+    S.MLPConfig("mlp_f32_geglu_ragged", 100, 72, 150, 3, 1.5, "geglu_tanh", "f32"),
+    S.MLPConfig("mlp_bf16_long_k", 256, 1024, 512, 16, 2.0, "geglu_tanh", "bf16"),
+]
+QKV_CASES = [
+    S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
+    S.QKVConfig("qkv_bf16_d128", 1, 520, 256, 4, 2, 128, 16, 2.0, 1.0e6, "bf16"),
+    S.QKVConfig("qkv_f32_d64", 2, 100, 192, 4, 4, 64, 4, 2.0, 1.0e4, "f32"),
+    S.QKVConfig("qkv_bf16_c4heads_ragged", 3, 77, 200, 14, 2, 64, 16, 2.0, 1.0e6, "bf16"),
+    S.QKVConfig("qkv_f32_d128", 1, 40, 128, 2, 1, 128, 16, 0.5, 1.0e4, "f32"),
+]
+
+
+def mlp_scales(cfg):
+    return (cfg.scale, cfg.scale, cfg.scale)
+
+
+def run_mlp_gpu(cfg: S.MLPConfig, t_cpu, dY_cpu=None, scales=None):
+    scales = scales or mlp_scales(cfg)
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev).contiguous() for k, v in t_cpu.items() if k != "dY"}
+    m = B.MLP(t, cfg.n_tokens, cfg.hidden, cfg.inter, cfg.rank, cfg.dtype, cfg.act, scales)
+    m.forward()
+    dY = (dY_cpu if dY_cpu is not None else t_cpu["dY"]).to(dev).contiguous()
+    m.backward(dY)
+    torch.cuda.synchronize()
+    out = {"Y": to64(m.Y), "G": to64(m.G), "U": to64(m.U),
+           "T_gate": to64(m.T[0]), "T_up": to64(m.T[1]), "T_down": to64(m.T[2]), "dX": to64(m.dX)}
+    out.update({k: to64(v) for k, v in m.grads.items()})
+    return out
+
+
+def run_mlp_oracle(cfg: S.MLPConfig, t_cpu, dY_cpu=None, scales=None, rows=None):
+    """Oracle on all tokens, or on the subset `rows` (outputs are per token;
+    with dY zero outside `rows` the adapter gradients are exact too)."""
+    scales = scales or mlp_scales(cfg)
+    p = S.to_f64({k: v for k, v in t_cpu.items() if k != "dY"})
+    dY = (dY_cpu if dY_cpu is not None else t_cpu["dY"]).to(torch.float64).numpy()
+    if rows is not None:
+        p["X"] = p["X"][rows]
+        dY = dY[rows]
+    f = orc.mlp_fwd(p, cfg.act, *scales)
+    g = orc.mlp_bwd(p, dY, cfg.act, *scales)
+    ref = {"Y": f["Y"], "G": f["G"], "U": f["U"], "T_gate": f["T_gate"], "T_up": f["T_up"],
+           "T_down": f["T_down"], "dX": g["dX"]}
+    for n in ("gate", "up", "down"):
+        ref["dA_" + n] = g["dA_" + n]
+        ref["dB_" + n] = g["dB_" + n]
+    return ref
+
+
+def run_qkv_gpu(cfg: S.QKVConfig, t_cpu, grads_cpu=None, scales=None):
+    scales = scales or (cfg.scale,) * 3
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev).contiguous() for k, v in t_cpu.items() if k not in ("dQ", "dK", "dV")}
+    m = B.QKV(t, cfg.batch, cfg.seq, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.rank, cfg.dtype, cfg.theta,
+              scales)
+    m.forward()
+    gc = grads_cpu if grads_cpu is not None else t_cpu
+    m.backward(gc["dQ"].to(dev).contiguous(), gc["dK"].to(dev).contiguous(), gc["dV"].to(dev).contiguous())
+    torch.cuda.synchronize()
+    out = {"Q": to64(m.Q), "K": to64(m.K), "V": to64(m.V), "T_q": to64(m.T[0]), "T_k": to64(m.T[1]),
+           "T_v": to64(m.T[2]), "dX": to64(m.dX)}
+    out.update({k: to64(v) for k, v in m.grads.items()})
+    return out
+
+
+def run_qkv_oracle(cfg: S.QKVConfig, t_cpu, grads_cpu=None, scales=None):
+    scales = scales or (cfg.scale,) * 3
+    p = S.to_f64({k: v for k, v in t_cpu.items() if k not in ("dQ", "dK", "dV")})
+    gc = grads_cpu if grads_cpu is not None else t_cpu
+    dQ, dK, dV = (gc[k].to(torch.float64).numpy() for k in ("dQ", "dK", "dV"))
+    shape = dict(batch=cfg.batch, seq=cfg.seq, n_q=cfg.n_q, n_kv=cfg.n_kv, head_dim=cfg.head_dim, theta=cfg.theta)
+    f = orc.qkv_fwd(p, scales=scales, **shape)
+    g = orc.qkv_bwd(p, dQ, dK, dV, scales=scales, **shape)
+    ref = {"Q": f["Q"], "K": f["K"], "V": f["V"], "T_q": f["T_q"], "T_k": f["T_k"], "T_v": f["T_v"],
+           "dX": g["dX"]}
+    for n in "qkv":
+        ref["dA_" + n] = g["dA_" + n]
+        ref["dB_" + n] = g["dB_" + n]
+    return ref
+
+
+def compare(name: str, gpu, ref, tol: float, keys=None):
+    """Assert every tensor within tol; returns the per-tensor errors."""
+    errs = {}
+    bad = []
+    for k in keys or ref:
+        a, b = gpu[k], ref[k]
+        assert a.shape == b.shape, (name, k, a.shape, b.shape)
+        if not np.all(np.isfinite(a)):
+            bad.append((k, "non-finite"))
+            continue
+        e = rel_err(a, b)
+        errs[k] = e
+        if e > tol:
+            bad.append((k, e))
+    say(f"{name}: " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
+    assert not bad, f"{name}: out of tolerance {tol}: {bad}"
+    return errs
