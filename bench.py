@@ -1,0 +1,225 @@
+"""Benchmark: fused LoRA QKV + MLP forward and backward on one MI355X.
+
+One step = LoRA QKV + RoPE fwd+bwd at 4 x 2048 tokens, h = 4096, 32/8 heads of
+128, r = 8, plus LoRA MLP (SwiGLU) fwd+bwd at 8192 tokens, h = 4096,
+i = 14336, r = 16, all bf16 with fp32 accumulation, on seeded synthetic
+inputs resident in HBM.  Throughput is algorithmic FLOPs (frozen base weights:
+no dW; elementwise work not counted) per second.
+
+Prints one JSON line.  Besides the headline value it carries
+  roofline:      the dominant kernel's achieved TFLOP/s against the bf16
+                 dense MFMA peak, timed live with HIP events around each launch
+                 on the stream it runs on;
+  cpu_baseline:  the CPU float64 oracle timed on a bounded token sample of the
+                 same workload (rank 0, N = 1 only).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "LoRA MLP+QKV fwd+bwd TFLOP/s and % bf16 MFMA peak, 8192 tokens, h=4096"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA (no sparsity)
+PEAK_HBM_GBS = 8000.0
+
+
+def kernel_flops(qkv, mlp):
+    """Algorithmic FLOPs per launch of each kernel at these shapes (no dW,
+    rank-r work counted once, elementwise not counted)."""
+    N, h, i, r = mlp.n_tokens, mlp.hidden, mlp.inter, mlp.rank
+    Nq, hq, rq = qkv.n_tokens, qkv.hidden, qkv.rank
+    O = sum(qkv.out_dims)
+    return {
+        "k_gateup_fwd": 4 * N * h * i + 4 * N * h * r + 4 * N * r * i,
+        "k_linear_fwd": 2 * N * i * h + 2 * N * i * r + 2 * N * r * h,
+        "k_qkv_fwd": 2 * Nq * hq * O + 6 * Nq * hq * rq + 2 * Nq * rq * O,
+        "k_down_bwd": 2 * N * h * i + 8 * N * r * i,
+        "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h,
+        "k_qkv_dx_bwd": 2 * Nq * O * hq + 12 * Nq * rq * hq,
+    }
+
+
+def source_hash(kernel: str) -> str:
+    """Hash of the HIP sources (used to tell whether stored counters are stale)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "lora_fine_tuning_mlp_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current sources (else None)."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p))
+    except ValueError:
+        return None
+    ent = d.get(kernel)
+    if not ent or ent.get("source_hash") != source_hash(kernel):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
+    """Time the CPU oracle (as it stands) on `tokens` tokens of each workload."""
+    import dataclasses
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from lora_fine_tuning_mlp_amd import synthetic as S
+    from oracle import lora_oracle as orc
+
+    mlp_s = dataclasses.replace(mlp_cfg, n_tokens=tokens)
+    qkv_s = dataclasses.replace(qkv_cfg, batch=1, seq=tokens)
+    tm = S.mlp_inputs(mlp_s, 0)
+    tq = S.qkv_inputs(qkv_s, 0)
+    pm = S.to_f64({k: v for k, v in tm.items() if k != "dY"})
+    dY = tm["dY"].double().numpy()
+    pq = S.to_f64({k: v for k, v in tq.items() if k not in ("dQ", "dK", "dV")})
+    dQ, dK, dV = (tq[k].double().numpy() for k in ("dQ", "dK", "dV"))
+    shape = dict(batch=1, seq=tokens, n_q=qkv_s.n_q, n_kv=qkv_s.n_kv, head_dim=qkv_s.head_dim, theta=qkv_s.theta)
+    sc = (qkv_s.scale,) * 3
+    t0 = time.perf_counter()
+    orc.qkv_fwd(pq, scales=sc, **shape)
+    orc.qkv_bwd(pq, dQ, dK, dV, scales=sc, **shape)
+    orc.mlp_fwd(pm, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
+    orc.mlp_bwd(pm, dY, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
+    dt = time.perf_counter() - t0
+    flops = qkv_s.flops() + mlp_s.flops()
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{tokens} tokens of each workload (QKV as 1 x {tokens}, positions 0..{tokens - 1}; MLP {tokens} rows), "
+                  f"float64 numpy, {dt:.2f} s wall",
+        "seconds": dt,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the CPU oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this size (calibrates rocprofv3 byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this build has no "
+              f"multi-GPU path: the projections are data-parallel over tokens and would shard as described in the "
+              f"design notes.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from lora_fine_tuning_mlp_amd import binding as B
+    from lora_fine_tuning_mlp_amd import synthetic as S
+
+    qkv_cfg, mlp_cfg = S.C1, S.C2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] generating inputs ({qkv_cfg.name}, {mlp_cfg.name})", file=sys.stderr, flush=True)
+    tq = {k: v.to(dev) for k, v in S.qkv_inputs(qkv_cfg, 0).items()}
+    tm = {k: v.to(dev) for k, v in S.mlp_inputs(mlp_cfg, 0).items()}
+    qkv = B.QKV({k: v for k, v in tq.items() if k not in ("dQ", "dK", "dV")}, qkv_cfg.batch, qkv_cfg.seq,
+                qkv_cfg.hidden, qkv_cfg.n_q, qkv_cfg.n_kv, qkv_cfg.head_dim, qkv_cfg.rank, qkv_cfg.dtype,
+                qkv_cfg.theta, (qkv_cfg.scale,) * 3)
+    mlp = B.MLP({k: v for k, v in tm.items() if k != "dY"}, mlp_cfg.n_tokens, mlp_cfg.hidden, mlp_cfg.inter,
+                mlp_cfg.rank, mlp_cfg.dtype, mlp_cfg.act, (mlp_cfg.scale,) * 3)
+    dQ, dK, dV, dY = tq["dQ"], tq["dK"], tq["dV"], tm["dY"]
+
+    def step():
+        qkv.forward()
+        qkv.backward(dQ, dK, dV)
+        mlp.forward()
+        mlp.backward(dY)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # Timed region: HIP events on the library's stream around the K steps, and
+    # the library's own per-launch events for the per-kernel roofline.
+    stream = torch.cuda.current_stream()
+    B.timing_reset()
+    B.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    B.timing_enable(False)
+    total_ms = e0.elapsed_time(e1)
+    ms_per_step = total_ms / args.steps
+    flops_step = qkv_cfg.flops() + mlp_cfg.flops()
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+
+    per_kernel = {}
+    for name in B.kernel_names():
+        ms, n = B.timing_query(name)
+        if n:
+            per_kernel[name] = {"total_ms": ms, "launches": n, "avg_us": 1e3 * ms / n}
+    kf = kernel_flops(qkv_cfg, mlp_cfg)
+    dominant = max((k for k in per_kernel if k in kf), key=lambda k: per_kernel[k]["total_ms"])
+    avg_s = per_kernel[dominant]["avg_us"] * 1e-6
+    achieved = kf[dominant] / avg_s / 1e12
+    for k in per_kernel:
+        if k in kf:
+            pk = per_kernel[k]
+            pk["tflops"] = kf[k] / (pk["avg_us"] * 1e-6) / 1e12
+            pk["frac_peak"] = pk["tflops"] / PEAK_BF16_TFLOPS
+    traffic = stored_traffic(dominant)
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dominant,
+                "flops_per_launch": kf[dominant], "avg_launch_us": round(per_kernel[dominant]["avg_us"], 2)}
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, device=dev, dtype=torch.float32).fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded normals: X, dY ~N(0,1); W std 0.02; A var 1/in; B std 0.02)",
+        "config": {"workload": "lora_qkv_rope_c1 + lora_mlp_swiglu_c2 fwd+bwd", "tokens": mlp_cfg.n_tokens,
+                   "hidden": mlp_cfg.hidden, "inter": mlp_cfg.inter, "mlp_rank": mlp_cfg.rank,
+                   "qkv_heads": f"{qkv_cfg.n_q}/{qkv_cfg.n_kv}x{qkv_cfg.head_dim}", "qkv_rank": qkv_cfg.rank,
+                   "rope_theta": qkv_cfg.theta, "flops_per_step": flops_step},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in per_kernel.items()},
+    }
+    if not args.no_cpu_baseline:
+        print(f"[bench] cpu oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(qkv_cfg, mlp_cfg, args.cpu_tokens)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -21,6 +21,8 @@
 //   k_reduce        fixed-order sum of partials -> dA / dB in the call dtype.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace lora {
@@ -246,11 +248,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
 // Fill Ts[slot][m][t] = sum over column ranges of the prologue's dT partials.
 __device__ __forceinline__ void load_dT(char* smem, const float* dT_part, int NCR, long N, long m0, int nslot) {
   float* Ts = ts_ptr(smem);
-  const int m = threadIdx.x;
+  const int m = threadIdx.x & (kBM - 1), th = (threadIdx.x >> 8) * 8;   // row, half of the ranks
   const long n = m0 + m;
   for (int sl = 0; sl < nslot; ++sl)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = th; t < th + 8; ++t) {
       float v = 0.f;
       if (n < N)
         for (int c = 0; c < NCR; ++c) v += dT_part[(((long)c * 3 + sl) * N + n) * 16 + t];
@@ -275,9 +277,15 @@ struct DownBwdArgs {
   int R, NC;
 };
 
-template <class T, int ACT>
-__global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
-  __shared__ __align__(16) char smem[kGemmLds];
+// dH parking area of the bf16 epilogue: 16 quads x 512 threads x 16 bytes
+// after Ts slot 0 (the only side slot this kernel uses).
+constexpr int kParkOff = kBM * kSlot * 4;
+constexpr int kDownBwdLds = kParkOff + 16 * kGemmThreads * 16;   // 147456
+static_assert(kDownBwdLds >= kGemmLds && kDownBwdLds <= 163840, "k_down_bwd LDS");
+
+template <class T, int ACT, bool FAST>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
+  __shared__ __align__(16) char smem[kDownBwdLds];
   const WaveId q = wave_id();
   int rb, cb;
   tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
@@ -287,13 +295,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
   const T* Wd = static_cast<const T*>(a.Wd);
   const long h = a.h, ni = a.i;
 
-  KNLoader<T, RowsA<T>, 0, KRow1<T>, SRowNone<T>, SMaskNone> ld;
-  ld.a.init(dY, h, a.N, m0, h, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  KNLoader<T, AOp, 0, KRow1<T>, SRowNone<T>, SMaskNone> ld;
+  ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
   ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
   ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
 
-  f32x4 acc[8][8];
-  f32x4 sacc[1][8];
+  f32x4 acc[kMB][8];
+  f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
   kloop<T, 0>(smem, nkt, ld, acc, sacc);
@@ -309,7 +318,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
   const float fs[kMaxSide] = {1.f, 0.f, 0.f};
   fold<T>(smem, acc, 1, fs, fb);
 
-  // Epilogue: lane holds dH[row][c0 + nb], nb = 0..7.
+  // Epilogue: lane holds dH[row][c0 + nb], nb = 0..7.  For bf16 the dH tile
+  // is parked in LDS first (quad mb*4+j of this thread: 8 bf16), which frees
+  // the accumulator registers for the GLU backward and the three partials.
+  u32x4* park = reinterpret_cast<u32x4*>(smem + kParkOff);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
+        park[(mb * 4 + j) * kGemmThreads + q.tid] = pack(v);
+      }
+  }
   const T* Gs = static_cast<const T*>(a.G);
   const T* Us = static_cast<const T*>(a.U);
   T* dGo = static_cast<T*>(a.dG);
@@ -323,75 +346,97 @@ __global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
+  // GLU backward of one row: H, dG, dU for the lane's 8 columns; stores dG, dU.
+  auto glu_row = [&](int mb, int j, float (&h8)[8], float (&dg8)[8], float (&du8)[8]) {
+    const long row = m0 + acc_row(q, mb, j);
+    const bool live = row < a.N && nvalid > 0;
+    float G8[8], U8[8], dH8[8];
+    if (live) {
+      load_row8<T>(Gs + row * ni, c0, ni, a.vecO, G8);
+      load_row8<T>(Us + row * ni, c0, ni, a.vecO, U8);
+    } else {
 #pragma unroll
-  for (int mp = 0; mp < 4; ++mp) {
-    float hv[8][8], gv[8][8], uv[8][8];    // [slot = mbl*4 + j][nb]
+      for (int e = 0; e < 8; ++e) { G8[e] = 0.f; U8[e] = 0.f; }
+    }
+    if constexpr (sizeof(T) == 2) {
+      unpack(park[(mb * 4 + j) * kGemmThreads + q.tid], dH8);
+    } else {
 #pragma unroll
-    for (int mbl = 0; mbl < 2; ++mbl)
+      for (int nb = 0; nb < 8; ++nb) dH8[nb] = acc[mb][nb][j];
+    }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int mb = 2 * mp + mbl, sl = mbl * 4 + j;
-        const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
-        float G8[8], U8[8];
-        if (row < a.N && nvalid > 0) {
-          const u32x4 g0 = gload<T>(Gs + row * ni, c0, ni, a.vecO);
-          const u32x4 u0 = gload<T>(Us + row * ni, c0, ni, a.vecO);
-          if constexpr (sizeof(T) == 2) {
-            unpack(g0, G8);
-            unpack(u0, U8);
-          } else {
-            const u32x4 g1 = gload<T>(Gs + row * ni, c0 + 4, ni, a.vecO);
-            const u32x4 u1 = gload<T>(Us + row * ni, c0 + 4, ni, a.vecO);
-            float t4[4];
-            unpack(g0, t4); for (int e = 0; e < 4; ++e) G8[e] = t4[e];
-            unpack(g1, t4); for (int e = 0; e < 4; ++e) G8[4 + e] = t4[e];
-            unpack(u0, t4); for (int e = 0; e < 4; ++e) U8[e] = t4[e];
-            unpack(u1, t4); for (int e = 0; e < 4; ++e) U8[4 + e] = t4[e];
-          }
-        } else {
+    for (int nb = 0; nb < 8; ++nb) {
+      float ph, dph;
+      act_both<ACT>(G8[nb], ph, dph);
+      dg8[nb] = dH8[nb] * U8[nb] * dph;
+      du8[nb] = dH8[nb] * ph;
+      h8[nb] = ph * U8[nb];
+    }
+    if (live) {
+      store_row8<T>(dGo + row * ni + c0, dg8, nvalid, a.vecO);
+      store_row8<T>(dUo + row * ni + c0, du8, nvalid, a.vecO);
+    }
+  };
+
 #pragma unroll
-          for (int e = 0; e < 8; ++e) { G8[e] = 0.f; U8[e] = 0.f; }
-        }
-        float dg8[8], du8[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          float ph, dph;
-          act_both<ACT>(G8[nb], ph, dph);
-          const float dh = acc[mb][nb][j];
-          dg8[nb] = dh * U8[nb] * dph;
-          du8[nb] = dh * ph;
-          hv[sl][nb] = ph * U8[nb];
-          gv[sl][nb] = dg8[nb];
-          uv[sl][nb] = du8[nb];
-        }
-        if (row < a.N && nvalid > 0) {
-          store_row8<T>(dGo + row * ni + c0, dg8, nvalid, a.vecO);
-          store_row8<T>(dUo + row * ni + c0, du8, nvalid, a.vecO);
-        }
-      }
+  for (int mp = 0; mp < kMB / 2; ++mp) {
     // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
-    // (s T_g), (s T_u) and dG, dU.  K = the 8 rows of this lane group.
-    const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q.wm, mp, q.g, q.r16);
+    // (s T_g), (s T_u) and dG, dU.  K slots = the 8 rows (mb pair, j) of this lane group.
+    const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q, mp);
     float tg[8], tu[8];
 #pragma unroll
     for (int mbl = 0; mbl < 2; ++mbl)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const long row = m0 + q.wm * 128 + (2 * mp + mbl) * 16 + 4 * q.g + j;
+        const long row = m0 + acc_row(q, 2 * mp + mbl, j);
         const bool ok = row < a.N && q.r16 < a.r;
         tg[mbl * 4 + j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
         tu[mbl * 4 + j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
       }
     const Frag<T> aTg = make_frag<T>(tg);
     const Frag<T> aTu = make_frag<T>(tu);
+    if constexpr (sizeof(T) == 2) {
+      unsigned fh[8][4], fg[8][4], fu[8][4];     // [nb][dword]: slots (2d, 2d+1)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      float b0[8], b1[8], b2[8];
+      for (int mbl = 0; mbl < 2; ++mbl)
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) { b0[sl] = hv[sl][nb]; b1[sl] = gv[sl][nb]; b2[sl] = uv[sl][nb]; }
-      pacc[0][nb] = mma(pacc[0][nb], adT, make_frag<T>(b0));
-      pacc[1][nb] = mma(pacc[1][nb], aTg, make_frag<T>(b1));
-      pacc[2][nb] = mma(pacc[2][nb], aTu, make_frag<T>(b2));
+        for (int jp = 0; jp < 2; ++jp) {
+          float h0[8], g0[8], u0[8], h1[8], g1[8], u1[8];
+          glu_row(2 * mp + mbl, 2 * jp, h0, g0, u0);
+          glu_row(2 * mp + mbl, 2 * jp + 1, h1, g1, u1);
+          const int d = mbl * 2 + jp;
+#pragma unroll
+          for (int nb = 0; nb < 8; ++nb) {
+            fh[nb][d] = pack_bf2(h0[nb], h1[nb]);
+            fg[nb][d] = pack_bf2(g0[nb], g1[nb]);
+            fu[nb][d] = pack_bf2(u0[nb], u1[nb]);
+          }
+        }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        Frag<T> b0, b1, b2;
+        b0.v = (u32x4){fh[nb][0], fh[nb][1], fh[nb][2], fh[nb][3]};
+        b1.v = (u32x4){fg[nb][0], fg[nb][1], fg[nb][2], fg[nb][3]};
+        b2.v = (u32x4){fu[nb][0], fu[nb][1], fu[nb][2], fu[nb][3]};
+        pacc[0][nb] = mma(pacc[0][nb], adT, b0);
+        pacc[1][nb] = mma(pacc[1][nb], aTg, b1);
+        pacc[2][nb] = mma(pacc[2][nb], aTu, b2);
+      }
+    } else {
+      float hv[8][8], gv[8][8], uv[8][8];    // [slot = mbl*4 + j][nb]
+#pragma unroll
+      for (int mbl = 0; mbl < 2; ++mbl)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) glu_row(2 * mp + mbl, j, hv[mbl * 4 + j], gv[mbl * 4 + j], uv[mbl * 4 + j]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        float b0[8], b1[8], b2[8];
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) { b0[sl] = hv[sl][nb]; b1[sl] = gv[sl][nb]; b2[sl] = uv[sl][nb]; }
+        pacc[0][nb] = mma(pacc[0][nb], adT, make_frag<T>(b0));
+        pacc[1][nb] = mma(pacc[1][nb], aTg, make_frag<T>(b1));
+        pacc[2][nb] = mma(pacc[2][nb], aTu, make_frag<T>(b2));
+      }
     }
   }
   float* const parts[3] = {a.pA_d + (long)rb * ni * 16, a.pB_g + (long)rb * ni * 16, a.pB_u + (long)rb * ni * 16};
@@ -402,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_down_bwd(DownBwdArgs a) {
 // Shared dX epilogue: store dX, then dA_p partials = (scale_p Ts_p)^T . X.
 // ===========================================================================
 template <class T, int NA>
-__device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[8][8], const float (&escale)[kMaxSide],
+__device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], const float (&escale)[kMaxSide],
                                             const T* X, T* dX, float* const (&parts)[NA], long N, long h, long m0,
                                             long n0, bool vecO) {
   const WaveId q = wave_id();
@@ -415,29 +460,21 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[8][8], cons
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mp = 0; mp < 4; ++mp) {
+  for (int mp = 0; mp < kMB / 2; ++mp) {
     float xv[8][8];   // [slot][nb]
 #pragma unroll
     for (int mbl = 0; mbl < 2; ++mbl)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int mb = 2 * mp + mbl, sl = mbl * 4 + j;
-        const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+        const long row = m0 + acc_row(q, mb, j);
         float X8[8];
         if (row < N && nvalid > 0) {
           float v[8];
 #pragma unroll
           for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
           store_row8<T>(dX + row * h + c0, v, nvalid, vecO);
-          const u32x4 x0 = gload<T>(X + row * h, c0, h, vecO);
-          if constexpr (sizeof(T) == 2) {
-            unpack(x0, X8);
-          } else {
-            const u32x4 x1 = gload<T>(X + row * h, c0 + 4, h, vecO);
-            float t4[4];
-            unpack(x0, t4); for (int e = 0; e < 4; ++e) X8[e] = t4[e];
-            unpack(x1, t4); for (int e = 0; e < 4; ++e) X8[4 + e] = t4[e];
-          }
+          load_row8<T>(X + row * h, c0, h, vecO, X8);
         } else {
 #pragma unroll
           for (int e = 0; e < 8; ++e) X8[e] = 0.f;
@@ -447,7 +484,7 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[8][8], cons
       }
     Frag<T> adT[NA];
 #pragma unroll
-    for (int o = 0; o < NA; ++o) adT[o] = ts_frag<T>(Ts, o, escale[o], q.wm, mp, q.g, q.r16);
+    for (int o = 0; o < NA; ++o) adT[o] = ts_frag<T>(Ts, o, escale[o], q, mp);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       float b[8];
@@ -478,9 +515,9 @@ struct MlpDxArgs {
   int R, NC;
 };
 
-template <class T>
-__global__ __launch_bounds__(kThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
-  __shared__ __align__(16) char smem[kGemmLds];
+template <class T, bool FAST>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
+  __shared__ __align__(16) char smem[FAST ? kGemmLdsX : kGemmLds];
   int rb, cb;
   tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
@@ -492,23 +529,60 @@ __global__ __launch_bounds__(kThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   const T* Bu = static_cast<const T*>(a.Bu);
   constexpr int BK = ET<T>::BK;
 
-  KNLoader<T, SplitRowsA<T>, 2, KRow2<T>, SRow2<T>, SMask2> ld;
-  ld.a.init(static_cast<const T*>(a.dG), ni, ni, static_cast<const T*>(a.dU), ni, ni, a.N, m0, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  KNLoader<T, AOp, 2, KRow2<T>, SRow2<T>, SMask2> ld;
+  ld.a.init(static_cast<const T*>(a.dG), static_cast<const T*>(a.dU), ni, ni, ni, a.N, m0, a.vecA);
   ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
-  ld.srow.B0 = Bg; ld.srow.B1 = Bu; ld.srow.K0 = ni; ld.srow.K1 = ni; ld.srow.ld = r;
+  ld.srow.B0 = Bg; ld.srow.lo0 = 0; ld.srow.hi0 = ni;
+  ld.srow.B1 = Bu; ld.srow.lo1 = ni; ld.srow.hi1 = 2 * ni;
+  ld.srow.ld = r;
   ld.smask_of.K0 = ni; ld.smask_of.BK = BK;
   ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
 
-  f32x4 acc[8][8];
-  f32x4 sacc[2][8];
+  f32x4 acc[kMB][8];
   zero_acc(acc);
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   const int nkt = (int)((2 * ni + BK - 1) / BK);
-  kloop<T, 2>(smem, nkt, ld, acc, sacc);
-  side_reduce<T, 2>(smem, sacc);
+  if constexpr (FAST) {
+    // i % BK == 0: the dG tiles carry only dT_g, the dU tiles only dT_u.  Two
+    // K-loop phases with one side accumulator; dT_g parks in the flush slot.
+    f32x4 sacc[1][kMB];
+    zero_side(sacc);
+    const int nk0 = (int)(ni / BK);
+    ld.smask_of.K0 = 1L << 40;                       // phase 1: block 0 always
+    kloop<T, 1>(smem, nk0, ld, acc, sacc);
+    {
+      const WaveId q = wave_id();
+      float* fl = reinterpret_cast<float*>(smem + kFlushOff);
+      if (q.wn == 0)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] = sacc[0][mb][j];
+      __syncthreads();
+      if (q.wn == 1)
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] += sacc[0][mb][j];
+    }
+    zero_side(sacc);
+    ld.srow.B0 = Bu;                                 // phase 2: block 0 carries B_u rows
+    ld.srow.lo0 = ni;
+    ld.srow.hi0 = 2 * ni;
+    kloop<T, 1>(smem, nkt, ld, acc, sacc, nk0);
+    side_reduce<T, 1>(smem, sacc, 1);                // dT_u -> slot 1
+    {
+      float* Ts = ts_ptr(smem);
+      const float* fl = reinterpret_cast<const float*>(smem + kFlushOff);
+      for (int e = threadIdx.x; e < kBM * kSlot; e += kGemmThreads) Ts[e] = fl[e];   // dT_g -> slot 0
+      __syncthreads();
+    }
+  } else {
+    f32x4 sacc[2][kMB];
+    zero_side(sacc);
+    kloop<T, 2>(smem, nkt, ld, acc, sacc);
+    side_reduce<T, 2>(smem, sacc);
+  }
 
   const T* Ag = static_cast<const T*>(a.Ag);
   const T* Au = static_cast<const T*>(a.Au);
@@ -543,8 +617,8 @@ struct QkvDxArgs {
   int R, NC;
 };
 
-template <class T>
-__global__ __launch_bounds__(kThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
+template <class T, bool FAST>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   int rb, cb;
   tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
@@ -556,14 +630,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
   const T* W2 = static_cast<const T*>(a.W[2]);
   const long o1 = a.off[1], o2 = a.off[2], o3 = a.off[3];
 
-  KNLoader<T, RowsA<T>, 0, KRow3<T>, SRowNone<T>, SMaskNone> ld;
-  ld.a.init(static_cast<const T*>(a.dP), a.O, a.N, m0, a.O, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  KNLoader<T, AOp, 0, KRow3<T>, SRowNone<T>, SMaskNone> ld;
+  ld.a.init(static_cast<const T*>(a.dP), nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
   ld.krow.W0 = W0; ld.krow.W1 = W1; ld.krow.W2 = W2;
   ld.krow.o1 = o1; ld.krow.o2 = o2; ld.krow.o3 = o3; ld.krow.ld = h;
   ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
 
-  f32x4 acc[8][8];
-  f32x4 sacc[1][8];
+  f32x4 acc[kMB][8];
+  f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.O + ET<T>::BK - 1) / ET<T>::BK;
   kloop<T, 0>(smem, nkt, ld, acc, sacc);

@@ -8,6 +8,8 @@
 //   P_p = X W_p^T + s_p (X A_p^T) B_p^T for p in {q, k, v}; Q, K rotated.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm.h"
 
 namespace lora {
@@ -33,8 +35,8 @@ __device__ __forceinline__ void gateup_row(int R, int j0, int& is_up, int& j) {
   j = j0 + (R >> 7) * 64 + (w & 63);
 }
 
-template <class T, int ACT>
-__global__ __launch_bounds__(kThreads, 1) void k_gateup_fwd(GateUpArgs a) {
+template <class T, int ACT, bool FAST>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   const WaveId q = wave_id();
   int rb, cb;
@@ -47,38 +49,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gateup_fwd(GateUpArgs a) {
   const T* Ag = static_cast<const T*>(a.Ag);
   const T* Au = static_cast<const T*>(a.Au);
 
-  NKLoader<T, RowsA<T>, 2> ld;
-  ld.a.init(X, a.h, a.N, m0, a.h, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  NKLoader<T, AOp, 2> ld;
+  ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
+  ld.bfallback = Wg;
   ld.K = a.h;
   ld.vecB = a.vecW;
   ld.vecS = a.vecS;
   ld.smask = 3u;
 #pragma unroll
-  for (int qq = 0; qq < 8; ++qq) {
+  for (int qq = 0; qq < 4; ++qq) {
     int up, j;
-    gateup_row((q.tid >> 3) + 32 * qq, j0, up, j);
+    gateup_row(ld.row_of(qq), j0, up, j);
     ld.brow[qq] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
   }
   {
-    const int sr = q.tid >> 3;          // side rows 0..31: A_g rows 0..15, A_u rows 0..15
+    const int sr = ld.side_row();       // side rows 0..31: A_g rows 0..15, A_u rows 0..15
     const int t = sr & 15;
-    ld.srow[0] = (t < a.r) ? ((sr < 16) ? Ag : Au) + (long)t * a.h : nullptr;
+    ld.srow = (sr < 32 && t < a.r) ? ((sr < 16) ? Ag : Au) + (long)t * a.h : nullptr;
   }
 
-  f32x4 acc[8][8];
-  f32x4 sacc[2][8];
+  f32x4 acc[kMB][8];
+  f32x4 sacc[2][kMB];
   zero_acc(acc);
-#pragma unroll
-  for (int s = 0; s < 2; ++s)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  zero_side(sacc);
 
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
   kloop<T, 2>(smem, nkt, ld, acc, sacc);
   side_reduce<T, 2>(smem, sacc);
 
   // The row block's T_g, T_u are saved once (by column block 0).
-  if (cb == 0) {
+  if (cb == 0 && q.tid < kBM) {
     const float* Ts = ts_ptr(smem);
     const long row = m0 + q.tid;
     if (row < a.N)
@@ -109,10 +110,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gateup_fwd(GateUpArgs a) {
   const int jj = j0 + q.wn * 64 + 4 * q.r16;
   const int nvalid = min(4, a.i - jj);
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      const long row = m0 + acc_row(q, mb, j);
       if (row >= a.N || nvalid <= 0) continue;
       float gv[4], uv[4], hv[4];
 #pragma unroll
@@ -140,8 +141,8 @@ struct LinearArgs {
   int R, NC;
 };
 
-template <class T>
-__global__ __launch_bounds__(kThreads, 1) void k_linear_fwd(LinearArgs a) {
+template <class T, bool FAST>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   const WaveId q = wave_id();
   int rb, cb;
@@ -152,32 +153,33 @@ __global__ __launch_bounds__(kThreads, 1) void k_linear_fwd(LinearArgs a) {
   const T* W = static_cast<const T*>(a.W);
   const T* A = static_cast<const T*>(a.A);
 
-  NKLoader<T, RowsA<T>, 1> ld;
-  ld.a.init(Z, a.K, a.N, m0, a.K, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  NKLoader<T, AOp, 1> ld;
+  ld.a.init(Z, nullptr, a.K, 0, a.K, a.N, m0, a.vecA);
+  ld.bfallback = W;
   ld.K = a.K;
   ld.vecB = a.vecW;
   ld.vecS = a.vecS;
   ld.smask = 1u;
 #pragma unroll
-  for (int qq = 0; qq < 8; ++qq) {
-    const long n = n0 + lds_row_col(0, (q.tid >> 3) + 32 * qq);
+  for (int qq = 0; qq < 4; ++qq) {
+    const long n = n0 + lds_row_col(0, ld.row_of(qq));
     ld.brow[qq] = (n < a.O) ? W + n * a.K : nullptr;
   }
   {
-    const int sr = q.tid >> 3;
-    ld.srow[0] = (sr < 16 && sr < a.r) ? A + (long)sr * a.K : nullptr;
+    const int sr = ld.side_row();
+    ld.srow = (sr < 16 && sr < a.r) ? A + (long)sr * a.K : nullptr;
   }
 
-  f32x4 acc[8][8];
-  f32x4 sacc[1][8];
+  f32x4 acc[kMB][8];
+  f32x4 sacc[1][kMB];
   zero_acc(acc);
-#pragma unroll
-  for (int mb = 0; mb < 8; ++mb) sacc[0][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  zero_side(sacc);
   const int nkt = (a.K + ET<T>::BK - 1) / ET<T>::BK;
   kloop<T, 1>(smem, nkt, ld, acc, sacc);
   side_reduce<T, 1>(smem, sacc);
 
-  if (cb == 0) {
+  if (cb == 0 && q.tid < kBM) {
     const float* Ts = ts_ptr(smem);
     const long row = m0 + q.tid;
     if (row < a.N)
@@ -198,10 +200,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_linear_fwd(LinearArgs a) {
   const long c0 = n0 + q.wn * 128 + 8 * q.r16;
   const int nvalid = (int)min(8L, a.O - c0);
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      const long row = m0 + acc_row(q, mb, j);
       if (row >= a.N || nvalid <= 0) continue;
       float v[8];
 #pragma unroll
@@ -241,8 +243,9 @@ struct QKVFwdArgs {
 };
 
 // LG = log2(256 / head_dim): 1 for d = 128, 2 for d = 64 (RoPE pairs share a lane).
-template <class T, int LG>
-__global__ __launch_bounds__(kThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
+// NS = the most projections any 256-column tile overlaps (side blocks held).
+template <class T, int LG, bool FAST, int NS>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   const WaveId q = wave_id();
   int rb, cb;
@@ -261,15 +264,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
   auto slot_of = [&](int p) { return (plist[0] == p) ? 0 : ((plist[1] == p) ? 1 : 2); };
 
-  NKLoader<T, RowsA<T>, 3> ld;
-  ld.a.init(X, a.h, a.N, m0, a.h, a.vecA);
+  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+  NKLoader<T, AOp, NS> ld;
+  ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
+  ld.bfallback = static_cast<const T*>(a.W[0]);
   ld.K = a.h;
   ld.vecB = a.vecW;
   ld.vecS = a.vecS;
   ld.smask = (1u << nslot) - 1u;
 #pragma unroll
-  for (int qq = 0; qq < 8; ++qq) {
-    const int o = n0 + lds_row_col(LG, (q.tid >> 3) + 32 * qq);
+  for (int qq = 0; qq < 4; ++qq) {
+    const int o = n0 + lds_row_col(LG, ld.row_of(qq));
     if (o < O) {
       const int p = proj_of(o);
       ld.brow[qq] = static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
@@ -277,31 +282,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       ld.brow[qq] = nullptr;
     }
   }
-#pragma unroll
-  for (int qq = 0; qq < NKLoader<T, RowsA<T>, 3>::NSQ; ++qq) {
-    const int sr = (q.tid >> 3) + 32 * qq;     // side row: slot sr/16, rank sr%16
+  {
+    const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
     const int sl = sr >> 4, t = sr & 15;
     const T* p = nullptr;
-    if (sr < 48 && sl < nslot && t < a.r) {
+    if (sl < NS && sl < nslot && t < a.r) {
       const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
       p = static_cast<const T*>(a.A[pj]) + (long)t * a.h;
     }
-    ld.srow[qq] = p;
+    ld.srow = p;
   }
 
-  f32x4 acc[8][8];
-  f32x4 sacc[3][8];
+  f32x4 acc[kMB][8];
+  f32x4 sacc[NS][kMB];
   zero_acc(acc);
-#pragma unroll
-  for (int s = 0; s < 3; ++s)
-#pragma unroll
-    for (int mb = 0; mb < 8; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  zero_side(sacc);
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, 3>(smem, nkt, ld, acc, sacc);
-  side_reduce<T, 3>(smem, sacc);
+  kloop<T, NS>(smem, nkt, ld, acc, sacc);
+  side_reduce<T, NS>(smem, sacc);
 
   // T_p is saved by the tile holding projection p's first column.
-  {
+  if (q.tid < kBM) {
     const float* Ts = ts_ptr(smem);
     const long row = m0 + q.tid;
     for (int sl = 0; sl < nslot; ++sl) {
@@ -333,10 +334,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   constexpr int cw = 8 >> LG;
   const int half = a.d >> 1;
 #pragma unroll
-  for (int mb = 0; mb < 8; ++mb)
+  for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + q.wm * 128 + mb * 16 + 4 * q.g + j;
+      const long row = m0 + acc_row(q, mb, j);
       if (row >= a.N) continue;
       const int s = (int)(row % a.S);
       const long bidx = row / a.S;

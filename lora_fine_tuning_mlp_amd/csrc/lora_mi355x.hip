@@ -9,6 +9,8 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
+#include <initializer_list>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -96,6 +98,26 @@ int vecw(int dtype) { return dtype == LORA_BF16 ? 8 : 4; }
 size_t esz(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
+
+// Direct global->LDS loads need full bf16 K tiles, 16-byte aligned rows and
+// 32-bit row offsets; other calls take the register-staged (masked) loaders.
+bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> ptrs);
+
+// Launch Fast<true> when allowed (bf16 only), else Fast<false>.
+#define LORA_LAUNCH_FAST(kid, FAST_COND, KERN_TRUE, KERN_FALSE, grid, block, st, args)                   \
+  ([&]() -> int {                                                                                        \
+    if constexpr (sizeof(T) == 2) {                                                                      \
+      if (FAST_COND) return launch(kid, KERN_TRUE, grid, block, st, args);                               \
+    }                                                                                                    \
+    return launch(kid, KERN_FALSE, grid, block, st, args);                                               \
+  }())
+
+bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> ptrs) {
+  if (dtype != LORA_BF16 || K % ET<bf16>::BK != 0 || rows * K >= (1L << 31)) return false;
+  for (const void* p : ptrs)
+    if (!al16(p)) return false;
+  return true;
+}
 
 struct Carver {
   char* base;
@@ -239,7 +261,9 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (h % V == 0) && al16(g.A) && al16(u.A);
     a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
     a.R = R; a.NC = (int)cdiv(i, 128);
-    const int rc = launch(0, k_gateup_fwd<T, ACT>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W});
+    const int rc = LORA_LAUNCH_FAST(0, fast, (k_gateup_fwd<T, ACT, true>), (k_gateup_fwd<T, ACT, false>),
+                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   {
@@ -252,7 +276,9 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (i % V == 0) && al16(dn.A);
     a.vecO = (h % 8 == 0) && al16(Y);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const int rc = launch(1, k_linear_fwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W});
+    const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
+                                    dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   return ok();
@@ -294,7 +320,9 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecW = (i % V == 0) && al16(dn.W);
     a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
     a.R = R; a.NC = (int)cdiv(i, kBN);
-    const int rc = launch(5, k_down_bwd<T, ACT>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    const bool fast = fast_ok(DT<T>::code, h, N, {dY});
+    const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
+                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   {
@@ -308,7 +336,9 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const int rc = launch(6, k_mlp_dx_bwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU});
+    const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
+                                    dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   {
@@ -371,8 +401,24 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
   a.vecO = oal;
   a.R = (int)cdiv(N, kBM);
   a.NC = (int)cdiv(a.off[3], kBN);
-  if (d.head_dim == 128) rc = launch(3, k_qkv_fwd<T, 1>, dim3(a.R * a.NC), dim3(kThreads), st, a);
-  else rc = launch(3, k_qkv_fwd<T, 2>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+  const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W});
+  // Most projections any 256-column tile overlaps: 1, 2 or 3 side blocks.
+  int ns = 1;
+  for (int cb = 0; cb < a.NC; ++cb) {
+    int c = 0;
+    for (int p = 0; p < 3; ++p)
+      if (a.off[p] < std::min((cb + 1) * kBN, a.off[3]) && a.off[p + 1] > cb * kBN) ++c;
+    ns = std::max(ns, c);
+  }
+  const dim3 grid(a.R * a.NC), blk(kGemmThreads);
+#define LORA_QKV_NS(LG, NS) \
+  LORA_LAUNCH_FAST(3, fast, (k_qkv_fwd<T, LG, true, NS>), (k_qkv_fwd<T, LG, false, NS>), grid, blk, st, a)
+  if (d.head_dim == 128) {
+    rc = ns == 1 ? LORA_QKV_NS(1, 1) : (ns == 2 ? LORA_QKV_NS(1, 2) : LORA_QKV_NS(1, 3));
+  } else {
+    rc = ns == 1 ? LORA_QKV_NS(2, 1) : (ns == 2 ? LORA_QKV_NS(2, 2) : LORA_QKV_NS(2, 3));
+  }
+#undef LORA_QKV_NS
   if (rc) return rc;
   return ok();
 }
@@ -430,7 +476,9 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.vecW = (h % V == 0) && wal;
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    rc = launch(7, k_qkv_dx_bwd<T>, dim3(a.R * a.NC), dim3(kThreads), st, a);
+    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP});
+    rc = LORA_LAUNCH_FAST(7, fast, (k_qkv_dx_bwd<T, true>), (k_qkv_dx_bwd<T, false>), dim3(a.R * a.NC),
+                          dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   {
