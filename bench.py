@@ -16,7 +16,6 @@ Prints one JSON line.  Besides the headline value it carries
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -46,16 +45,6 @@ def kernel_flops(qkv, mlp):
     }
 
 
-def source_hash(kernel: str) -> str:
-    """Hash of the HIP sources (used to tell whether stored counters are stale)."""
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "lora_fine_tuning_mlp_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".h", ".hip")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def stored_traffic(kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current sources (else None)."""
@@ -66,14 +55,17 @@ def stored_traffic(kernel: str):
         d = json.load(open(p))
     except ValueError:
         return None
+    from lora_fine_tuning_mlp_amd.profiling import source_hash
     ent = d.get(kernel)
-    if not ent or ent.get("source_hash") != source_hash(kernel):
+    if not ent or ent.get("source_hash") != source_hash():
         return None
     return ent.get("bytes_per_launch")
 
 
 def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
-    """Time the CPU oracle (as it stands) on `tokens` tokens of each workload."""
+    """Time the CPU oracle (as it stands) on `tokens` tokens of each workload.
+    The QKV sample keeps the workload's sequence length (batches of seq) when
+    `tokens` is a multiple of it, else it is one sequence of `tokens`."""
     import dataclasses
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -81,14 +73,17 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
     from oracle import lora_oracle as orc
 
     mlp_s = dataclasses.replace(mlp_cfg, n_tokens=tokens)
-    qkv_s = dataclasses.replace(qkv_cfg, batch=1, seq=tokens)
+    if tokens % qkv_cfg.seq == 0:
+        qkv_s = dataclasses.replace(qkv_cfg, batch=tokens // qkv_cfg.seq)
+    else:
+        qkv_s = dataclasses.replace(qkv_cfg, batch=1, seq=tokens)
     tm = S.mlp_inputs(mlp_s, 0)
     tq = S.qkv_inputs(qkv_s, 0)
     pm = S.to_f64({k: v for k, v in tm.items() if k != "dY"})
     dY = tm["dY"].double().numpy()
     pq = S.to_f64({k: v for k, v in tq.items() if k not in ("dQ", "dK", "dV")})
     dQ, dK, dV = (tq[k].double().numpy() for k in ("dQ", "dK", "dV"))
-    shape = dict(batch=1, seq=tokens, n_q=qkv_s.n_q, n_kv=qkv_s.n_kv, head_dim=qkv_s.head_dim, theta=qkv_s.theta)
+    shape = dict(batch=qkv_s.batch, seq=qkv_s.seq, n_q=qkv_s.n_q, n_kv=qkv_s.n_kv, head_dim=qkv_s.head_dim, theta=qkv_s.theta)
     sc = (qkv_s.scale,) * 3
     t0 = time.perf_counter()
     orc.qkv_fwd(pq, scales=sc, **shape)
@@ -103,8 +98,8 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{tokens} tokens of each workload (QKV as 1 x {tokens}, positions 0..{tokens - 1}; MLP {tokens} rows), "
-                  f"float64 numpy, {dt:.2f} s wall",
+        "sample": f"{tokens} tokens of each workload (QKV as {qkv_s.batch} x {qkv_s.seq}; MLP {tokens} rows): one "
+                  f"fwd+bwd of both in float64 numpy, {dt:.2f} s wall",
         "seconds": dt,
     }
 
@@ -114,7 +109,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-tokens", type=int, default=1024, help="token sample for the CPU oracle baseline")
+    ap.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates rocprofv3 byte counters)")

@@ -27,6 +27,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;       // 4 waves of 64
 constexpr int kBM = 256;            // tile rows (tokens)
@@ -153,6 +154,15 @@ __device__ __forceinline__ f32x4 mma(f32x4 c, const Frag<float>& a, const Frag<f
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.z), __uint_as_float(b.v1.z), c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.v1.w), __uint_as_float(b.v1.w), c, 0, 0, 0);
   return c;
+}
+
+// v_mfma_f32_16x16x16_bf16: half the K of the main MFMA.  Lane l holds K
+// slots 4*(l>>4) .. 4*(l>>4)+3 of row / column l & 15 (two bf16 per dword,
+// lower slot in the low half), so in C layout a lane's four rows j = 0..3 of
+// one m-block are exactly its K slots.
+__device__ __forceinline__ f32x4 mma16(f32x4 c, u32x2 a, u32x2 b) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b), c, 0,
+                                                   0, 0);
 }
 
 // Fragment of LDS tile row `row`, K-step ks, lane group g (= lane >> 4).

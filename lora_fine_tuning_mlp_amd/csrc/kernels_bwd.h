@@ -378,51 +378,62 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
     }
   };
 
+  // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
+  // (s T_g), (s T_u) and dG, dU, as MFMAs whose K runs over this wave's rows.
+  if constexpr (sizeof(T) == 2) {
+    // bf16: 16x16x16 MFMAs, one m-block at a time.  The K slots of a lane are
+    // its own four rows j = 0..3, so only those four GLU rows are live.
 #pragma unroll
-  for (int mp = 0; mp < kMB / 2; ++mp) {
-    // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
-    // (s T_g), (s T_u) and dG, dU.  K slots = the 8 rows (mb pair, j) of this lane group.
-    const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q, mp);
-    float tg[8], tu[8];
-#pragma unroll
-    for (int mbl = 0; mbl < 2; ++mbl)
+    for (int mb = 0; mb < kMB; ++mb) {
+      float dt4[4], tg4[4], tu4[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const long row = m0 + acc_row(q, 2 * mp + mbl, j);
+        const long row = m0 + acc_row(q, mb, j);
         const bool ok = row < a.N && q.r16 < a.r;
-        tg[mbl * 4 + j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
-        tu[mbl * 4 + j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
+        dt4[j] = Ts[ts_idx(0, acc_row(q, mb, j), q.r16)];
+        tg4[j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
+        tu4[j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
       }
-    const Frag<T> aTg = make_frag<T>(tg);
-    const Frag<T> aTu = make_frag<T>(tu);
-    if constexpr (sizeof(T) == 2) {
-      unsigned fh[8][4], fg[8][4], fu[8][4];     // [nb][dword]: slots (2d, 2d+1)
+      const u32x2 adT = {pack_bf2(dt4[0], dt4[1]), pack_bf2(dt4[2], dt4[3])};
+      const u32x2 aTg = {pack_bf2(tg4[0], tg4[1]), pack_bf2(tg4[2], tg4[3])};
+      const u32x2 aTu = {pack_bf2(tu4[0], tu4[1]), pack_bf2(tu4[2], tu4[3])};
+      u32x2 fh[8], fg[8], fu[8];      // [nb]: slots (2 jp, 2 jp + 1) in dword jp
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        float h0[8], g0[8], u0[8], h1[8], g1[8], u1[8];
+        glu_row(mb, 2 * jp, h0, g0, u0);
+        glu_row(mb, 2 * jp + 1, h1, g1, u1);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          fh[nb][jp] = pack_bf2(h0[nb], h1[nb]);
+          fg[nb][jp] = pack_bf2(g0[nb], g1[nb]);
+          fu[nb][jp] = pack_bf2(u0[nb], u1[nb]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        pacc[0][nb] = mma16(pacc[0][nb], adT, fh[nb]);
+        pacc[1][nb] = mma16(pacc[1][nb], aTg, fg[nb]);
+        pacc[2][nb] = mma16(pacc[2][nb], aTu, fu[nb]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int mp = 0; mp < kMB / 2; ++mp) {
+      // fp32: K = 8 rows (m-block pair mp, j) per fragment.
+      const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q, mp);
+      float tg[8], tu[8];
 #pragma unroll
       for (int mbl = 0; mbl < 2; ++mbl)
 #pragma unroll
-        for (int jp = 0; jp < 2; ++jp) {
-          float h0[8], g0[8], u0[8], h1[8], g1[8], u1[8];
-          glu_row(2 * mp + mbl, 2 * jp, h0, g0, u0);
-          glu_row(2 * mp + mbl, 2 * jp + 1, h1, g1, u1);
-          const int d = mbl * 2 + jp;
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) {
-            fh[nb][d] = pack_bf2(h0[nb], h1[nb]);
-            fg[nb][d] = pack_bf2(g0[nb], g1[nb]);
-            fu[nb][d] = pack_bf2(u0[nb], u1[nb]);
-          }
+        for (int j = 0; j < 4; ++j) {
+          const long row = m0 + acc_row(q, 2 * mp + mbl, j);
+          const bool ok = row < a.N && q.r16 < a.r;
+          tg[mbl * 4 + j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
+          tu[mbl * 4 + j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
         }
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        Frag<T> b0, b1, b2;
-        b0.v = (u32x4){fh[nb][0], fh[nb][1], fh[nb][2], fh[nb][3]};
-        b1.v = (u32x4){fg[nb][0], fg[nb][1], fg[nb][2], fg[nb][3]};
-        b2.v = (u32x4){fu[nb][0], fu[nb][1], fu[nb][2], fu[nb][3]};
-        pacc[0][nb] = mma(pacc[0][nb], adT, b0);
-        pacc[1][nb] = mma(pacc[1][nb], aTg, b1);
-        pacc[2][nb] = mma(pacc[2][nb], aTu, b2);
-      }
-    } else {
+      const Frag<T> aTg = make_frag<T>(tg);
+      const Frag<T> aTu = make_frag<T>(tu);
       float hv[8][8], gv[8][8], uv[8][8];    // [slot = mbl*4 + j][nb]
 #pragma unroll
       for (int mbl = 0; mbl < 2; ++mbl)
