@@ -4,28 +4,34 @@
 // blocks of 16 x 16.
 //
 //   acc  = Z_tile . Bop_tile                       (K-loop, bf16 or fp32 MFMA)
-//   side = Z_tile . Sop^T                          (same K-loop, same A fragments:
+//   side = Z_tile . Sop                            (same K-loop, same A fragments:
 //                                                   the rank-r product, <= 3 adapters)
 //   acc += [s_1 T_1 | s_2 T_2 | ...] . [F_1 ; F_2 ; ...]   (the fold: extra K steps)
 //
-// The side product rides along the base GEMM's K-loop: its operand rows sit
-// in LDS right after the B tile and reuse the A fragments already in
-// registers, so X (or H, or dG|dU) is read once for both.  Each wave does the
-// side MFMAs on one of the two 32-wide K sub-steps of a tile (bf16), which
-// splits that work evenly across the wave-row; the halves are summed through
-// LDS after the loop.  Two waves per SIMD hide LDS and barrier latency, and a
-// 4 x 8 wave tile keeps the accumulators (128 + 16 per adapter) in AGPRs.
+// The side product rides along the base GEMM's K-loop: its operand sits in
+// LDS right after the B tile and reuses the A fragments already in
+// registers, so X (or H, or dG|dU) is read once for both.  The two waves that
+// share a row range take alternate K tiles of the side work; their halves are
+// summed through LDS after the loop.
 //
-// Operands reach LDS in two ways.  K-contiguous operands (activations, and
-// the forward's weight rows) go straight from global memory into LDS with
-// 16-byte direct loads (no staging registers); the swizzle is applied by
-// choosing which global chunk each lane fetches.  The backward's weights,
-// stored [K][N], are register-staged and transposed on the way in.
+// K-loop pipeline.  LDS holds a ring of four stages of one K tile each
+// (32 bf16 / 16 fp32 along K).  On the fast path every operand travels by
+// direct global -> LDS loads (no staging registers), and the loads for tile
+// kt + 3 are issued while tile kt is computed, so three tiles of loads are in
+// flight per workgroup.  The end of each iteration waits (vmcnt) only until
+// tile kt + 1 has landed and then barriers; a plain __syncthreads() would
+// drain every outstanding load.  Register-staged loaders (fp32, unaligned or
+// ragged shapes) prefetch one tile ahead.
 //
-// LDS during the K-loop: two stages of [A 256 rows | B 256 rows | side 48 rows]
-// x 128 bytes.  After the loop the same memory holds: Ts (float side products,
-// [3][256][16]), the fold A tile and the fold B tile; epilogues reuse the fold
-// tiles for cross-wave reductions.
+// B operands: weights stored [N][K] (forward) are rows of the tile like A;
+// weights stored [K][N] (backward, bf16) keep that layout in LDS and are read
+// as MFMA fragments with ds_read_b64_tr_b16, which leaves the accumulators in
+// natural column order; the epilogue turns them through LDS ("park") where it
+// needs 8 consecutive columns per lane.  fp32 [K][N] tiles are transposed
+// while register-staged.
+//
+// LDS after the K-loop: Ts (float side products, [3][256][16]), the fold A
+// tile and the fold B tile; epilogues reuse the fold area for reductions.
 #pragma once
 
 #include "common.h"
@@ -36,17 +42,20 @@ constexpr int kGemmThreads = 512;                          // 8 waves
 constexpr int kMB = 4;                                     // MFMA row blocks per wave
 constexpr int kARows = kBM;
 constexpr int kBRows = kBN + kSlot * kMaxSide;
-constexpr int kABytes = kARows * kRowBytes;
-constexpr int kBBytes = kBRows * kRowBytes;
-constexpr int kStage = kABytes + kBBytes;
-constexpr int kGemmLds = 2 * kStage;                       // 143360 bytes
+constexpr int kABytes = kARows * kRowBytes;                // 16384
+constexpr int kBBytes = kBRows * kRowBytes;                // 19456
+constexpr int kSideOff = kBN * kRowBytes;                  // side operand inside the B region
+constexpr int kStage = kABytes + kBBytes;                  // 35840
+constexpr int kNStage = 4;
+constexpr int kGemmLds = kNStage * kStage;                 // 143360 bytes
 
 constexpr int kTsOff = 0;
 constexpr int kTsBytes = kMaxSide * kBM * kSlot * 4;       // 49152
 constexpr int kFAOff = kTsBytes;
 constexpr int kFBOff = kFAOff + kBM * kRowBytes;
 constexpr int kRedOff = kFAOff;                            // epilogue scratch (fold tiles are dead)
-constexpr int kRedBytes = 2 * kBM * kRowBytes;             // 65536
+constexpr int kRedBytes = 65536;
+static_assert(kRedOff + kRedBytes <= kGemmLds, "reduction scratch overflows");
 static_assert(kFBOff + kBN * kRowBytes <= kGemmLds, "post-loop LDS layout overflows");
 // One extra Ts-sized slot past the K-loop stages (kernels that declare
 // kGemmLdsX): holds a side product across a second K-loop phase.
@@ -75,7 +84,8 @@ __device__ __forceinline__ int ts_idx(int slot, int row, int t) { return (slot *
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads (gfx950 global_load_lds_dwordx4): lane l of a
-// wave writes 16 bytes at LDS base + 16 l, so a 1 KB block = 8 tile rows.
+// wave writes 16 bytes at LDS base + 16 l, so a 1 KB block = 16 tile rows of
+// 64 bytes.  Lanes switched off by the exec mask write nothing.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void g2lds16(const void* g, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
@@ -83,71 +93,195 @@ __device__ __forceinline__ void g2lds16(const void* g, char* lds_wave_base) {
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Logical chunk a lane must fetch so that, written at physical chunk
-// (lane & 7) of row 8*blk + (lane >> 3), the tile obeys lds_off's swizzle.
-__device__ __forceinline__ int direct_chunk(int lane, int) { return (lane & 7) ^ (lane >> 3); }
-// 1 KB block `it` of this wave (wave w fills blocks w + 8 it, it = 0..3).
+// (lane & 3) of row 16*blk + (lane >> 2), the tile obeys lds_off's swizzle.
+__device__ __forceinline__ int direct_chunk(int lane) { return (lane & 3) ^ ((lane >> 3) & 3); }
+// 1 KB block `it` of this wave (wave w fills blocks w + 8 it, it = 0, 1).
 __device__ __forceinline__ int direct_blk(int it) { return (int)(threadIdx.x >> 6) + 8 * it; }
 // Tile row this lane fills in its direct block it.
-__device__ __forceinline__ int direct_row(int it) { return 8 * direct_blk(it) + (int)((threadIdx.x & 63) >> 3); }
+__device__ __forceinline__ int direct_row(int it) { return 16 * direct_blk(it) + (int)((threadIdx.x & 63) >> 2); }
+
+// ---------------------------------------------------------------------------
+// [K][N] bf16 B tiles in their natural layout (32 rows k x 256 columns, 512
+// bytes a row), read as MFMA B fragments with ds_read_b64_tr_b16.  Within
+// each 16-lane group that instruction hands lane i the 4 elements
+// M[4j + i/4][i % 4] (j = 0..3), M[s] being the 8 bytes lane s addressed.  So
+// lane s addresses row kb + s/4, columns nb0 + 4 (s % 4) .. +3, and lane i
+// receives column nb0 + i at rows kb .. kb+3; two reads give the 8 K slots.
+// 16-byte segments are XOR-swizzled per row (kn_off) so the 8 rows one read
+// touches hit distinct bank groups.
+// ---------------------------------------------------------------------------
+//
+// The transpose reads are issued as inline asm: the compiler's wait-count
+// pass treats the ds_read_tr intrinsic as possibly aliasing the direct loads
+// still in flight and would wait for all of them, which empties the
+// pipeline.  Their results become valid through lgkm_tie(), an explicit
+// lgkmcnt wait that names the destination registers (LDS operations of a
+// wave complete in order, so "at most N outstanding" means everything but
+// the last N issued has landed; the compiler's own lgkmcnt waits only get
+// more conservative from the extra operations).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int ftr(int k) { return ((k & 3) | (((k >> 3) & 1) << 2)) << 1; }
+__device__ __forceinline__ int kn_off(int k, int col) {   // byte offset of (k, col) in the tile
+  return k * 512 + ((((col >> 3) ^ ftr(k))) << 4) + ((col & 7) << 1);
+}
+__device__ __forceinline__ unsigned lds_addr(const char* p) {
+  return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+__device__ __forceinline__ u32x2 tr16(unsigned addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void lgkm_tie(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f, u32x2& g,
+                                         u32x2& h) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+               : "n"(N));
+}
+__device__ __forceinline__ void lgkm_tie0(u32x2& a, u32x2& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+// The two reads of B fragment nb (K slots 0..3 and 4..7 of the lane).
+__device__ __forceinline__ void tr_issue(const char* Bs, int nb, const WaveId& q, u32x2& lo, u32x2& hi) {
+  const int s = q.r16;
+  const int col = q.wn * 128 + nb * 16 + 4 * (s & 3);
+  const int k1 = 8 * q.g + (s >> 2);
+  lo = tr16(lds_addr(Bs + kn_off(k1, col)));
+  hi = tr16(lds_addr(Bs + kn_off(k1 + 4, col)));
+}
+// Side operand stored [K][r] (r = 16): a [32 k][16 t] tile of 32-byte rows.
+__device__ __forceinline__ void tr_side_issue(const char* S, const WaveId& q, u32x2& lo, u32x2& hi) {
+  const int s = q.r16;
+  const int off = (8 * q.g + (s >> 2)) * 32 + 8 * (s & 3);
+  lo = tr16(lds_addr(S + off));
+  hi = tr16(lds_addr(S + off + 128));
+}
+__device__ __forceinline__ Frag<bf16> tr_make(u32x2 lo, u32x2 hi) {
+  Frag<bf16> f;
+  f.v = (u32x4){lo.x, lo.y, hi.x, hi.y};
+  return f;
+}
+
+// ---------------------------------------------------------------------------
+// End-of-iteration synchronisation: wait until at most `ahead` tiles of
+// direct loads (L per thread each) are still in flight, finish this wave's
+// LDS traffic, then barrier.  Written as one asm statement so the compiler
+// neither adds the fence of __syncthreads (which would wait for every load)
+// nor moves memory accesses across it.
+// ---------------------------------------------------------------------------
+template <int L>
+__device__ __forceinline__ void sync_tiles(int ahead) {
+  if (ahead >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * L) : "memory");
+  } else if (ahead == 1) {
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(L) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+}
 
 // ---------------------------------------------------------------------------
 // K-loop.  Loader interface:
+//   kDepth                   tiles issued ahead of the one being computed (3 or 1)
+//   kLoads                   direct loads per thread per tile (kDepth 3)
+//   kBTr                     B (and side) fragments by transpose reads
 //   issue(kt, As, Bs)        direct global -> LDS loads for K tile kt
 //   load(kt)                 register-staged global loads for K tile kt
-//   store(As, Bs)            registers -> LDS stage (A rows, B rows, side rows)
+//   store(As, Bs)            registers -> LDS stage
 //   side_mask(kt)            bit sb set when side block sb has data in tile kt
+// K tiles kt0 .. nkt-1 (the ring restarts at stage 0).
 // ---------------------------------------------------------------------------
-// K tiles kt0 .. nkt-1 (stage buffers restart at stage 0).
 template <class T, int NSIDE, class Loader>
 __device__ __forceinline__ void kloop(char* smem, int nkt, Loader& ld, f32x4 (&acc)[kMB][8],
                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
-  constexpr int KSUB = ET<T>::KSUB;
+  constexpr int D = Loader::kDepth;
+  constexpr int L = Loader::kLoads;
+  static_assert(D == 1 || D == 3, "pipeline depth");
   const WaveId q = wave_id();
   if (nkt <= kt0) return;
-  ld.issue(kt0, smem, smem + kABytes);
-  ld.load(kt0);
-  ld.store(smem, smem + kABytes);
-  wait_vmem();
-  __syncthreads();
-  for (int kt = kt0; kt < nkt; ++kt) {
-    const char* As = smem + ((kt - kt0) & 1) * kStage;
-    const char* Bs = As + kABytes;
-    char* An = smem + ((kt - kt0 + 1) & 1) * kStage;
-    const bool more = kt + 1 < nkt;
-    if (more) {
-      ld.issue(kt + 1, An, An + kABytes);
-      ld.load(kt + 1);
+  auto stage = [&](int kt) { return smem + ((kt - kt0) & (kNStage - 1)) * kStage; };
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    const int kt = kt0 + d;
+    if (kt < nkt) {
+      char* S = stage(kt);
+      ld.issue(kt, S, S + kABytes);
+      ld.load(kt);
+      ld.store(S, S + kABytes);
     }
-    unsigned smask = 0u;
-    if constexpr (NSIDE > 0) smask = ld.side_mask(kt);
+  }
+  if constexpr (D == 3) {
+    sync_tiles<L>(min(nkt - 1, kt0 + 2) - kt0);
+  } else {
+    sync_tiles<L>(0);
+  }
+  for (int kt = kt0; kt < nkt; ++kt) {
+    const char* As = stage(kt);
+    const char* Bs = As + kABytes;
+    const int nx = kt + D;
+    const bool more = nx < nkt;
+    char* Sn = stage(nx);
+    if (more) {
+      ld.issue(nx, Sn, Sn + kABytes);
+      ld.load(nx);
+    }
+    Frag<T> af[kMB];
 #pragma unroll
-    for (int ks = 0; ks < KSUB; ++ks) {
-      Frag<T> af[kMB];
+    for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<T>(As, q.wm * 64 + mb * 16 + q.r16, q.g);
+    if constexpr (Loader::kBTr) {
+      u32x2 lo[8], hi[8];
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<T>(As, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
+      for (int nb = 0; nb < 8; ++nb) tr_issue(Bs, nb, q, lo[nb], hi[nb]);
+      lgkm_tie<8>(lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const Frag<T> bfr = lds_frag<T>(Bs, q.wn * 128 + nb * 16 + q.r16, ks, q.g);
+      for (int nb = 0; nb < 4; ++nb) {
+        const Frag<T> bfr = tr_make(lo[nb], hi[nb]);
 #pragma unroll
         for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
       }
-      if constexpr (NSIDE > 0) {
-        const bool mine = (KSUB == 2) ? (ks == q.wn) : (q.wn == 0);
-        if (mine) {
+      lgkm_tie<0>(lo[4], hi[4], lo[5], hi[5], lo[6], hi[6], lo[7], hi[7]);
 #pragma unroll
-          for (int sb = 0; sb < NSIDE; ++sb) {
-            if ((smask >> sb) & 1u) {
-              const Frag<T> bfr = lds_frag<T>(Bs, kBN + sb * 16 + q.r16, ks, q.g);
+      for (int nb = 4; nb < 8; ++nb) {
+        const Frag<T> bfr = tr_make(lo[nb], hi[nb]);
 #pragma unroll
-              for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = mma(sacc[sb][mb], af[mb], bfr);
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const Frag<T> bfr = lds_frag<T>(Bs, q.wn * 128 + nb * 16 + q.r16, q.g);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      }
+    }
+    if constexpr (NSIDE > 0) {
+      if ((kt & 1) == q.wn) {
+        const unsigned smask = ld.side_mask(kt);
+#pragma unroll
+        for (int sb = 0; sb < NSIDE; ++sb) {
+          if ((smask >> sb) & 1u) {
+            Frag<T> bfr;
+            if constexpr (Loader::kBTr) {
+              u32x2 lo, hi;
+              tr_side_issue(Bs + kSideOff + sb * 1024, q, lo, hi);
+              lgkm_tie0(lo, hi);
+              bfr = tr_make(lo, hi);
+            } else {
+              bfr = lds_frag<T>(Bs, kBN + sb * 16 + q.r16, q.g);
             }
+#pragma unroll
+            for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = mma(sacc[sb][mb], af[mb], bfr);
           }
         }
       }
     }
-    if (more) ld.store(An, An + kABytes);
-    wait_vmem();
-    __syncthreads();
+    if (more) ld.store(Sn, Sn + kABytes);
+    if constexpr (D == 3) {
+      sync_tiles<L>(min(nkt - 1, kt + D) - (kt + 1));
+    } else {
+      sync_tiles<L>(0);
+    }
   }
 }
 
@@ -165,13 +299,12 @@ __device__ __forceinline__ void zero_side(f32x4 (&sacc)[NS][kMB]) {
     for (int mb = 0; mb < kMB; ++mb) sacc[s][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
-// Sum the per-wave side products into Ts[sb][row][t] (float, raw Z.Sop^T).
-// Must follow the K-loop's final barrier.  The fold reads only slots < NSIDE.
+// Sum the two per-wave halves of the side products into Ts[sb][row][t]
+// (float, raw Z.Sop).  Must follow the K-loop's final barrier.
 template <class T, int NSIDE>
 __device__ __forceinline__ void side_reduce(char* smem, f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int slot0 = 0) {
   const WaveId q = wave_id();
   float* Ts = ts_ptr(smem) + slot0 * kBM * kSlot;
-  constexpr bool two = ET<T>::KSUB == 2;
   if (q.wn == 0) {
 #pragma unroll
     for (int sb = 0; sb < NSIDE; ++sb)
@@ -181,7 +314,7 @@ __device__ __forceinline__ void side_reduce(char* smem, f32x4 (&sacc)[NSIDE > 0 
         for (int j = 0; j < 4; ++j) Ts[ts_idx(sb, acc_row(q, mb, j), q.r16)] = sacc[sb][mb][j];
   }
   __syncthreads();
-  if (two && q.wn == 1) {
+  if (q.wn == 1) {
 #pragma unroll
     for (int sb = 0; sb < NSIDE; ++sb)
 #pragma unroll
@@ -195,15 +328,16 @@ __device__ __forceinline__ void side_reduce(char* smem, f32x4 (&sacc)[NSIDE > 0 
 // ---------------------------------------------------------------------------
 // Fold: acc += FA . FB^T with FA[m][16 s + t] = fscale[s] * Ts[s][m][t] and
 // FB[n][16 s + t] supplied by the kernel (adapter s's fold operand for output
-// column n).  One fold tile holds BK / 16 slots (4 for bf16, 2 for fp32).
-// FB functor: fb(R, slot, t0, v) fills v[0..VEC) for LDS row R (a permuted
-// output column), adapter slot `slot`, ranks t0..t0+VEC-1; v is pre-zeroed.
-// Threads 0..255 build FA rows, threads 256..511 build FB rows.
+// column n).  One fold tile holds BK / 16 slots (2 for bf16, 1 for fp32).
+// FB functor: fb(R, slot, t0, v) fills v[0..VEC) for FB row R (the output
+// column the B fragments of row R feed), adapter slot `slot`, ranks
+// t0..t0+VEC-1; v is pre-zeroed.  Threads 0..255 build FA rows, threads
+// 256..511 build FB rows.
 // ---------------------------------------------------------------------------
 template <class T, class FB>
 __device__ __forceinline__ void fold(char* smem, f32x4 (&acc)[kMB][8], int nslot, const float (&fscale)[kMaxSide],
                                      FB& fb) {
-  constexpr int VEC = ET<T>::VEC, BK = ET<T>::BK, KSUB = ET<T>::KSUB;
+  constexpr int VEC = ET<T>::VEC, BK = ET<T>::BK;
   const WaveId q = wave_id();
   if (nslot <= 0) return;
   const int nft = (nslot * kSlot + BK - 1) / BK;
@@ -214,7 +348,7 @@ __device__ __forceinline__ void fold(char* smem, f32x4 (&acc)[kMB][8], int nslot
   const int m = q.tid & (kBM - 1);
   for (int ft = 0; ft < nft; ++ft) {
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < 4; ++c) {
       const int kk = ft * BK + c * VEC;
       const int slot = kk / kSlot, t0 = kk % kSlot;
       float v[VEC];
@@ -234,17 +368,14 @@ __device__ __forceinline__ void fold(char* smem, f32x4 (&acc)[kMB][8], int nslot
       *reinterpret_cast<u32x4*>((build_a ? FA : FBt) + lds_off(m, c)) = pack(v);
     }
     __syncthreads();
+    Frag<T> af[kMB];
 #pragma unroll
-    for (int ks = 0; ks < KSUB; ++ks) {
-      Frag<T> af[kMB];
+    for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<T>(FA, q.wm * 64 + mb * 16 + q.r16, q.g);
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<T>(FA, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
+    for (int nb = 0; nb < 8; ++nb) {
+      const Frag<T> bfr = lds_frag<T>(FBt, q.wn * 128 + nb * 16 + q.r16, q.g);
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const Frag<T> bfr = lds_frag<T>(FBt, q.wn * 128 + nb * 16 + q.r16, ks, q.g);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
-      }
+      for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
     }
     __syncthreads();
   }
@@ -256,12 +387,12 @@ __device__ __forceinline__ int lds_row_col(int lg, int R) { return (R >> 7) * 12
 __device__ __forceinline__ int col_lds_row(int lg, int n) { return (n >> 7) * 128 + perm_row(lg, n & 127); }
 
 // ---------------------------------------------------------------------------
-// Loaders.
+// A operands.
 // ---------------------------------------------------------------------------
 
-// A operand, register-staged: rows of a row-major matrix, optionally split
-// along K into [A0 | A1] (A0 has K0 columns, A1 has K1; both row stride ld).
-// Thread t stages chunk (t & 7) of rows (t >> 3) + 64 qq, qq = 0..3.
+// Register-staged: rows of a row-major matrix, optionally split along K into
+// [A0 | A1] (A0 has K0 columns, A1 has K1; both row stride ld).  Thread t
+// stages chunk (t & 3) of rows (t >> 2) + 128 qq, qq = 0, 1.
 template <class T>
 struct RowsA {
   static constexpr bool kDirect = false;
@@ -272,7 +403,7 @@ struct RowsA {
   bool vec;
   __device__ __forceinline__ void init(const T* A0, const T* A1, long Kd0, long Kd1, long lda, long M, long m0,
                                        bool v) {
-    const int r0 = threadIdx.x >> 3;
+    const int r0 = threadIdx.x >> 2;
     ld = lda; K0 = Kd0; K1 = Kd1; vec = v;
     avail = (int)min((long)(1 << 30), M - m0 - r0);
     b0 = (avail > 0) ? A0 + (m0 + r0) * lda : nullptr;
@@ -280,10 +411,10 @@ struct RowsA {
   }
   __device__ __forceinline__ u32x4 get(int qq, long k) const {
     constexpr int VEC = ET<T>::VEC;
-    if (64 * qq >= avail) return zero4();
-    const T* r0p = b0 + (long)(64 * qq) * ld;
+    if (128 * qq >= avail) return zero4();
+    const T* r0p = b0 + (long)(128 * qq) * ld;
     if (k + VEC <= K0 || b1 == nullptr) return gload<T>(r0p, k, K0, vec);
-    const T* r1p = b1 + (long)(64 * qq) * ld;
+    const T* r1p = b1 + (long)(128 * qq) * ld;
     if (k >= K0) return gload<T>(r1p, k - K0, K1, vec);
     float v[VEC];   // a chunk straddling the seam
 #pragma unroll
@@ -296,21 +427,21 @@ struct RowsA {
   __device__ __forceinline__ void issue(int, char*) const {}
 };
 
-// A operand, direct to LDS.  Requires K0 % BK == 0 (each K tile inside one
-// segment), 16-byte aligned rows, and every K tile full.  Rows past M are
-// clamped to row M-1 (finite values; those rows are never stored and every
-// row reduction masks them).
+// Direct to LDS.  Requires K0 % BK == 0 (each K tile inside one segment),
+// 16-byte aligned rows, and every K tile full.  Rows past M are clamped to
+// row M-1 (finite values; those rows are never stored and every row
+// reduction masks them).
 template <class T>
 struct DirectA {
   static constexpr bool kDirect = true;
   const T* b0;
   const T* b1;
   long K0;
-  int off[4];
+  int off[2];
   __device__ __forceinline__ void init(const T* A0, const T* A1, long Kd0, long, long lda, long M, long m0, bool) {
     b0 = A0; b1 = A1 ? A1 : A0; K0 = A1 ? Kd0 : (1L << 40);
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < 2; ++it) {
       long row = m0 + direct_row(it);
       if (row > M - 1) row = M - 1;
       off[it] = (int)(row * lda);
@@ -323,188 +454,245 @@ struct DirectA {
     const T* b = b0;
     if (k >= K0) { b = b1; k -= K0; }
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int blk = direct_blk(it);
-      g2lds16(b + off[it] + k + direct_chunk(L, blk) * ET<T>::VEC, As + blk * 1024);
-    }
+    for (int it = 0; it < 2; ++it) g2lds16(b + off[it] + k + direct_chunk(L) * ET<T>::VEC, As + direct_blk(it) * 1024);
   }
 };
 
+// ---------------------------------------------------------------------------
 // NK loader: A rows + B rows (output columns, row-major [n][K]) + side rows
-// (adapter A_p rows [t][K]), all K-contiguous.  B row pointers are resolved
-// once per tile by the kernel for the rows row_of(qq), qq = 0..3, of this
-// thread.  With a direct A operand (AOp::kDirect) the B rows are also loaded
-// straight into LDS; a nullptr B row then falls back to `bfallback` (a valid
-// row whose output columns are never stored).  Side rows (one chunk per
-// thread for threads < 128 * NSIDE) are register-staged and zero-filled past
-// the rank.
+// (adapter A_p rows [t][K]), all K-contiguous.  The kernel resolves the B row
+// pointers once for the rows row_of(qq), qq = 0, 1, of this thread, and the
+// side row pointer for side_row() (see side_ptr).
+//   Direct (AOp::kDirect): all three go straight into LDS.  A nullptr B row
+//   falls back to `bfallback` (a valid row whose output columns are never
+//   stored).  Side rows: lanes 0 .. 8 NSIDE - 1 of every wave load one chunk
+//   each; ranks past r read row r-1 (finite; their products meet zero fold
+//   rows and are never saved).
+//   Staged: A and B rows in registers, side rows zero-filled past the rank.
+// ---------------------------------------------------------------------------
 template <class T, class AOp, int NSIDE>
 struct NKLoader {
   static constexpr bool DIRECT = AOp::kDirect;
+  static constexpr int kDepth = DIRECT ? 3 : 1;
+  static constexpr int kLoads = 4 + (NSIDE > 0 ? 1 : 0);
+  static constexpr bool kBTr = false;
   AOp a;
-  const T* brow[4];
+  const T* brow[2];
   const T* bfallback;
   const T* srow;
   long K;
   bool vecB, vecS;
   unsigned smask;
-  u32x4 ra[DIRECT ? 1 : 4], rb[DIRECT ? 1 : 4], rs;
+  u32x4 ra[DIRECT ? 1 : 2], rb[DIRECT ? 1 : 2], rs;
   __device__ static __forceinline__ int row_of(int qq) {
-    return DIRECT ? direct_row(qq) : (int)(threadIdx.x >> 3) + 64 * qq;
+    return DIRECT ? direct_row(qq) : (int)(threadIdx.x >> 2) + 128 * qq;
   }
-  // Side row this thread stages (>= 16 * NSIDE: none).
-  __device__ static __forceinline__ int side_row() { return (int)(threadIdx.x >> 3); }
+  // Side row (16 sb + t) this thread loads, or -1.
+  __device__ static __forceinline__ int side_row() {
+    if constexpr (DIRECT) {
+      const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+      return (l < 8 * NSIDE) ? (w * 8 * NSIDE + l) >> 2 : -1;
+    } else {
+      const int r = threadIdx.x >> 2;
+      return (r < 16 * NSIDE) ? r : -1;
+    }
+  }
+  // Pointer for side row t of an adapter whose rows start at `base` (nullptr:
+  // no adapter in this block); `fallback` is any valid row.
+  __device__ static __forceinline__ const T* side_ptr(const T* base, int t, int r, long Kd, const T* fallback) {
+    if constexpr (DIRECT) return base ? base + (long)min(t, r - 1) * Kd : fallback;
+    else return (base && t < r) ? base + (long)t * Kd : nullptr;
+  }
   __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
     if constexpr (DIRECT) {
       a.issue(kt, As);
       const int L = threadIdx.x & 63;
       const long k = (long)kt * ET<T>::BK;
 #pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int blk = direct_blk(it);
+      for (int it = 0; it < 2; ++it) {
         const T* p = brow[it] ? brow[it] : bfallback;
-        g2lds16(p + k + direct_chunk(L, blk) * ET<T>::VEC, Bs + blk * 1024);
+        g2lds16(p + k + direct_chunk(L) * ET<T>::VEC, Bs + direct_blk(it) * 1024);
+      }
+      if constexpr (NSIDE > 0) {
+        if (L < 8 * NSIDE) {
+          const int w = threadIdx.x >> 6;
+          const int ci = w * 8 * NSIDE + L, sr = ci >> 2;
+          const int chunk = (ci & 3) ^ ((sr >> 1) & 3);
+          g2lds16(srow + k + chunk * ET<T>::VEC, Bs + kSideOff + w * 128 * NSIDE);
+        }
       }
     }
   }
   __device__ __forceinline__ void load(int kt) {
-    const long k = (long)kt * ET<T>::BK + (threadIdx.x & 7) * ET<T>::VEC;
     if constexpr (!DIRECT) {
+      const long k = (long)kt * ET<T>::BK + (threadIdx.x & 3) * ET<T>::VEC;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) ra[qq] = a.get(qq, k);
+      for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, k);
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) rb[qq] = gload<T>(brow[qq], k, K, vecB);
+      for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<T>(brow[qq], k, K, vecB);
+      if constexpr (NSIDE > 0) {
+        rs = zero4();
+        if ((int)(threadIdx.x >> 2) < 16 * NSIDE) rs = gload<T>(srow, k, K, vecS);
+      }
     }
-    if constexpr (NSIDE > 0) rs = gload<T>(srow, k, K, vecS);
   }
   __device__ __forceinline__ void store(char* As, char* Bs) const {
-    const int c = threadIdx.x & 7, r0 = threadIdx.x >> 3;
     if constexpr (!DIRECT) {
+      const int c = threadIdx.x & 3, r0 = threadIdx.x >> 2;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 64 * qq, c)) = ra[qq];
+      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(Bs + lds_off(r0 + 64 * qq, c)) = rb[qq];
+      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + lds_off(r0 + 128 * qq, c)) = rb[qq];
+      if constexpr (NSIDE > 0)
+        if (r0 < NSIDE * 16) *reinterpret_cast<u32x4*>(Bs + lds_off(kBN + r0, c)) = rs;
     }
-    if constexpr (NSIDE > 0)
-      if (r0 < NSIDE * 16) *reinterpret_cast<u32x4*>(Bs + lds_off(kBN + r0, c)) = rs;
   }
   __device__ __forceinline__ unsigned side_mask(int) const { return smask; }
 };
 
-// Transpose helpers: 4 rows x 8 bf16 -> 8 columns x 4 rows (u32x2 each), and 4x4 fp32.
-__device__ __forceinline__ void transpose4x8_bf16(const u32x4 (&in)[4], u32x2 (&out)[8]) {
-  const unsigned* w = reinterpret_cast<const unsigned*>(in);   // w[k*4 + n/2]
-#pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    const unsigned a0 = w[0 * 4 + n / 2], a1 = w[1 * 4 + n / 2], a2 = w[2 * 4 + n / 2], a3 = w[3 * 4 + n / 2];
-    if (n & 1) {
-      out[n].x = (a0 >> 16) | (a1 & 0xffff0000u);
-      out[n].y = (a2 >> 16) | (a3 & 0xffff0000u);
-    } else {
-      out[n].x = (a0 & 0xffffu) | (a1 << 16);
-      out[n].y = (a2 & 0xffffu) | (a3 << 16);
-    }
-  }
-}
-__device__ __forceinline__ void transpose4x4_f32(const u32x4 (&in)[4], u32x4 (&out)[4]) {
-  out[0] = (u32x4){in[0].x, in[1].x, in[2].x, in[3].x};
-  out[1] = (u32x4){in[0].y, in[1].y, in[2].y, in[3].y};
-  out[2] = (u32x4){in[0].z, in[1].z, in[2].z, in[3].z};
-  out[3] = (u32x4){in[0].w, in[1].w, in[2].w, in[3].w};
-}
-
-// KN loader: A rows (token-major) + B stored [K][N] (N contiguous, e.g. W_d
-// for dH = dY W_d) transposed into LDS rows while staging, + optional side
-// operands stored [K][r] (e.g. B_g for dT_g = dG B_g).
+// ---------------------------------------------------------------------------
+// KN loaders: B stored [K][N] (N contiguous, e.g. W_d for dH = dY W_d) plus
+// optional side operands stored [K][r] (e.g. B_g for dT_g = dG B_g).
 //   krow(k)        -> pointer to row k of the B matrix (nullptr past K)
 //   srow(sb, k)    -> pointer to row k of side operand sb (nullptr if inactive)
 //   smask_of(kt)   -> active side blocks in tile kt
-// Output columns n0 .. n0+255 (bounded by N) go to LDS rows col_lds_row(0, n).
-// Each thread stages a 4 (k) x 8 (n) bf16 block (4 x 4 for fp32).
-template <class T, class AOp, int NSIDE, class KRow, class SRow, class SMask>
-struct KNLoader {
+// ---------------------------------------------------------------------------
+
+// bf16: the B tile keeps the [k][n] layout (kn_off) and is read with
+// transpose reads; output column (within the tile) = wn*128 + 16 nb + r16.
+// The side tile of block sb is [32 k][16 t] at kSideOff + 1024 sb.
+//   Direct (AOp::kDirect): requires every K tile full, N % 8 == 0, 16-byte
+//   aligned rows; columns past N are clamped to the last chunk (never
+//   stored).  A direct side operand needs r == 16 and NSIDE <= 1.
+//   Staged: 2 chunks of B and 2 of A per thread, zero-filled past K and N.
+template <class AOp, class KRow, class SRow, class SMask, int NSIDE>
+struct KNTrLoader {
   static constexpr bool DIRECT = AOp::kDirect;
-  static constexpr int VEC = ET<T>::VEC, BK = ET<T>::BK;
+  static constexpr int kDepth = DIRECT ? 3 : 1;
+  static constexpr int kLoads = 4 + (NSIDE > 0 ? 1 : 0);
+  static constexpr bool kBTr = true;
+  static_assert(!DIRECT || NSIDE <= 1, "direct KN side operand: one block");
   AOp a;
   KRow krow;
   SRow srow;
   SMask smask_of;
   long n0, N;
-  bool vecB;
-  int r;            // adapter rank (side columns beyond r are zero)
-  bool vecS;
-  u32x4 ra[DIRECT ? 1 : 4];
-  u32x4 rb[4];
-  u32x4 rs;
-  __device__ __forceinline__ void issue(int kt, char* As, char*) const {
-    if constexpr (DIRECT) a.issue(kt, As);
+  int r;
+  bool vecB, vecS;
+  u32x4 ra[DIRECT ? 1 : 2], rb[DIRECT ? 1 : 2], rs;
+  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
+    if constexpr (DIRECT) {
+      a.issue(kt, As);
+      const int L = threadIdx.x & 63;
+      const long k0 = (long)kt * 32;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int blk = direct_blk(it);
+        const int row = 2 * blk + (L >> 5);
+        const int lseg = (L & 31) ^ ftr(row);
+        const long col = min(n0 + lseg * 8, N - 8);
+        g2lds16(krow(k0 + row) + col, Bs + blk * 1024);
+      }
+      if constexpr (NSIDE > 0) {
+        if (L < 8) {
+          const int w = threadIdx.x >> 6, ci = 8 * w + L;
+          const bf16* p = srow(0, k0 + (ci >> 1));
+          g2lds16(p + 8 * (ci & 1), Bs + kSideOff + 128 * w);
+        }
+      }
+    }
   }
   __device__ __forceinline__ void load(int kt) {
-    const int tid = threadIdx.x;
-    const long k = (long)kt * BK + (tid & 7) * VEC;
     if constexpr (!DIRECT) {
+      const int tid = threadIdx.x;
+      const long ka = (long)kt * 32 + (tid & 3) * 8;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) ra[qq] = a.get(qq, k);
+      for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, ka);
+      const int seg = tid & 31, kr = tid >> 5;           // k rows kr, kr + 16
+#pragma unroll
+      for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<bf16>(krow((long)kt * 32 + kr + 16 * qq), n0 + seg * 8, N, vecB);
+      if constexpr (NSIDE > 0) {
+        const int sb = tid >> 6, e = tid & 63;
+        rs = zero4();
+        if (sb < NSIDE) rs = gload<bf16>(srow(sb, (long)kt * 32 + (e >> 1)), (e & 1) * 8, r, vecS);
+      }
     }
-    if constexpr (sizeof(T) == 2) {
-      const int ng = tid & 31, kg = tid >> 5;              // 8 columns, rows 4 kg .. 4 kg + 3
+  }
+  __device__ __forceinline__ void store(char* As, char* Bs) const {
+    if constexpr (!DIRECT) {
+      const int tid = threadIdx.x;
+      const int c = tid & 3, r0 = tid >> 2;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = gload<T>(krow((long)kt * BK + kg * 4 + i), n0 + ng * 8, N, vecB);
-    } else {
-      const int ng = tid & 63, kg = tid >> 6;              // 4 columns, rows 4 kg .. 4 kg + 3
+      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
+      const int seg = tid & 31, kr = tid >> 5;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) rb[i] = gload<T>(krow((long)kt * BK + kg * 4 + i), n0 + ng * 4, N, vecB);
+      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + kn_off(kr + 16 * qq, seg * 8)) = rb[qq];
+      if constexpr (NSIDE > 0) {
+        const int sb = tid >> 6, e = tid & 63;
+        if (sb < NSIDE) *reinterpret_cast<u32x4*>(Bs + kSideOff + sb * 1024 + 16 * e) = rs;
+      }
+    }
+  }
+  __device__ __forceinline__ unsigned side_mask(int kt) const { return smask_of(kt); }
+};
+
+// fp32: register-staged, transposed into B rows (output columns, LDS row
+// col_lds_row(0, n), G = 1 order) and side rows [t][k].  Thread t stages a
+// 4 (k) x 2 (n) block of B.
+template <class KRow, class SRow, class SMask, int NSIDE>
+struct KNLoader32 {
+  static constexpr int kDepth = 1;
+  static constexpr int kLoads = 0;
+  static constexpr bool kBTr = false;
+  RowsA<float> a;
+  KRow krow;
+  SRow srow;
+  SMask smask_of;
+  long n0, N;
+  int r;
+  bool vecB, vecS;
+  u32x4 ra[2];
+  float rb[4][2];
+  float rs;
+  __device__ __forceinline__ void issue(int, char*, char*) const {}
+  __device__ __forceinline__ void load(int kt) {
+    const int tid = threadIdx.x;
+    const long ka = (long)kt * 16 + (tid & 3) * 4;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, ka);
+    const int ng = tid & 127, kg = tid >> 7;              // columns 2 ng, 2 ng + 1; rows 4 kg .. 4 kg + 3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float* row = krow((long)kt * 16 + 4 * kg + i);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const long n = n0 + 2 * ng + c;
+        rb[i][c] = (row && n < N) ? row[n] : 0.f;
+      }
     }
     if constexpr (NSIDE > 0) {
-      // side block sb is staged by threads [128 sb, 128 sb + 128)
-      const int sb = tid >> 7, tt = tid & 127;
-      rs = zero4();
+      const int sb = tid >> 8, e = tid & 255;               // k = e >> 4, t = e & 15
+      rs = 0.f;
       if (sb < NSIDE) {
-        if constexpr (sizeof(T) == 2) rs = gload<T>(srow(sb, (long)kt * BK + (tt >> 1)), (tt & 1) * 8, r, vecS);
-        else rs = gload<T>(srow(sb, (long)kt * BK + (tt >> 2)), (tt & 3) * 4, r, vecS);
+        const float* row = srow(sb, (long)kt * 16 + (e >> 4));
+        if (row && (e & 15) < r) rs = row[e & 15];
       }
     }
   }
   __device__ __forceinline__ void store(char* As, char* Bs) const {
     const int tid = threadIdx.x;
-    const int c = tid & 7, r0 = tid >> 3;
-    if constexpr (!DIRECT) {
+    const int c = tid & 3, r0 = tid >> 2;
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 64 * qq, c)) = ra[qq];
-    }
-    if constexpr (sizeof(T) == 2) {
-      const int ng = tid & 31, kg = tid >> 5;
-      u32x2 cols[8];
-      transpose4x8_bf16(rb, cols);
+    for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
+    const int ng = tid & 127, kg = tid >> 7;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        *reinterpret_cast<u32x2*>(Bs + lds_off(col_lds_row(0, ng * 8 + i), kg >> 1) + (kg & 1) * 8) = cols[i];
-    } else {
-      const int ng = tid & 63, kg = tid >> 6;
-      u32x4 cols[4];
-      transpose4x4_f32(rb, cols);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(Bs + lds_off(col_lds_row(0, ng * 4 + i), kg)) = cols[i];
+    for (int cc = 0; cc < 2; ++cc) {
+      const float v[4] = {rb[0][cc], rb[1][cc], rb[2][cc], rb[3][cc]};
+      *reinterpret_cast<u32x4*>(Bs + lds_off(col_lds_row(0, 2 * ng + cc), kg)) = pack(v);
     }
     if constexpr (NSIDE > 0) {
-      const int sb = tid >> 7, tt = tid & 127;
-      if (sb < NSIDE) {
-        // rs holds ranks t0 .. t0+VEC-1 of one k: scatter into rows kBN + 16 sb + t.
-        const unsigned* wv = reinterpret_cast<const unsigned*>(&rs);
-        if constexpr (sizeof(T) == 2) {
-          const int kk = tt >> 1, t0 = (tt & 1) * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const unsigned short h = (e & 1) ? (unsigned short)(wv[e >> 1] >> 16) : (unsigned short)(wv[e >> 1] & 0xffffu);
-            *reinterpret_cast<unsigned short*>(Bs + lds_off(kBN + sb * 16 + t0 + e, kk >> 3) + (kk & 7) * 2) = h;
-          }
-        } else {
-          const int kk = tt >> 2, t0 = (tt & 3) * 4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            *reinterpret_cast<unsigned*>(Bs + lds_off(kBN + sb * 16 + t0 + e, kk >> 2) + (kk & 3) * 4) = wv[e];
-        }
-      }
+      const int sb = tid >> 8, e = tid & 255, k = e >> 4, t = e & 15;
+      if (sb < NSIDE) *reinterpret_cast<float*>(Bs + lds_off(kBN + 16 * sb + t, k >> 2) + (k & 3) * 4) = rs;
     }
   }
   __device__ __forceinline__ unsigned side_mask(int kt) const { return smask_of(kt); }
@@ -574,8 +762,16 @@ struct SRow2 {                // side block b: rows k - lo[b] of B[b] for lo[b] 
     return (k >= lo1 && k < hi1) ? B1 + (k - lo1) * ld : nullptr;
   }
 };
+template <class T>
+struct SRowLin {              // one side block: row k - kb of B (caller keeps k in range)
+  const T* B; long kb, ld;
+  __device__ __forceinline__ const T* operator()(int, long k) const { return B + (k - kb) * ld; }
+};
 struct SMaskNone {
   __device__ __forceinline__ unsigned operator()(int) const { return 0u; }
+};
+struct SMaskOne {
+  __device__ __forceinline__ unsigned operator()(int) const { return 1u; }
 };
 struct SMask2 {               // block 0 active while the tile overlaps [0, K0), block 1 beyond
   long K0; int BK;
@@ -585,21 +781,39 @@ struct SMask2 {               // block 0 active while the tile overlaps [0, K0),
 };
 
 // ---------------------------------------------------------------------------
-// Epilogue helper: per-wave partial P[t][col] = sum over the wave's 64 rows
-// of Aop[row][t] * V[row][col], as MFMAs with K = rows.  The A fragment of
-// row pair (mb, mb+1) takes rows 16mb+4g+j and 16(mb+1)+4g+j (j = 0..3) as
-// its 8 K slots, which is exactly what a lane holds of V in C layout, so V
-// needs no shuffles.  Results stay in C layout: lane holds P[4g+j][col(r16, nb)].
+// Epilogue helpers.
+//
+// ts_frag4: the A operand (scale * Ts[slot]) of an adapter partial
+// P[t][col] = sum over the wave's rows of Aop[row][t] * V[row][col], one
+// m-block (16 rows, K = 16) per MFMA: a lane's K slots are its rows j = 0..3,
+// exactly what it holds of V in C layout, so V needs no shuffles.
 // ---------------------------------------------------------------------------
 template <class T>
-__device__ __forceinline__ Frag<T> ts_frag(const float* Ts, int slot, float scale, const WaveId& q, int mp) {
-  float v[8];
+__device__ __forceinline__ Frag4<T> ts_frag4(const float* Ts, int slot, float scale, const WaveId& q, int mb) {
+  float v[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    v[j] = scale * Ts[ts_idx(slot, acc_row(q, 2 * mp, j), q.r16)];
-    v[4 + j] = scale * Ts[ts_idx(slot, acc_row(q, 2 * mp + 1, j), q.r16)];
-  }
-  return make_frag<T>(v);
+  for (int j = 0; j < 4; ++j) v[j] = scale * Ts[ts_idx(slot, acc_row(q, mb, j), q.r16)];
+  return make_frag4<T>(v);
+}
+
+// Park: after a transpose-read K-loop a lane holds columns wn*128 + 16 nb +
+// r16 of its rows.  park_mb() writes one m-block of the wave's accumulators
+// (bf16) into a wave-private 4 KB area; park_row() then returns 8
+// consecutive columns wn*128 + 8 r16 .. +7 of row (mb, j), the layout the
+// epilogue's 16-byte loads and stores use.  No barrier: only this wave
+// touches its area.
+__device__ __forceinline__ int park_off(int row, int colbyte) {   // row 0..15, byte 0..255
+  return row * 256 + ((((colbyte >> 5) ^ (((row >> 2) & 3) << 1))) << 5) + (colbyte & 31);
+}
+__device__ __forceinline__ void park_mb(char* base, const f32x4 (&acc)[kMB][8], int mb, const WaveId& q) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<bf16*>(base + park_off(4 * q.g + j, (16 * nb + q.r16) * 2)) = (bf16)acc[mb][nb][j];
+}
+__device__ __forceinline__ void park_row(const char* base, int j, const WaveId& q, float (&v)[8]) {
+  unpack(*reinterpret_cast<const u32x4*>(base + park_off(4 * q.g + j, 16 * q.r16)), v);
 }
 
 // Sum of NOUT partial tiles [16 t][128 cols] over the four wave-rows (fixed

@@ -50,6 +50,49 @@ struct ProArgs {
   int vecP, vecB;
 };
 
+// The prologue's LDS tiles use 128-byte rows (64 bf16 / 32 fp32 along K),
+// eight 16-byte chunks XOR-swizzled with row & 7, and MFMA K-steps of 32 bf16
+// (two per row) or 8 x 4 fp32: its chunking of the column range is
+// independent of the GEMM core's.
+constexpr int kPRowBytes = 128;
+template <class T> struct PT;
+template <> struct PT<bf16> { static constexpr int VEC = 8, BK = 64, KSUB = 2; };
+template <> struct PT<float> { static constexpr int VEC = 4, BK = 32, KSUB = 1; };
+__device__ __forceinline__ int p_off(int row, int chunk) { return row * kPRowBytes + ((chunk ^ (row & 7)) << 4); }
+template <class T> struct PFrag;
+template <> struct PFrag<bf16> { u32x4 v; };
+template <> struct PFrag<float> { u32x4 v0, v1; };
+template <class T> __device__ __forceinline__ PFrag<T> p_frag(const char* buf, int row, int ks, int g);
+template <> __device__ __forceinline__ PFrag<bf16> p_frag<bf16>(const char* buf, int row, int ks, int g) {
+  PFrag<bf16> f;
+  f.v = *reinterpret_cast<const u32x4*>(buf + p_off(row, ks * 4 + g));
+  return f;
+}
+template <> __device__ __forceinline__ PFrag<float> p_frag<float>(const char* buf, int row, int, int g) {
+  PFrag<float> f;
+  f.v0 = *reinterpret_cast<const u32x4*>(buf + p_off(row, 2 * g));
+  f.v1 = *reinterpret_cast<const u32x4*>(buf + p_off(row, 2 * g + 1));
+  return f;
+}
+__device__ __forceinline__ f32x4 p_mma(f32x4 c, const PFrag<bf16>& a, const PFrag<bf16>& b) {
+  Frag<bf16> fa, fb;
+  fa.v = a.v;
+  fb.v = b.v;
+  return mma(c, fa, fb);
+}
+__device__ __forceinline__ f32x4 p_mma(f32x4 c, const PFrag<float>& a, const PFrag<float>& b) {
+  Frag<float> f0, f1, g0, g1;
+  f0.v = a.v0; f1.v = a.v1; g0.v = b.v0; g1.v = b.v1;
+  return mma(mma(c, f0, g0), f1, g1);
+}
+
+__device__ __forceinline__ void transpose4x4_f32(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+  out[0] = (u32x4){in[0].x, in[1].x, in[2].x, in[3].x};
+  out[1] = (u32x4){in[0].y, in[1].y, in[2].y, in[3].y};
+  out[2] = (u32x4){in[0].z, in[1].z, in[2].z, in[3].z};
+  out[3] = (u32x4){in[0].w, in[1].w, in[2].w, in[3].w};
+}
+
 constexpr int kProPr = 0;                       // [256 rows][BK]   row-major P tile
 constexpr int kProPc = 32768;                   // tiles [BK cols][BK tokens] x (256 / BK)
 constexpr int kProBt = 65536;                   // [16 t][BK]       B_p^T chunk
@@ -58,9 +101,9 @@ constexpr int kProLds = kProTT + 3 * 16384;     // 116736
 
 template <class T>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
-  constexpr int VEC = ET<T>::VEC, BK = ET<T>::BK, KSUB = ET<T>::KSUB, HW = BK / 2;
+  constexpr int VEC = PT<T>::VEC, BK = PT<T>::BK, KSUB = PT<T>::KSUB, HW = BK / 2;
   constexpr int NKB = kBM / BK;                 // token tiles per 256 rows
-  constexpr int TTB = 16 * kRowBytes * NKB;     // bytes of one adapter's T^T
+  constexpr int TTB = 16 * kPRowBytes * NKB;     // bytes of one adapter's T^T
   __shared__ __align__(16) char smem[kProLds];
   const WaveId q = wave_id();
   const int rb = blockIdx.x, cr = blockIdx.y;
@@ -77,7 +120,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       const float v = (n < a.N && t < a.r) ? a.s[p] * a.Tp[p][n * a.r + t] : 0.f;
-      char* dst = TT + p * TTB + (row / BK) * (16 * kRowBytes) + lds_off(t, (row % BK) / VEC) + (row % VEC) * ET<T>::BYTES;
+      char* dst = TT + p * TTB + (row / BK) * (16 * kPRowBytes) + p_off(t, (row % BK) / VEC) + (row % VEC) * ET<T>::BYTES;
       *reinterpret_cast<T*>(dst) = from_f<T>(v);
     }
   }
@@ -149,12 +192,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
     // 2. Row-major copy for dT, column-major copy for dB.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(Pr + lds_off(4 * rg4 + i, pc)) = lo[i];
-      *reinterpret_cast<u32x4*>(Pr + lds_off(4 * rg4 + i, pc + 4)) = hi[i];
+      *reinterpret_cast<u32x4*>(Pr + p_off(4 * rg4 + i, pc)) = lo[i];
+      *reinterpret_cast<u32x4*>(Pr + p_off(4 * rg4 + i, pc + 4)) = hi[i];
     }
     {
       const int r0 = 4 * rg4;                     // 4 tokens: tile kb, chunk (r0 % BK) / VEC
-      char* tile = Pc + (r0 / BK) * (BK * kRowBytes);
+      char* tile = Pc + (r0 / BK) * (BK * kPRowBytes);
       const int kc = (r0 % BK) / VEC, sub = (r0 % VEC) * ET<T>::BYTES;
       if constexpr (sizeof(T) == 2) {
         const unsigned* wl = reinterpret_cast<const unsigned*>(lo);
@@ -166,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
           const unsigned l2 = (wl[2 * 4 + c / 2] >> sh) & 0xffffu, l3 = (wl[3 * 4 + c / 2] >> sh) & 0xffffu;
           const unsigned h0 = (wh[0 * 4 + c / 2] >> sh) & 0xffffu, h1 = (wh[1 * 4 + c / 2] >> sh) & 0xffffu;
           const unsigned h2 = (wh[2 * 4 + c / 2] >> sh) & 0xffffu, h3 = (wh[3 * 4 + c / 2] >> sh) & 0xffffu;
-          *reinterpret_cast<u32x2*>(tile + lds_off(pc * VEC + c, kc) + sub) = (u32x2){l0 | (l1 << 16), l2 | (l3 << 16)};
-          *reinterpret_cast<u32x2*>(tile + lds_off(HW + pc * VEC + c, kc) + sub) = (u32x2){h0 | (h1 << 16), h2 | (h3 << 16)};
+          *reinterpret_cast<u32x2*>(tile + p_off(pc * VEC + c, kc) + sub) = (u32x2){l0 | (l1 << 16), l2 | (l3 << 16)};
+          *reinterpret_cast<u32x2*>(tile + p_off(HW + pc * VEC + c, kc) + sub) = (u32x2){h0 | (h1 << 16), h2 | (h3 << 16)};
         }
       } else {
         u32x4 tl[4], th[4];
@@ -175,8 +218,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
         transpose4x4_f32(hi, th);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          *reinterpret_cast<u32x4*>(tile + lds_off(pc * VEC + c, kc)) = tl[c];
-          *reinterpret_cast<u32x4*>(tile + lds_off(HW + pc * VEC + c, kc)) = th[c];
+          *reinterpret_cast<u32x4*>(tile + p_off(pc * VEC + c, kc)) = tl[c];
+          *reinterpret_cast<u32x4*>(tile + p_off(HW + pc * VEC + c, kc)) = th[c];
         }
       }
     }
@@ -191,7 +234,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
       const unsigned* wv = reinterpret_cast<const unsigned*>(&v);
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
-        char* dst = Bt + lds_off(t0 + e, kk / VEC) + (kk % VEC) * ET<T>::BYTES;
+        char* dst = Bt + p_off(t0 + e, kk / VEC) + (kk % VEC) * ET<T>::BYTES;
         if constexpr (sizeof(T) == 2)
           *reinterpret_cast<unsigned short*>(dst) = (unsigned short)((e & 1) ? (wv[e >> 1] >> 16) : (wv[e >> 1] & 0xffffu));
         else
@@ -203,13 +246,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
     // 4. dT_p[rows][t] += P[rows][chunk] . B_p[chunk][t]   (wave w: rows 64w .. 64w+63)
 #pragma unroll
     for (int ks = 0; ks < KSUB; ++ks) {
-      const Frag<T> bf = lds_frag<T>(Bt, q.r16, ks, q.g);
+      const PFrag<T> bf = p_frag<T>(Bt, q.r16, ks, q.g);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const Frag<T> af = lds_frag<T>(Pr, (4 * q.w + i) * 16 + q.r16, ks, q.g);
-        if (p == 0) dT[0][i] = mma(dT[0][i], af, bf);
-        else if (p == 1) dT[1][i] = mma(dT[1][i], af, bf);
-        else dT[2][i] = mma(dT[2][i], af, bf);
+        const PFrag<T> af = p_frag<T>(Pr, (4 * q.w + i) * 16 + q.r16, ks, q.g);
+        if (p == 0) dT[0][i] = p_mma(dT[0][i], af, bf);
+        else if (p == 1) dT[1][i] = p_mma(dT[1][i], af, bf);
+        else dT[2][i] = p_mma(dT[2][i], af, bf);
       }
     }
     // 5. dB_p[col][t] (row-block partial) = P[rows][col]^T . (s_p T_p)[rows][t]
@@ -219,9 +262,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int ks = 0; ks < KSUB; ++ks) {
-          const Frag<T> af = lds_frag<T>(Pc + kb * (BK * kRowBytes), q.w * 16 + q.r16, ks, q.g);
-          const Frag<T> bf = lds_frag<T>(TT + p * TTB + kb * (16 * kRowBytes), q.r16, ks, q.g);
-          db = mma(db, af, bf);
+          const PFrag<T> af = p_frag<T>(Pc + kb * (BK * kPRowBytes), q.w * 16 + q.r16, ks, q.g);
+          const PFrag<T> bf = p_frag<T>(TT + p * TTB + kb * (16 * kPRowBytes), q.r16, ks, q.g);
+          db = p_mma(db, af, bf);
         }
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -277,14 +320,16 @@ struct DownBwdArgs {
   int R, NC;
 };
 
-// dH parking area of the bf16 epilogue: 16 quads x 512 threads x 16 bytes
-// after Ts slot 0 (the only side slot this kernel uses).
-constexpr int kParkOff = kBM * kSlot * 4;
-constexpr int kDownBwdLds = kParkOff + 16 * kGemmThreads * 16;   // 147456
+// The whole dH tile is parked (bf16) before the GLU backward: 16 KB per wave
+// (its 64 rows x 128 columns) after Ts slot 0, the only side slot this kernel
+// uses.  That frees the accumulators for the GLU backward and the partials.
+constexpr int kDownParkOff = kBM * kSlot * 4;
+constexpr int kDownBwdLds = kDownParkOff + 8 * 16384;            // 147456
 static_assert(kDownBwdLds >= kGemmLds && kDownBwdLds <= 163840, "k_down_bwd LDS");
 
 template <class T, int ACT, bool FAST>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
+  constexpr bool TR = sizeof(T) == 2;   // bf16: transpose-read K-loop, natural column order
   __shared__ __align__(16) char smem[kDownBwdLds];
   const WaveId q = wave_id();
   int rb, cb;
@@ -295,22 +340,29 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   const T* Wd = static_cast<const T*>(a.Wd);
   const long h = a.h, ni = a.i;
 
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  KNLoader<T, AOp, 0, KRow1<T>, SRowNone<T>, SMaskNone> ld;
-  ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
-  ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
-  ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
-
   f32x4 acc[kMB][8];
   f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  if constexpr (TR) {
+    using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+    KNTrLoader<AOp, KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
+    ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
+    ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
+    ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+    kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  } else {
+    KNLoader32<KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
+    ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
+    ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
+    ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+    kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  }
 
   load_dT(smem, a.dT_part, a.NCR, a.N, m0, 1);
   const T* Ad = static_cast<const T*>(a.Ad);
   auto fb = [&](int R, int slot, int t0, float* v) {
-    const long n = n0 + lds_row_col(0, R);
+    const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (slot != 0 || n >= ni) return;
     for (int e = 0; e < ET<T>::VEC; ++e)
       if (t0 + e < a.r) v[e] = to_f<T>(Ad[(long)(t0 + e) * ni + n]);
@@ -318,20 +370,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   const float fs[kMaxSide] = {1.f, 0.f, 0.f};
   fold<T>(smem, acc, 1, fs, fb);
 
-  // Epilogue: lane holds dH[row][c0 + nb], nb = 0..7.  For bf16 the dH tile
-  // is parked in LDS first (quad mb*4+j of this thread: 8 bf16), which frees
-  // the accumulator registers for the GLU backward and the three partials.
-  u32x4* park = reinterpret_cast<u32x4*>(smem + kParkOff);
-  if constexpr (sizeof(T) == 2) {
+  // Epilogue: the lane's view of a row is the 8 consecutive columns c0 .. c0+7.
+  char* wpark = smem + kDownParkOff + q.w * 16384;
+  if constexpr (TR) {
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float v[8];
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
-        park[(mb * 4 + j) * kGemmThreads + q.tid] = pack(v);
-      }
+    for (int mb = 0; mb < kMB; ++mb) park_mb(wpark + 4096 * mb, acc, mb, q);
   }
   const T* Gs = static_cast<const T*>(a.G);
   const T* Us = static_cast<const T*>(a.U);
@@ -358,8 +401,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) { G8[e] = 0.f; U8[e] = 0.f; }
     }
-    if constexpr (sizeof(T) == 2) {
-      unpack(park[(mb * 4 + j) * kGemmThreads + q.tid], dH8);
+    if constexpr (TR) {
+      park_row(wpark + 4096 * mb, j, q, dH8);
     } else {
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) dH8[nb] = acc[mb][nb][j];
@@ -379,75 +422,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   };
 
   // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
-  // (s T_g), (s T_u) and dG, dU, as MFMAs whose K runs over this wave's rows.
-  if constexpr (sizeof(T) == 2) {
-    // bf16: 16x16x16 MFMAs, one m-block at a time.  The K slots of a lane are
-    // its own four rows j = 0..3, so only those four GLU rows are live.
+  // (s T_g), (s T_u) and dG, dU, as MFMAs whose K runs over this wave's rows,
+  // one m-block at a time (a lane's K slots are its own rows j = 0..3).
 #pragma unroll
-    for (int mb = 0; mb < kMB; ++mb) {
-      float dt4[4], tg4[4], tu4[4];
+  for (int mb = 0; mb < kMB; ++mb) {
+    float tg4[4], tu4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const long row = m0 + acc_row(q, mb, j);
-        const bool ok = row < a.N && q.r16 < a.r;
-        dt4[j] = Ts[ts_idx(0, acc_row(q, mb, j), q.r16)];
-        tg4[j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
-        tu4[j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
-      }
-      const u32x2 adT = {pack_bf2(dt4[0], dt4[1]), pack_bf2(dt4[2], dt4[3])};
-      const u32x2 aTg = {pack_bf2(tg4[0], tg4[1]), pack_bf2(tg4[2], tg4[3])};
-      const u32x2 aTu = {pack_bf2(tu4[0], tu4[1]), pack_bf2(tu4[2], tu4[3])};
-      u32x2 fh[8], fg[8], fu[8];      // [nb]: slots (2 jp, 2 jp + 1) in dword jp
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {
-        float h0[8], g0[8], u0[8], h1[8], g1[8], u1[8];
-        glu_row(mb, 2 * jp, h0, g0, u0);
-        glu_row(mb, 2 * jp + 1, h1, g1, u1);
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-          fh[nb][jp] = pack_bf2(h0[nb], h1[nb]);
-          fg[nb][jp] = pack_bf2(g0[nb], g1[nb]);
-          fu[nb][jp] = pack_bf2(u0[nb], u1[nb]);
-        }
-      }
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        pacc[0][nb] = mma16(pacc[0][nb], adT, fh[nb]);
-        pacc[1][nb] = mma16(pacc[1][nb], aTg, fg[nb]);
-        pacc[2][nb] = mma16(pacc[2][nb], aTu, fu[nb]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + acc_row(q, mb, j);
+      const bool ok = row < a.N && q.r16 < a.r;
+      tg4[j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
+      tu4[j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
     }
-  } else {
+    const Frag4<T> adT = ts_frag4<T>(Ts, 0, 1.f, q, mb);
+    const Frag4<T> aTg = make_frag4<T>(tg4);
+    const Frag4<T> aTu = make_frag4<T>(tu4);
+    float hv[4][8], gv[4][8], uv[4][8];    // [j][nb]
 #pragma unroll
-    for (int mp = 0; mp < kMB / 2; ++mp) {
-      // fp32: K = 8 rows (m-block pair mp, j) per fragment.
-      const Frag<T> adT = ts_frag<T>(Ts, 0, 1.f, q, mp);
-      float tg[8], tu[8];
+    for (int j = 0; j < 4; ++j) glu_row(mb, j, hv[j], gv[j], uv[j]);
 #pragma unroll
-      for (int mbl = 0; mbl < 2; ++mbl)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const long row = m0 + acc_row(q, 2 * mp + mbl, j);
-          const bool ok = row < a.N && q.r16 < a.r;
-          tg[mbl * 4 + j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
-          tu[mbl * 4 + j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
-        }
-      const Frag<T> aTg = make_frag<T>(tg);
-      const Frag<T> aTu = make_frag<T>(tu);
-      float hv[8][8], gv[8][8], uv[8][8];    // [slot = mbl*4 + j][nb]
-#pragma unroll
-      for (int mbl = 0; mbl < 2; ++mbl)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) glu_row(2 * mp + mbl, j, hv[mbl * 4 + j], gv[mbl * 4 + j], uv[mbl * 4 + j]);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        float b0[8], b1[8], b2[8];
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) { b0[sl] = hv[sl][nb]; b1[sl] = gv[sl][nb]; b2[sl] = uv[sl][nb]; }
-        pacc[0][nb] = mma(pacc[0][nb], adT, make_frag<T>(b0));
-        pacc[1][nb] = mma(pacc[1][nb], aTg, make_frag<T>(b1));
-        pacc[2][nb] = mma(pacc[2][nb], aTu, make_frag<T>(b2));
-      }
+    for (int nb = 0; nb < 8; ++nb) {
+      const float b0[4] = {hv[0][nb], hv[1][nb], hv[2][nb], hv[3][nb]};
+      const float b1[4] = {gv[0][nb], gv[1][nb], gv[2][nb], gv[3][nb]};
+      const float b2[4] = {uv[0][nb], uv[1][nb], uv[2][nb], uv[3][nb]};
+      pacc[0][nb] = mma4(pacc[0][nb], adT, make_frag4<T>(b0));
+      pacc[1][nb] = mma4(pacc[1][nb], aTg, make_frag4<T>(b1));
+      pacc[2][nb] = mma4(pacc[2][nb], aTu, make_frag4<T>(b2));
     }
   }
   float* const parts[3] = {a.pA_d + (long)rb * ni * 16, a.pB_g + (long)rb * ni * 16, a.pB_u + (long)rb * ni * 16};
@@ -456,8 +456,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
 
 // ===========================================================================
 // Shared dX epilogue: store dX, then dA_p partials = (scale_p Ts_p)^T . X.
+// TR: the accumulators are in natural column order and go through a 4 KB
+// per-wave park (after the three Ts slots) one m-block at a time.
 // ===========================================================================
-template <class T, int NA>
+constexpr int kParkOff = kTsBytes;
+
+template <class T, int NA, bool TR>
 __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], const float (&escale)[kMaxSide],
                                             const T* X, T* dX, float* const (&parts)[NA], long N, long h, long m0,
                                             long n0, bool vecO) {
@@ -465,45 +469,43 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], co
   const float* Ts = ts_ptr(smem);
   const long c0 = n0 + q.wn * 128 + 8 * q.r16;
   const int nvalid = (int)min(8L, h - c0);
+  char* wpark = smem + kParkOff + q.w * 4096;
   f32x4 pacc[NA][8];
 #pragma unroll
   for (int o = 0; o < NA; ++o)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mp = 0; mp < kMB / 2; ++mp) {
-    float xv[8][8];   // [slot][nb]
+  for (int mb = 0; mb < kMB; ++mb) {
+    if constexpr (TR) park_mb(wpark, acc, mb, q);
+    float xv[4][8];   // [j][nb]
 #pragma unroll
-    for (int mbl = 0; mbl < 2; ++mbl)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int mb = 2 * mp + mbl, sl = mbl * 4 + j;
-        const long row = m0 + acc_row(q, mb, j);
-        float X8[8];
-        if (row < N && nvalid > 0) {
-          float v[8];
-#pragma unroll
-          for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
-          store_row8<T>(dX + row * h + c0, v, nvalid, vecO);
-          load_row8<T>(X + row * h, c0, h, vecO, X8);
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + acc_row(q, mb, j);
+      if (row < N && nvalid > 0) {
+        float v[8];
+        if constexpr (TR) {
+          park_row(wpark, j, q, v);
         } else {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) X8[e] = 0.f;
+          for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
         }
+        store_row8<T>(dX + row * h + c0, v, nvalid, vecO);
+        load_row8<T>(X + row * h, c0, h, vecO, xv[j]);
+      } else {
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) xv[sl][nb] = X8[nb];
+        for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
       }
-    Frag<T> adT[NA];
+    }
+    Frag4<T> adT[NA];
 #pragma unroll
-    for (int o = 0; o < NA; ++o) adT[o] = ts_frag<T>(Ts, o, escale[o], q, mp);
+    for (int o = 0; o < NA; ++o) adT[o] = ts_frag4<T>(Ts, o, escale[o], q, mb);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      float b[8];
+      const float b[4] = {xv[0][nb], xv[1][nb], xv[2][nb], xv[3][nb]};
+      const Frag4<T> bf = make_frag4<T>(b);
 #pragma unroll
-      for (int sl = 0; sl < 8; ++sl) b[sl] = xv[sl][nb];
-      const Frag<T> bf = make_frag<T>(b);
-#pragma unroll
-      for (int o = 0; o < NA; ++o) pacc[o][nb] = mma(pacc[o][nb], adT[o], bf);
+      for (int o = 0; o < NA; ++o) pacc[o][nb] = mma4(pacc[o][nb], adT[o], bf);
     }
   }
   reduce_store_partials<NA>(smem, pacc, parts, n0, h);
@@ -528,6 +530,7 @@ struct MlpDxArgs {
 
 template <class T, bool FAST>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
+  constexpr bool TR = sizeof(T) == 2;
   __shared__ __align__(16) char smem[FAST ? kGemmLdsX : kGemmLds];
   int rb, cb;
   tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
@@ -538,28 +541,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   const T* Wu = static_cast<const T*>(a.Wu);
   const T* Bg = static_cast<const T*>(a.Bg);
   const T* Bu = static_cast<const T*>(a.Bu);
+  const T* dG = static_cast<const T*>(a.dG);
+  const T* dU = static_cast<const T*>(a.dU);
   constexpr int BK = ET<T>::BK;
-
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  KNLoader<T, AOp, 2, KRow2<T>, SRow2<T>, SMask2> ld;
-  ld.a.init(static_cast<const T*>(a.dG), static_cast<const T*>(a.dU), ni, ni, ni, a.N, m0, a.vecA);
-  ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
-  ld.srow.B0 = Bg; ld.srow.lo0 = 0; ld.srow.hi0 = ni;
-  ld.srow.B1 = Bu; ld.srow.lo1 = ni; ld.srow.hi1 = 2 * ni;
-  ld.srow.ld = r;
-  ld.smask_of.K0 = ni; ld.smask_of.BK = BK;
-  ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
 
   f32x4 acc[kMB][8];
   zero_acc(acc);
   const int nkt = (int)((2 * ni + BK - 1) / BK);
   if constexpr (FAST) {
-    // i % BK == 0: the dG tiles carry only dT_g, the dU tiles only dT_u.  Two
-    // K-loop phases with one side accumulator; dT_g parks in the flush slot.
+    // bf16, i % BK == 0, r == 16: the dG tiles carry only dT_g, the dU tiles
+    // only dT_u.  Two K-loop phases with one side accumulator; dT_g parks in
+    // the flush slot.
+    KNTrLoader<DirectA<T>, KRow2<T>, SRowLin<T>, SMaskOne, 1> ld;
+    ld.a.init(dG, dU, ni, ni, ni, a.N, m0, a.vecA);
+    ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
+    ld.srow.B = Bg; ld.srow.kb = 0; ld.srow.ld = r;          // phase 1: B_g rows
+    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
     f32x4 sacc[1][kMB];
     zero_side(sacc);
     const int nk0 = (int)(ni / BK);
-    ld.smask_of.K0 = 1L << 40;                       // phase 1: block 0 always
     kloop<T, 1>(smem, nk0, ld, acc, sacc);
     {
       const WaveId q = wave_id();
@@ -577,9 +577,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
           for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] += sacc[0][mb][j];
     }
     zero_side(sacc);
-    ld.srow.B0 = Bu;                                 // phase 2: block 0 carries B_u rows
-    ld.srow.lo0 = ni;
-    ld.srow.hi0 = 2 * ni;
+    ld.srow.B = Bu;                                  // phase 2: B_u rows
+    ld.srow.kb = ni;
     kloop<T, 1>(smem, nkt, ld, acc, sacc, nk0);
     side_reduce<T, 1>(smem, sacc, 1);                // dT_u -> slot 1
     {
@@ -588,7 +587,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
       for (int e = threadIdx.x; e < kBM * kSlot; e += kGemmThreads) Ts[e] = fl[e];   // dT_g -> slot 0
       __syncthreads();
     }
+  } else if constexpr (TR) {
+    KNTrLoader<RowsA<T>, KRow2<T>, SRow2<T>, SMask2, 2> ld;
+    ld.a.init(dG, dU, ni, ni, ni, a.N, m0, a.vecA);
+    ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
+    ld.srow.B0 = Bg; ld.srow.lo0 = 0; ld.srow.hi0 = ni;
+    ld.srow.B1 = Bu; ld.srow.lo1 = ni; ld.srow.hi1 = 2 * ni;
+    ld.srow.ld = r;
+    ld.smask_of.K0 = ni; ld.smask_of.BK = BK;
+    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
+    f32x4 sacc[2][kMB];
+    zero_side(sacc);
+    kloop<T, 2>(smem, nkt, ld, acc, sacc);
+    side_reduce<T, 2>(smem, sacc);
   } else {
+    KNLoader32<KRow2<T>, SRow2<T>, SMask2, 2> ld;
+    ld.a.init(dG, dU, ni, ni, ni, a.N, m0, a.vecA);
+    ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
+    ld.srow.B0 = Bg; ld.srow.lo0 = 0; ld.srow.hi0 = ni;
+    ld.srow.B1 = Bu; ld.srow.lo1 = ni; ld.srow.hi1 = 2 * ni;
+    ld.srow.ld = r;
+    ld.smask_of.K0 = ni; ld.smask_of.BK = BK;
+    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
     f32x4 sacc[2][kMB];
     zero_side(sacc);
     kloop<T, 2>(smem, nkt, ld, acc, sacc);
@@ -598,7 +618,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   const T* Ag = static_cast<const T*>(a.Ag);
   const T* Au = static_cast<const T*>(a.Au);
   auto fb = [&](int R, int slot, int t0, float* v) {
-    const long n = n0 + lds_row_col(0, R);
+    const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;
     const T* src = (slot == 0) ? Ag : Au;
     for (int e = 0; e < ET<T>::VEC; ++e)
@@ -608,8 +628,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   fold<T>(smem, acc, 2, fs, fb);
 
   float* const parts[2] = {a.pA_g + (long)rb * h * 16, a.pA_u + (long)rb * h * 16};
-  dx_epilogue<T, 2>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
-                    a.vecO);
+  dx_epilogue<T, 2, TR>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                        a.vecO);
 }
 
 // ===========================================================================
@@ -630,33 +650,42 @@ struct QkvDxArgs {
 
 template <class T, bool FAST>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
+  constexpr bool TR = sizeof(T) == 2;
   __shared__ __align__(16) char smem[kGemmLds];
   int rb, cb;
   tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
   const long n0 = (long)cb * kBN;
   const long h = a.h;
-  const T* W0 = static_cast<const T*>(a.W[0]);
-  const T* W1 = static_cast<const T*>(a.W[1]);
-  const T* W2 = static_cast<const T*>(a.W[2]);
-  const long o1 = a.off[1], o2 = a.off[2], o3 = a.off[3];
-
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  KNLoader<T, AOp, 0, KRow3<T>, SRowNone<T>, SMaskNone> ld;
-  ld.a.init(static_cast<const T*>(a.dP), nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
-  ld.krow.W0 = W0; ld.krow.W1 = W1; ld.krow.W2 = W2;
-  ld.krow.o1 = o1; ld.krow.o2 = o2; ld.krow.o3 = o3; ld.krow.ld = h;
-  ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+  const T* dP = static_cast<const T*>(a.dP);
+  KRow3<T> kr;
+  kr.W0 = static_cast<const T*>(a.W[0]);
+  kr.W1 = static_cast<const T*>(a.W[1]);
+  kr.W2 = static_cast<const T*>(a.W[2]);
+  kr.o1 = a.off[1]; kr.o2 = a.off[2]; kr.o3 = a.off[3]; kr.ld = h;
 
   f32x4 acc[kMB][8];
   f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.O + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  if constexpr (TR) {
+    using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
+    KNTrLoader<AOp, KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
+    ld.a.init(dP, nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
+    ld.krow = kr;
+    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+    kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  } else {
+    KNLoader32<KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
+    ld.a.init(dP, nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
+    ld.krow = kr;
+    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
+    kloop<T, 0>(smem, nkt, ld, acc, sacc);
+  }
 
   load_dT(smem, a.dT_part, a.NCR, a.N, m0, 3);
   auto fb = [&](int R, int slot, int t0, float* v) {
-    const long n = n0 + lds_row_col(0, R);
+    const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;
     const T* src = static_cast<const T*>(a.A[0]);
     if (slot == 1) src = static_cast<const T*>(a.A[1]);
@@ -668,8 +697,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
   fold<T>(smem, acc, 3, fs, fb);
 
   float* const parts[3] = {a.pA[0] + (long)rb * h * 16, a.pA[1] + (long)rb * h * 16, a.pA[2] + (long)rb * h * 16};
-  dx_epilogue<T, 3>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
-                    a.vecO);
+  dx_epilogue<T, 3, TR>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                        a.vecO);
 }
 
 // ===========================================================================

@@ -58,15 +58,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
   ld.vecS = a.vecS;
   ld.smask = 3u;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
+  for (int qq = 0; qq < 2; ++qq) {
     int up, j;
     gateup_row(ld.row_of(qq), j0, up, j);
     ld.brow[qq] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
   }
+  ld.srow = nullptr;
   {
     const int sr = ld.side_row();       // side rows 0..31: A_g rows 0..15, A_u rows 0..15
-    const int t = sr & 15;
-    ld.srow = (sr < 32 && t < a.r) ? ((sr < 16) ? Ag : Au) + (long)t * a.h : nullptr;
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr((sr < 16) ? Ag : Au, sr & 15, a.r, a.h, Ag);
   }
 
   f32x4 acc[kMB][8];
@@ -162,13 +162,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   ld.vecS = a.vecS;
   ld.smask = 1u;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
+  for (int qq = 0; qq < 2; ++qq) {
     const long n = n0 + lds_row_col(0, ld.row_of(qq));
     ld.brow[qq] = (n < a.O) ? W + n * a.K : nullptr;
   }
+  ld.srow = nullptr;
   {
     const int sr = ld.side_row();
-    ld.srow = (sr < 16 && sr < a.r) ? A + (long)sr * a.K : nullptr;
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(A, sr, a.r, a.K, A);
   }
 
   f32x4 acc[kMB][8];
@@ -273,7 +274,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   ld.vecS = a.vecS;
   ld.smask = (1u << nslot) - 1u;
 #pragma unroll
-  for (int qq = 0; qq < 4; ++qq) {
+  for (int qq = 0; qq < 2; ++qq) {
     const int o = n0 + lds_row_col(LG, ld.row_of(qq));
     if (o < O) {
       const int p = proj_of(o);
@@ -282,15 +283,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       ld.brow[qq] = nullptr;
     }
   }
+  ld.srow = nullptr;
   {
     const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
-    const int sl = sr >> 4, t = sr & 15;
-    const T* p = nullptr;
-    if (sl < NS && sl < nslot && t < a.r) {
-      const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
-      p = static_cast<const T*>(a.A[pj]) + (long)t * a.h;
+    if (sr >= 0) {
+      const int sl = sr >> 4, t = sr & 15;
+      const T* base = nullptr;
+      if (sl < nslot) {
+        const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+        base = static_cast<const T*>(a.A[pj]);
+      }
+      ld.srow = decltype(ld)::side_ptr(base, t, a.r, a.h, static_cast<const T*>(a.A[plist[0]]));
     }
-    ld.srow = p;
   }
 
   f32x4 acc[kMB][8];

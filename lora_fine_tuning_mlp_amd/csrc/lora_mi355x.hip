@@ -100,7 +100,8 @@ size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
 // Direct global->LDS loads need full bf16 K tiles, 16-byte aligned rows and
-// 32-bit row offsets; other calls take the register-staged (masked) loaders.
+// 32-bit row offsets (each call adds what its other operands need); other
+// calls take the register-staged (masked) loaders.
 bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> ptrs);
 
 // Launch Fast<true> when allowed (bf16 only), else Fast<false>.
@@ -144,7 +145,7 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
   const long N = d.n_tokens, h = d.hidden, i = d.inter;
   const long R = cdiv(N, kBM);
   const size_t es = esz(d.dtype);
-  const int BK = d.dtype == LORA_BF16 ? ET<bf16>::BK : ET<float>::BK;
+  const int BK = d.dtype == LORA_BF16 ? PT<bf16>::BK : PT<float>::BK;   // prologue column chunk
   w.NCH = (int)cdiv(h, BK);
   w.NCR = w.NCH < 8 ? w.NCH : 8;
   w.CPC = (int)cdiv(w.NCH, w.NCR);
@@ -179,7 +180,7 @@ QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
   const long O = (long)(d.n_q + 2 * d.n_kv) * d.head_dim;
   const long R = cdiv(N, kBM);
   const size_t es = esz(d.dtype);
-  const int BK = d.dtype == LORA_BF16 ? ET<bf16>::BK : ET<float>::BK;
+  const int BK = d.dtype == LORA_BF16 ? PT<bf16>::BK : PT<float>::BK;   // prologue column chunk
   w.cs = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
   w.sn = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
   w.NCH = (int)(O / BK);
@@ -261,7 +262,7 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (h % V == 0) && al16(g.A) && al16(u.A);
     a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
     a.R = R; a.NC = (int)cdiv(i, 128);
-    const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W});
+    const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W, g.A, u.A});
     const int rc = LORA_LAUNCH_FAST(0, fast, (k_gateup_fwd<T, ACT, true>), (k_gateup_fwd<T, ACT, false>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -276,7 +277,7 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (i % V == 0) && al16(dn.A);
     a.vecO = (h % 8 == 0) && al16(Y);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W});
+    const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W, dn.A});
     const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
                                     dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -320,7 +321,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecW = (i % V == 0) && al16(dn.W);
     a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
     a.R = R; a.NC = (int)cdiv(i, kBN);
-    const bool fast = fast_ok(DT<T>::code, h, N, {dY});
+    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0;
     const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -336,7 +337,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU});
+    const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16;
     const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
                                     dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -401,7 +402,7 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
   a.vecO = oal;
   a.R = (int)cdiv(N, kBM);
   a.NC = (int)cdiv(a.off[3], kBN);
-  const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W});
+  const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W, pr[0]->A, pr[1]->A, pr[2]->A});
   // Most projections any 256-column tile overlaps: 1, 2 or 3 side blocks.
   int ns = 1;
   for (int cb = 0; cb < a.NC; ++cb) {
@@ -476,7 +477,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.vecW = (h % V == 0) && wal;
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP});
+    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0;
     rc = LORA_LAUNCH_FAST(7, fast, (k_qkv_dx_bwd<T, true>), (k_qkv_dx_bwd<T, false>), dim3(a.R * a.NC),
                           dim3(kGemmThreads), st, a);
     if (rc) return rc;
