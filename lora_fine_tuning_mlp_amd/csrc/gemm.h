@@ -285,6 +285,124 @@ __device__ __forceinline__ void kloop(char* smem, int nkt, Loader& ld, f32x4 (&a
   }
 }
 
+// ---------------------------------------------------------------------------
+// Forward fast path (bf16, weights stored [N][K]): K tiles of 64 in
+// 128-byte LDS rows (eight chunks swizzled with row & 7), two stages.  With
+// K-contiguous operands every direct load then requests whole 128-byte cache
+// lines; 64-byte rows would split each line over two tiles and double the
+// L1 -> L2 requests.  The price is one tile of loads in flight instead of
+// three, which these kernels, with both operands K-contiguous, can afford.
+// ---------------------------------------------------------------------------
+constexpr int kRow2 = 128;
+constexpr int kStage2A = kBM * kRow2;                                 // 32768
+constexpr int kStage2 = (kBM + kBN + kSlot * kMaxSide) * kRow2;      // 71680
+static_assert(2 * kStage2 <= kGemmLds, "two 128-byte-row stages");
+__device__ __forceinline__ int lds_off2(int row, int chunk) { return row * kRow2 + ((chunk ^ (row & 7)) << 4); }
+__device__ __forceinline__ Frag<bf16> lds_frag2(const char* buf, int row, int ks, int g) {
+  Frag<bf16> f;
+  f.v = *reinterpret_cast<const u32x4*>(buf + lds_off2(row, ks * 4 + g));
+  return f;
+}
+// A 1 KB direct block is 8 rows of 128 bytes: lane l writes physical chunk
+// l & 7 of row 8 blk + (l >> 3), so it fetches logical chunk (l & 7) ^ (l >> 3).
+__device__ __forceinline__ int direct2_chunk(int lane) { return (lane & 7) ^ (lane >> 3); }
+__device__ __forceinline__ int direct2_row(int it) { return 8 * direct_blk(it) + (int)((threadIdx.x & 63) >> 3); }
+
+// All operands direct: A rows (tokens), B rows (output columns, resolved by
+// the kernel for rows row_of(it), it = 0..3; nullptr -> bfallback) and side
+// rows (lanes 0 .. 16 NSIDE - 1 of each wave; ranks past r clamped as in
+// NKLoader).  Requires K % 64 == 0, 16-byte aligned rows, 32-bit A offsets.
+template <int NSIDE>
+struct NKPairLoader {
+  static constexpr int kLoads = 8 + (NSIDE > 0 ? 1 : 0);
+  const bf16* A;
+  int aoff[4];
+  const bf16* brow[4];
+  const bf16* bfallback;
+  const bf16* srow;
+  unsigned smask;
+  __device__ static __forceinline__ int row_of(int it) { return direct2_row(it); }
+  __device__ static __forceinline__ int side_row() {
+    const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+    return (l < 16 * NSIDE) ? (w * 16 * NSIDE + l) >> 3 : -1;
+  }
+  __device__ static __forceinline__ const bf16* side_ptr(const bf16* base, int t, int r, long Kd,
+                                                         const bf16* fallback) {
+    return base ? base + (long)min(t, r - 1) * Kd : fallback;
+  }
+  __device__ __forceinline__ void init_a(const bf16* A0, long lda, long M, long m0) {
+    A = A0;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      long row = m0 + direct2_row(it);
+      if (row > M - 1) row = M - 1;
+      aoff[it] = (int)(row * lda);
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
+    const int L = threadIdx.x & 63;
+    const long k = (long)kt * 64 + direct2_chunk(L) * 8;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(A + aoff[it] + k, As + direct_blk(it) * 1024);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const bf16* p = brow[it] ? brow[it] : bfallback;
+      g2lds16(p + k, Bs + direct_blk(it) * 1024);
+    }
+    if constexpr (NSIDE > 0) {
+      if (L < 16 * NSIDE) {
+        const int w = threadIdx.x >> 6;
+        const int ci = w * 16 * NSIDE + L, sr = ci >> 3;
+        const int chunk = (ci & 7) ^ (sr & 7);
+        g2lds16(srow + (long)kt * 64 + chunk * 8, Bs + kBN * kRow2 + w * 256 * NSIDE);
+      }
+    }
+  }
+};
+
+template <int NSIDE>
+__device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<NSIDE>& ld, f32x4 (&acc)[kMB][8],
+                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB]) {
+  constexpr int L = NKPairLoader<NSIDE>::kLoads;
+  const WaveId q = wave_id();
+  if (nkt <= 0) return;
+  ld.issue(0, smem, smem + kStage2A);
+  sync_tiles<L>(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const char* As = smem + (kt & 1) * kStage2;
+    const char* Bs = As + kStage2A;
+    if (kt + 1 < nkt) {
+      char* An = smem + ((kt + 1) & 1) * kStage2;
+      ld.issue(kt + 1, An, An + kStage2A);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag<bf16> af[kMB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag2(As, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const Frag<bf16> bfr = lds_frag2(Bs, q.wn * 128 + nb * 16 + q.r16, ks, q.g);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      }
+      if constexpr (NSIDE > 0) {
+        if (ks == q.wn) {
+#pragma unroll
+          for (int sb = 0; sb < NSIDE; ++sb) {
+            if ((ld.smask >> sb) & 1u) {
+              const Frag<bf16> bfr = lds_frag2(Bs, kBN + sb * 16 + q.r16, ks, q.g);
+#pragma unroll
+              for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = mma(sacc[sb][mb], af[mb], bfr);
+            }
+          }
+        }
+      }
+    }
+    sync_tiles<L>(0);
+  }
+}
+
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[kMB][8]) {
 #pragma unroll
   for (int i = 0; i < kMB; ++i)

@@ -49,33 +49,43 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
   const T* Ag = static_cast<const T*>(a.Ag);
   const T* Au = static_cast<const T*>(a.Au);
 
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  NKLoader<T, AOp, 2> ld;
-  ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
-  ld.bfallback = Wg;
-  ld.K = a.h;
-  ld.vecB = a.vecW;
-  ld.vecS = a.vecS;
-  ld.smask = 3u;
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
+  auto brow_of = [&](int R) -> const T* {
     int up, j;
-    gateup_row(ld.row_of(qq), j0, up, j);
-    ld.brow[qq] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
-  }
-  ld.srow = nullptr;
-  {
-    const int sr = ld.side_row();       // side rows 0..31: A_g rows 0..15, A_u rows 0..15
-    if (sr >= 0) ld.srow = decltype(ld)::side_ptr((sr < 16) ? Ag : Au, sr & 15, a.r, a.h, Ag);
-  }
+    gateup_row(R, j0, up, j);
+    return (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
+  };
+  auto side_base = [&](int sb) -> const T* { return sb == 0 ? Ag : Au; };   // side rows: A_g, then A_u
 
   f32x4 acc[kMB][8];
   f32x4 sacc[2][kMB];
   zero_acc(acc);
   zero_side(sacc);
-
-  const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, 2>(smem, nkt, ld, acc, sacc);
+  if constexpr (FAST) {
+    NKPairLoader<2> ld;
+    ld.init_a(X, a.h, a.N, m0);
+    ld.bfallback = Wg;
+    ld.smask = 3u;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
+    ld.srow = Ag;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = ld.side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, Ag);
+    kloop2<2>(smem, a.h / 64, ld, acc, sacc);
+  } else {
+    NKLoader<T, RowsA<T>, 2> ld;
+    ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
+    ld.bfallback = Wg;
+    ld.K = a.h;
+    ld.vecB = a.vecW;
+    ld.vecS = a.vecS;
+    ld.smask = 3u;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) ld.brow[qq] = brow_of(ld.row_of(qq));
+    ld.srow = nullptr;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, Ag);
+    kloop<T, 2>(smem, (a.h + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
+  }
   side_reduce<T, 2>(smem, sacc);
 
   // The row block's T_g, T_u are saved once (by column block 0).
@@ -153,31 +163,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   const T* W = static_cast<const T*>(a.W);
   const T* A = static_cast<const T*>(a.A);
 
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  NKLoader<T, AOp, 1> ld;
-  ld.a.init(Z, nullptr, a.K, 0, a.K, a.N, m0, a.vecA);
-  ld.bfallback = W;
-  ld.K = a.K;
-  ld.vecB = a.vecW;
-  ld.vecS = a.vecS;
-  ld.smask = 1u;
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const long n = n0 + lds_row_col(0, ld.row_of(qq));
-    ld.brow[qq] = (n < a.O) ? W + n * a.K : nullptr;
-  }
-  ld.srow = nullptr;
-  {
-    const int sr = ld.side_row();
-    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(A, sr, a.r, a.K, A);
-  }
+  auto brow_of = [&](int R) -> const T* {
+    const long n = n0 + lds_row_col(0, R);
+    return (n < a.O) ? W + n * a.K : nullptr;
+  };
 
   f32x4 acc[kMB][8];
   f32x4 sacc[1][kMB];
   zero_acc(acc);
   zero_side(sacc);
-  const int nkt = (a.K + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, 1>(smem, nkt, ld, acc, sacc);
+  if constexpr (FAST) {
+    NKPairLoader<1> ld;
+    ld.init_a(Z, a.K, a.N, m0);
+    ld.bfallback = W;
+    ld.smask = 1u;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
+    ld.srow = A;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = ld.side_ptr(A, sr, a.r, a.K, A);
+    kloop2<1>(smem, a.K / 64, ld, acc, sacc);
+  } else {
+    NKLoader<T, RowsA<T>, 1> ld;
+    ld.a.init(Z, nullptr, a.K, 0, a.K, a.N, m0, a.vecA);
+    ld.bfallback = W;
+    ld.K = a.K;
+    ld.vecB = a.vecW;
+    ld.vecS = a.vecS;
+    ld.smask = 1u;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) ld.brow[qq] = brow_of(ld.row_of(qq));
+    ld.srow = nullptr;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(A, sr, a.r, a.K, A);
+    kloop<T, 1>(smem, (a.K + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
+  }
   side_reduce<T, 1>(smem, sacc);
 
   if (cb == 0 && q.tid < kBM) {
@@ -265,44 +285,49 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
   auto slot_of = [&](int p) { return (plist[0] == p) ? 0 : ((plist[1] == p) ? 1 : 2); };
 
-  using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-  NKLoader<T, AOp, NS> ld;
-  ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
-  ld.bfallback = static_cast<const T*>(a.W[0]);
-  ld.K = a.h;
-  ld.vecB = a.vecW;
-  ld.vecS = a.vecS;
-  ld.smask = (1u << nslot) - 1u;
-#pragma unroll
-  for (int qq = 0; qq < 2; ++qq) {
-    const int o = n0 + lds_row_col(LG, ld.row_of(qq));
-    if (o < O) {
-      const int p = proj_of(o);
-      ld.brow[qq] = static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
-    } else {
-      ld.brow[qq] = nullptr;
-    }
-  }
-  ld.srow = nullptr;
-  {
-    const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
-    if (sr >= 0) {
-      const int sl = sr >> 4, t = sr & 15;
-      const T* base = nullptr;
-      if (sl < nslot) {
-        const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
-        base = static_cast<const T*>(a.A[pj]);
-      }
-      ld.srow = decltype(ld)::side_ptr(base, t, a.r, a.h, static_cast<const T*>(a.A[plist[0]]));
-    }
-  }
+  auto brow_of = [&](int R) -> const T* {
+    const int o = n0 + lds_row_col(LG, R);
+    if (o >= O) return nullptr;
+    const int p = proj_of(o);
+    return static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
+  };
+  auto side_base = [&](int sl) -> const T* {        // side block sl: adapter of plist[sl]
+    if (sl >= nslot) return nullptr;
+    const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+    return static_cast<const T*>(a.A[pj]);
+  };
+  const T* afall = static_cast<const T*>(a.A[plist[0]]);
 
   f32x4 acc[kMB][8];
   f32x4 sacc[NS][kMB];
   zero_acc(acc);
   zero_side(sacc);
-  const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
-  kloop<T, NS>(smem, nkt, ld, acc, sacc);
+  if constexpr (FAST) {
+    NKPairLoader<NS> ld;
+    ld.init_a(X, a.h, a.N, m0);
+    ld.bfallback = static_cast<const T*>(a.W[0]);
+    ld.smask = (1u << nslot) - 1u;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
+    ld.srow = afall;
+    const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
+    if (sr >= 0) ld.srow = ld.side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
+    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
+  } else {
+    NKLoader<T, RowsA<T>, NS> ld;
+    ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
+    ld.bfallback = static_cast<const T*>(a.W[0]);
+    ld.K = a.h;
+    ld.vecB = a.vecW;
+    ld.vecS = a.vecS;
+    ld.smask = (1u << nslot) - 1u;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) ld.brow[qq] = brow_of(ld.row_of(qq));
+    ld.srow = nullptr;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
+    kloop<T, NS>(smem, (a.h + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
+  }
   side_reduce<T, NS>(smem, sacc);
 
   // T_p is saved by the tile holding projection p's first column.

@@ -262,7 +262,7 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (h % V == 0) && al16(g.A) && al16(u.A);
     a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
     a.R = R; a.NC = (int)cdiv(i, 128);
-    const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W, g.A, u.A});
+    const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W, g.A, u.A}) && h % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(0, fast, (k_gateup_fwd<T, ACT, true>), (k_gateup_fwd<T, ACT, false>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -277,7 +277,7 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecS = (i % V == 0) && al16(dn.A);
     a.vecO = (h % 8 == 0) && al16(Y);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W, dn.A});
+    const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W, dn.A}) && i % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
                                     dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -402,7 +402,8 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
   a.vecO = oal;
   a.R = (int)cdiv(N, kBM);
   a.NC = (int)cdiv(a.off[3], kBN);
-  const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W, pr[0]->A, pr[1]->A, pr[2]->A});
+  const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W, pr[0]->A, pr[1]->A, pr[2]->A}) &&
+                    h % 64 == 0;
   // Most projections any 256-column tile overlaps: 1, 2 or 3 side blocks.
   int ns = 1;
   for (int cb = 0; cb < a.NC; ++cb) {
