@@ -62,10 +62,11 @@ def stored_traffic(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
-    """Time the CPU oracle (as it stands) on `tokens` tokens of each workload.
-    The QKV sample keeps the workload's sequence length (batches of seq) when
-    `tokens` is a multiple of it, else it is one sequence of `tokens`."""
+def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int, reps: int = 1):
+    """Time the CPU oracle (as it stands) on `tokens` tokens of each workload,
+    `reps` times over.  The QKV sample keeps the workload's sequence length
+    (batches of seq) when `tokens` is a multiple of it, else it is one
+    sequence of `tokens`."""
     import dataclasses
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -86,20 +87,21 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int):
     shape = dict(batch=qkv_s.batch, seq=qkv_s.seq, n_q=qkv_s.n_q, n_kv=qkv_s.n_kv, head_dim=qkv_s.head_dim, theta=qkv_s.theta)
     sc = (qkv_s.scale,) * 3
     t0 = time.perf_counter()
-    orc.qkv_fwd(pq, scales=sc, **shape)
-    orc.qkv_bwd(pq, dQ, dK, dV, scales=sc, **shape)
-    orc.mlp_fwd(pm, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
-    orc.mlp_bwd(pm, dY, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
+    for _ in range(reps):
+        orc.qkv_fwd(pq, scales=sc, **shape)
+        orc.qkv_bwd(pq, dQ, dK, dV, scales=sc, **shape)
+        orc.mlp_fwd(pm, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
+        orc.mlp_bwd(pm, dY, mlp_s.act, mlp_s.scale, mlp_s.scale, mlp_s.scale)
     dt = time.perf_counter() - t0
-    flops = qkv_s.flops() + mlp_s.flops()
+    flops = reps * (qkv_s.flops() + mlp_s.flops())
     threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": f"{tokens} tokens of each workload (QKV as {qkv_s.batch} x {qkv_s.seq}; MLP {tokens} rows): one "
-                  f"fwd+bwd of both in float64 numpy, {dt:.2f} s wall",
+        "sample": f"{tokens} tokens of each workload (QKV as {qkv_s.batch} x {qkv_s.seq}; MLP {tokens} rows): "
+                  f"fwd+bwd of both in float64 numpy, {reps} time(s), {dt:.2f} s wall",
         "seconds": dt,
     }
 
@@ -110,6 +112,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle baseline")
+    ap.add_argument("--cpu-reps", type=int, default=2, help="repetitions of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates rocprofv3 byte counters)")
@@ -210,7 +213,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(qkv_cfg, mlp_cfg, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(qkv_cfg, mlp_cfg, args.cpu_tokens, args.cpu_reps)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

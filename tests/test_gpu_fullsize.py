@@ -1,0 +1,111 @@
+"""GPU parity at the benchmark's full sizes, in the launch configuration
+bench.py times (same binding classes, same kernels).
+
+Every output row (Y, G, U, T, dX; Q, K, V) depends only on its own token,
+and zeroing the upstream gradient outside a set of rows removes every other
+row's contribution to dA and dB.  So the GPU runs the whole problem, the
+upstream gradient is masked to a row sample, and the CPU oracle runs on the
+sampled rows only: per-token outputs are compared on the sample, adapter
+gradients in full (they are then exact sums over the sample).  For QKV the
+sample is one whole sequence, so RoPE positions are unchanged.
+"""
+import numpy as np
+import pytest
+import torch
+
+from lora_fine_tuning_mlp_amd import synthetic as S
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    from lora_fine_tuning_mlp_amd import binding
+    binding.lib()   # fails loudly when the HIP library is missing
+
+
+def sample_rows(n: int, seed: int) -> np.ndarray:
+    """First and last 24 rows (tile edges) plus 80 random interior rows."""
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(24, n - 24), size=80, replace=False)
+    return np.unique(np.concatenate([np.arange(24), mid, np.arange(n - 24, n)]))
+
+
+PER_TOKEN_MLP = ("Y", "G", "U", "T_gate", "T_up", "T_down", "dX")
+GRADS_MLP = ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")
+
+
+@pytest.mark.parametrize("cfg", [S.C2, S.C3, S.C4_MLP], ids=lambda c: c.name)
+def test_mlp_full_size(cfg):
+    gc.say(f"full-size mlp {cfg.name}: generating inputs")
+    t = S.mlp_inputs(cfg, 0)
+    rows = sample_rows(cfg.n_tokens, 11)
+    mask = torch.zeros(cfg.n_tokens, 1, dtype=t["dY"].dtype)
+    mask[torch.from_numpy(rows)] = 1
+    dY = t["dY"] * mask
+    gc.say(f"full-size mlp {cfg.name}: GPU")
+    out = gc.run_mlp_gpu(cfg, t, dY_cpu=dY)
+    gc.say(f"full-size mlp {cfg.name}: oracle on {len(rows)} rows")
+    ref = gc.run_mlp_oracle(cfg, t, dY_cpu=dY, rows=rows)
+    sampled = {k: out[k][rows] for k in PER_TOKEN_MLP}
+    sampled.update({k: out[k] for k in GRADS_MLP})
+    gc.compare(f"{cfg.name}/sampled", sampled, ref, gc.TOL[cfg.dtype])
+    # Rows outside the sample had zero upstream gradient: their dX is exactly 0.
+    others = np.setdiff1d(np.arange(cfg.n_tokens), rows)
+    assert not np.any(out["dX"][others]), "dX non-zero where dY is zero"
+
+
+def test_mlp_full_size_deterministic():
+    cfg = S.C2
+    t = S.mlp_inputs(cfg, 1)
+    gc.say("full-size mlp determinism: two GPU runs")
+    a = gc.run_mlp_gpu(cfg, t)
+    b = gc.run_mlp_gpu(cfg, t)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def qkv_batch_view(cfg: S.QKVConfig, out: dict, b: int) -> dict:
+    s0, s1 = b * cfg.seq, (b + 1) * cfg.seq
+    v = {k: out[k][b:b + 1] for k in ("Q", "K", "V")}
+    for k in ("T_q", "T_k", "T_v", "dX"):
+        v[k] = out[k][s0:s1]
+    for p in "qkv":
+        v["dA_" + p] = out["dA_" + p]
+        v["dB_" + p] = out["dB_" + p]
+    return v
+
+
+@pytest.mark.parametrize("cfg", [S.C1], ids=lambda c: c.name)
+def test_qkv_full_size_one_sequence(cfg):
+    b = cfg.batch - 1
+    gc.say(f"full-size qkv {cfg.name}: generating inputs")
+    t = S.qkv_inputs(cfg, 0)
+    grads = {}
+    for k in ("dQ", "dK", "dV"):
+        g = torch.zeros_like(t[k])
+        g[b] = t[k][b]
+        grads[k] = g
+    gc.say(f"full-size qkv {cfg.name}: GPU")
+    out = gc.run_qkv_gpu(cfg, t, grads_cpu=grads)
+    gc.say(f"full-size qkv {cfg.name}: oracle on sequence {b}")
+    one = S.QKVConfig(cfg.name + "_seq", 1, cfg.seq, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.rank,
+                      cfg.scale, cfg.theta, cfg.dtype)
+    s0, s1 = b * cfg.seq, (b + 1) * cfg.seq
+    t1 = {k: v for k, v in t.items() if k not in ("X", "dQ", "dK", "dV")}
+    t1["X"] = t["X"][s0:s1]
+    g1 = {k: grads[k][b:b + 1] for k in grads}
+    ref = gc.run_qkv_oracle(one, t1, grads_cpu=g1)
+    gc.compare(f"{cfg.name}/seq{b}", qkv_batch_view(cfg, out, b), ref, gc.TOL[cfg.dtype])
+    others = np.concatenate([np.arange(0, s0), np.arange(s1, cfg.n_tokens)])
+    assert not np.any(out["dX"][others]), "dX non-zero where the upstream gradient is zero"
+
+
+def test_qkv_c4_full():
+    cfg = S.C4_QKV
+    t = S.qkv_inputs(cfg, 0)
+    gc.say("full-size qkv C4: GPU + full oracle")
+    gc.compare(cfg.name, gc.run_qkv_gpu(cfg, t), gc.run_qkv_oracle(cfg, t), gc.TOL[cfg.dtype])
