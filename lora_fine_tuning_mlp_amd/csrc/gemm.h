@@ -845,6 +845,31 @@ __device__ __forceinline__ void load_row8(const T* row, long c0, long len, bool 
   }
 }
 
+// 8 consecutive values of one row, still packed as loaded (one 16-byte
+// chunk for bf16, two for fp32), so a fetch can be issued well before use.
+template <class T> struct Row8 { u32x4 c[sizeof(T) / 2]; };
+template <class T>
+__device__ __forceinline__ Row8<T> fetch_row8(const T* row, long c0, long len, bool vec) {
+  Row8<T> r;
+  r.c[0] = gload<T>(row, c0, len, vec);
+  if constexpr (sizeof(T) == 4) r.c[1] = gload<T>(row, c0 + 4, len, vec);
+  return r;
+}
+template <class T>
+__device__ __forceinline__ void unpack_row8(const Row8<T>& r, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    unpack(r.c[0], v);
+  } else {
+    float t4[4];
+    unpack(r.c[0], t4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = t4[e];
+    unpack(r.c[1], t4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[4 + e] = t4[e];
+  }
+}
+
 // Row maps for KN loaders (default-constructible functors).
 template <class T>
 struct KRow1 {                // rows of one [K][ld] matrix

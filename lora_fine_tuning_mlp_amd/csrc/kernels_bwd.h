@@ -288,18 +288,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
       }
 }
 
-// Fill Ts[slot][m][t] = sum over column ranges of the prologue's dT partials.
-__device__ __forceinline__ void load_dT(char* smem, const float* dT_part, int NCR, long N, long m0, int nslot) {
-  float* Ts = ts_ptr(smem);
-  const int m = threadIdx.x & (kBM - 1), th = (threadIdx.x >> 8) * 8;   // row, half of the ranks
-  const long n = m0 + m;
+// dT[p][n][t] = sum over the prologue's column ranges c (fixed order) of its
+// partials [NCR][3][N][16], for the adapters p < nadp.  One float4 per thread.
+__global__ __launch_bounds__(256) void k_dt_sum(const float* part, float* dT, int NCR, long N) {
+  const int p = blockIdx.y;
+  const long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;   // float4 index within [N][16]
+  if (e4 >= N * 4) return;
+  f32x4 v = {0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < NCR; ++c) v += reinterpret_cast<const f32x4*>(part + ((long)c * 3 + p) * N * 16)[e4];
+  reinterpret_cast<f32x4*>(dT + (long)p * N * 16)[e4] = v;
+}
+
+// Fill Ts[slot][m][t] (slots < nslot) with the rows m0 .. m0+255 of dT [3][N][16].
+__device__ __forceinline__ void load_dT(char* smem, const float* dT, long N, long m0, int nslot) {
+  f32x4* Ts = reinterpret_cast<f32x4*>(ts_ptr(smem));
   for (int sl = 0; sl < nslot; ++sl)
 #pragma unroll
-    for (int t = th; t < th + 8; ++t) {
-      float v = 0.f;
-      if (n < N)
-        for (int c = 0; c < NCR; ++c) v += dT_part[(((long)c * 3 + sl) * N + n) * 16 + t];
-      Ts[ts_idx(sl, m, t)] = v;
+    for (int i = 0; i < 2; ++i) {
+      const int e = threadIdx.x + kGemmThreads * i;        // float4 index within the slot: row e / 4
+      const long n = m0 + (e >> 2);
+      f32x4 v = {0.f, 0.f, 0.f, 0.f};
+      if (n < N) v = reinterpret_cast<const f32x4*>(dT + ((long)sl * N + n) * 16)[e & 3];
+      Ts[sl * kBM * 4 + e] = v;
     }
   __syncthreads();
 }
@@ -311,7 +321,7 @@ struct DownBwdArgs {
   const void* dY; const void* Wd; const void* Ad;
   const void* G; const void* U;
   const float* Tg; const float* Tu;
-  const float* dT_part; int NCR;
+  const float* dT;              // [3][N][16], summed prologue partials
   float sg, su;
   void* dG; void* dU;
   float* pA_d; float* pB_g; float* pB_u;     // [R][i][16]
@@ -359,7 +369,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
     kloop<T, 0>(smem, nkt, ld, acc, sacc);
   }
 
-  load_dT(smem, a.dT_part, a.NCR, a.N, m0, 1);
+  load_dT(smem, a.dT, a.N, m0, 1);
   const T* Ad = static_cast<const T*>(a.Ad);
   auto fb = [&](int R, int slot, int t0, float* v) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
@@ -389,18 +399,36 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // GLU backward of one row: H, dG, dU for the lane's 8 columns; stores dG, dU.
-  auto glu_row = [&](int mb, int j, float (&h8)[8], float (&dg8)[8], float (&du8)[8]) {
+  // Per m-block inputs of the GLU backward: G and U for the lane's 8 columns
+  // of its four rows, and (s T_g), (s T_u) of those rows for its rank r16.
+  // They are fetched as one batch per m-block (four rows in flight at once
+  // instead of one); fetching further ahead does not fit the registers.
+  struct MbIn {
+    Row8<T> g[4], u[4];
+    float tg[4], tu[4];
+  };
+  auto fetch = [&](int mb, MbIn& in) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + acc_row(q, mb, j);
+      const bool live = row < a.N && nvalid > 0;
+      in.g[j] = fetch_row8<T>(live ? Gs + row * ni : nullptr, c0, ni, a.vecO);
+      in.u[j] = fetch_row8<T>(live ? Us + row * ni : nullptr, c0, ni, a.vecO);
+      const bool ok = row < a.N && q.r16 < a.r;
+      in.tg[j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
+      in.tu[j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
+    }
+  };
+  // GLU backward of m-block mb (H, dG, dU for the lane's 8 columns of each
+  // row; stores dG, dU), then the row-block partials: dA_d^T from dT_d
+  // (Ts slot 0) and H; dB_g, dB_u from (s T_g), (s T_u) and dG, dU, as MFMAs
+  // whose K runs over the block's rows (a lane's K slots are its rows j).
+  auto glu_row = [&](int mb, int j, const MbIn& in, float (&h8)[8], float (&g8)[8], float (&u8)[8]) {
     const long row = m0 + acc_row(q, mb, j);
     const bool live = row < a.N && nvalid > 0;
     float G8[8], U8[8], dH8[8];
-    if (live) {
-      load_row8<T>(Gs + row * ni, c0, ni, a.vecO, G8);
-      load_row8<T>(Us + row * ni, c0, ni, a.vecO, U8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) { G8[e] = 0.f; U8[e] = 0.f; }
-    }
+    unpack_row8<T>(in.g[j], G8);
+    unpack_row8<T>(in.u[j], U8);
     if constexpr (TR) {
       park_row(wpark + 4096 * mb, j, q, dH8);
     } else {
@@ -411,44 +439,68 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
     for (int nb = 0; nb < 8; ++nb) {
       float ph, dph;
       act_both<ACT>(G8[nb], ph, dph);
-      dg8[nb] = dH8[nb] * U8[nb] * dph;
-      du8[nb] = dH8[nb] * ph;
+      g8[nb] = dH8[nb] * U8[nb] * dph;
+      u8[nb] = dH8[nb] * ph;
       h8[nb] = ph * U8[nb];
     }
     if (live) {
-      store_row8<T>(dGo + row * ni + c0, dg8, nvalid, a.vecO);
-      store_row8<T>(dUo + row * ni + c0, du8, nvalid, a.vecO);
+      store_row8<T>(dGo + row * ni + c0, g8, nvalid, a.vecO);
+      store_row8<T>(dUo + row * ni + c0, u8, nvalid, a.vecO);
     }
   };
-
-  // Row-block partials: dA_d^T from dT_d (Ts slot 0) and H; dB_g, dB_u from
-  // (s T_g), (s T_u) and dG, dU, as MFMAs whose K runs over this wave's rows,
-  // one m-block at a time (a lane's K slots are its own rows j = 0..3).
+  auto process = [&](int mb, const MbIn& in) {
+    const Frag4<T> adT = ts_frag4<T>(Ts, 0, 1.f, q, mb);
+    const Frag4<T> aTg = make_frag4<T>(in.tg);
+    const Frag4<T> aTu = make_frag4<T>(in.tu);
+    if constexpr (sizeof(T) == 2) {
+      // bf16: rows (2 jp, 2 jp + 1) go straight into packed fragment dwords.
+      u32x2 fh[8], fg[8], fu[8];
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {
+        float h0[8], g0[8], u0[8], h1[8], g1[8], u1[8];
+        glu_row(mb, 2 * jp, in, h0, g0, u0);
+        glu_row(mb, 2 * jp + 1, in, h1, g1, u1);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+          fh[nb][jp] = pack_bf2(h0[nb], h1[nb]);
+          fg[nb][jp] = pack_bf2(g0[nb], g1[nb]);
+          fu[nb][jp] = pack_bf2(u0[nb], u1[nb]);
+        }
+      }
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        Frag4<T> b0, b1, b2;
+        b0.v = fh[nb];
+        b1.v = fg[nb];
+        b2.v = fu[nb];
+        pacc[0][nb] = mma4(pacc[0][nb], adT, b0);
+        pacc[1][nb] = mma4(pacc[1][nb], aTg, b1);
+        pacc[2][nb] = mma4(pacc[2][nb], aTu, b2);
+      }
+    } else {
+      float hv[4][8], gv[4][8], uv[4][8];    // [j][nb]
+#pragma unroll
+      for (int j = 0; j < 4; ++j) glu_row(mb, j, in, hv[j], gv[j], uv[j]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const float b0[4] = {hv[0][nb], hv[1][nb], hv[2][nb], hv[3][nb]};
+        const float b1[4] = {gv[0][nb], gv[1][nb], gv[2][nb], gv[3][nb]};
+        const float b2[4] = {uv[0][nb], uv[1][nb], uv[2][nb], uv[3][nb]};
+        pacc[0][nb] = mma4(pacc[0][nb], adT, make_frag4<T>(b0));
+        pacc[1][nb] = mma4(pacc[1][nb], aTg, make_frag4<T>(b1));
+        pacc[2][nb] = mma4(pacc[2][nb], aTu, make_frag4<T>(b2));
+      }
+    }
+  };
+  constexpr int PD = 0;                      // fetch distance in m-blocks
+  MbIn in[kMB];
+#pragma unroll
+  for (int mb = 0; mb < PD; ++mb) fetch(mb, in[mb]);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
-    float tg4[4], tu4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const long row = m0 + acc_row(q, mb, j);
-      const bool ok = row < a.N && q.r16 < a.r;
-      tg4[j] = ok ? a.sg * a.Tg[row * a.r + q.r16] : 0.f;
-      tu4[j] = ok ? a.su * a.Tu[row * a.r + q.r16] : 0.f;
-    }
-    const Frag4<T> adT = ts_frag4<T>(Ts, 0, 1.f, q, mb);
-    const Frag4<T> aTg = make_frag4<T>(tg4);
-    const Frag4<T> aTu = make_frag4<T>(tu4);
-    float hv[4][8], gv[4][8], uv[4][8];    // [j][nb]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) glu_row(mb, j, hv[j], gv[j], uv[j]);
-#pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const float b0[4] = {hv[0][nb], hv[1][nb], hv[2][nb], hv[3][nb]};
-      const float b1[4] = {gv[0][nb], gv[1][nb], gv[2][nb], gv[3][nb]};
-      const float b2[4] = {uv[0][nb], uv[1][nb], uv[2][nb], uv[3][nb]};
-      pacc[0][nb] = mma4(pacc[0][nb], adT, make_frag4<T>(b0));
-      pacc[1][nb] = mma4(pacc[1][nb], aTg, make_frag4<T>(b1));
-      pacc[2][nb] = mma4(pacc[2][nb], aTu, make_frag4<T>(b2));
-    }
+    if (mb + PD < kMB) fetch(mb + PD, in[mb + PD]);
+    process(mb, in[mb]);
+    asm volatile("" ::: "memory");   // keep later fetches from being hoisted (register pressure)
   }
   float* const parts[3] = {a.pA_d + (long)rb * ni * 16, a.pB_g + (long)rb * ni * 16, a.pB_u + (long)rb * ni * 16};
   reduce_store_partials<3>(smem, pacc, parts, n0, ni);
@@ -475,8 +527,24 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], co
   for (int o = 0; o < NA; ++o)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  // X rows of m-block mb (the B operand of the dA partials), fetched as one
+  // batch per m-block and, with at most two adapters (registers allow), one
+  // m-block ahead so the loads overlap the previous block's work.
+  auto fetch = [&](int mb, Row8<T> (&x)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + acc_row(q, mb, j);
+      const bool live = row < N && nvalid > 0;
+      x[j] = fetch_row8<T>(live ? X + row * h : nullptr, c0, h, vecO);
+    }
+  };
+  constexpr int PD = NA <= 2 ? 1 : 0;
+  Row8<T> xin[kMB][4];
+#pragma unroll
+  for (int mb = 0; mb < PD; ++mb) fetch(mb, xin[mb]);
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
+    if (mb + PD < kMB) fetch(mb + PD, xin[mb + PD]);
     if constexpr (TR) park_mb(wpark, acc, mb, q);
     float xv[4][8];   // [j][nb]
 #pragma unroll
@@ -491,11 +559,8 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], co
           for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
         }
         store_row8<T>(dX + row * h + c0, v, nvalid, vecO);
-        load_row8<T>(X + row * h, c0, h, vecO, xv[j]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) xv[j][e] = 0.f;
       }
+      unpack_row8<T>(xin[mb][j], xv[j]);
     }
     Frag4<T> adT[NA];
 #pragma unroll
@@ -507,6 +572,7 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], co
 #pragma unroll
       for (int o = 0; o < NA; ++o) pacc[o][nb] = mma4(pacc[o][nb], adT[o], bf);
     }
+    asm volatile("" ::: "memory");   // keep later fetches from being hoisted (register pressure)
   }
   reduce_store_partials<NA>(smem, pacc, parts, n0, h);
 }
@@ -638,7 +704,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
 struct QkvDxArgs {
   const void* dP;
   const void* W[3]; const void* A[3];
-  const float* dT_part; int NCR;
+  const float* dT;                // [3][N][16]
   const void* X;
   void* dX;
   float* pA[3];                   // [R][h][16]
@@ -683,7 +749,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
     kloop<T, 0>(smem, nkt, ld, acc, sacc);
   }
 
-  load_dT(smem, a.dT_part, a.NCR, a.N, m0, 3);
+  load_dT(smem, a.dT, a.N, m0, 3);
   auto fb = [&](int R, int slot, int t0, float* v) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;

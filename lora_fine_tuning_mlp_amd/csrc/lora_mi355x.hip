@@ -38,7 +38,7 @@ int ok() {
 
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
-                        "k_down_bwd",   "k_mlp_dx_bwd", "k_qkv_dx_bwd", "k_reduce"};
+                        "k_down_bwd",   "k_mlp_dx_bwd", "k_qkv_dx_bwd", "k_reduce",    "k_dt_sum"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -135,7 +135,7 @@ struct Carver {
 struct MlpWs {
   void* H;
   void *dG, *dU;
-  float *dT_part, *pA_d, *pB_g, *pB_u, *pA_g, *pA_u, *pB_d;
+  float *dT_part, *dT, *pA_d, *pB_g, *pB_u, *pA_g, *pA_u, *pB_d;
   int NCR, NCH, CPC;
   size_t bytes;
 };
@@ -155,6 +155,7 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
     w.dG = c.take<void>(N * i * es);
     w.dU = c.take<void>(N * i * es);
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    w.dT = c.take<float>((size_t)3 * N * 16 * 4);
     w.pA_d = c.take<float>(R * i * 16 * 4);
     w.pB_g = c.take<float>(R * i * 16 * 4);
     w.pB_u = c.take<float>(R * i * 16 * 4);
@@ -169,7 +170,7 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
 struct QkvWs {
   float *cs, *sn;
   void* dP;
-  float *dT_part, *pA[3], *dB_part;
+  float *dT_part, *dT, *pA[3], *dB_part;
   int NCR, NCH, CPC;
   size_t bytes;
 };
@@ -189,6 +190,7 @@ QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
   if (pass == 1) {
     w.dP = c.take<void>(N * O * es);
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    w.dT = c.take<float>((size_t)3 * N * 16 * 4);
     for (int p = 0; p < 3; ++p) w.pA[p] = c.take<float>(R * h * 16 * 4);
     w.dB_part = c.take<float>(R * O * 16 * 4);
   }
@@ -305,14 +307,17 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
     a.vecP = (h % V == 0) && al16(dY);
     a.vecB = (r % V == 0) && al16(dn.B);
-    const int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+    int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+    if (rc) return rc;
+    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
+                w.NCR, N);
     if (rc) return rc;
   }
   {
     DownBwdArgs a{};
     a.dY = dY; a.Wd = dn.W; a.Ad = dn.A; a.G = G; a.U = U;
     a.Tg = T3; a.Tu = T3 + N * r;
-    a.dT_part = w.dT_part; a.NCR = w.NCR;
+    a.dT = w.dT;
     a.sg = g.scale; a.su = u.scale;
     a.dG = w.dG; a.dU = w.dU;
     a.pA_d = w.pA_d; a.pB_g = w.pB_g; a.pB_u = w.pB_u;
@@ -461,6 +466,9 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.vecB = (r % V == 0) && bal;
     rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
     if (rc) return rc;
+    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 3), dim3(256), st, (const float*)w.dT_part, w.dT,
+                w.NCR, N);
+    if (rc) return rc;
   }
   {
     QkvDxArgs a{};
@@ -470,7 +478,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
       a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.pA[p] = w.pA[p];
       wal = wal && al16(pr[p]->W);
     }
-    a.dT_part = w.dT_part; a.NCR = w.NCR;
+    a.dT = w.dT;
     a.X = X; a.dX = dX;
     a.N = N; a.h = h; a.O = O; a.r = r;
     for (int k = 0; k < 4; ++k) a.off[k] = off[k];
