@@ -359,11 +359,44 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   fold<T>(smem, acc, nslot, fs, fb);
 
   // RoPE + split.  Groups alternate first half / second half of a head, so
-  // block b (first half) pairs with block b + cw in the same lane.
+  // block b (first half) pairs with block b + cw in the same lane.  Per
+  // m-block the lane first fetches the cos / sin of its four rows (cw
+  // consecutive entries each, one vector load), then rotates and stores.
   constexpr int cw = 8 >> LG;
+  constexpr int NG = 8 / (2 * cw);                    // head-half pair groups per lane
   const int half = a.d >> 1;
+  const float* __restrict__ cs = a.cs;
+  const float* __restrict__ sn = a.sn;
+  auto load_cw = [&](const float* ptr, float (&v)[cw]) {
+    if constexpr (cw == 4) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(ptr);
+      v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+    } else {
+      typedef float f32x2 __attribute__((ext_vector_type(2)));
+      const f32x2 t = *reinterpret_cast<const f32x2*>(ptr);
+      v[0] = t.x; v[1] = t.y;
+    }
+  };
 #pragma unroll
-  for (int mb = 0; mb < kMB; ++mb)
+  for (int mb = 0; mb < kMB; ++mb) {
+    float cc[4][NG][cw], ss[4][NG][cw];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const long row = m0 + acc_row(q, mb, j);
+      const int s = (int)(row % a.S);
+#pragma unroll
+      for (int gi = 0; gi < NG; ++gi) {
+        const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+        const int jj = (o1 - a.off[proj_of(o1)]) % a.d;
+        if (row < a.N && o1 < O && proj_of(o1) < 2) {
+          load_cw(cs + (long)s * half + jj, cc[j][gi]);
+          load_cw(sn + (long)s * half + jj, ss[j][gi]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < cw; ++e) { cc[j][gi][e] = 1.f; ss[j][gi][e] = 0.f; }
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long row = m0 + acc_row(q, mb, j);
@@ -371,7 +404,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       const int s = (int)(row % a.S);
       const long bidx = row / a.S;
 #pragma unroll
-      for (int b1 = 0; b1 < 8; b1 += 2 * cw) {       // first block of each head-half pair group
+      for (int gi = 0; gi < NG; ++gi) {
+        const int b1 = 2 * cw * gi;                  // first block of the pair group
         const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, b1);
         if (o1 >= O) continue;
         const int p = proj_of(o1);
@@ -383,9 +417,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
           const float x1 = acc[mb][b1 + e][j];
           const float x2 = acc[mb][b1 + cw + e][j];
           if (p < 2) {
-            const float c = a.cs[(long)s * half + jj + e], sn = a.sn[(long)s * half + jj + e];
-            y1[e] = x1 * c - x2 * sn;
-            y2[e] = x2 * c + x1 * sn;
+            y1[e] = x1 * cc[j][gi][e] - x2 * ss[j][gi][e];
+            y2[e] = x2 * cc[j][gi][e] + x1 * ss[j][gi][e];
           } else {
             y1[e] = x1;
             y2[e] = x2;
@@ -396,6 +429,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
         gstore<T, cw>(dst + half, y2, cw, a.vecO);
       }
     }
+  }
 }
 
 }  // namespace lora
