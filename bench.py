@@ -41,7 +41,7 @@ def kernel_flops(qkv, mlp):
         "k_qkv_fwd": 2 * Nq * hq * O + 6 * Nq * hq * rq + 2 * Nq * rq * O,
         "k_down_bwd": 2 * N * h * i + 8 * N * r * i,
         "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h,
-        "k_qkv_dx_bwd": 2 * Nq * O * hq + 12 * Nq * rq * hq,
+        "k_proj_dx_bwd": 2 * Nq * O * hq + 12 * Nq * rq * hq,
     }
 
 

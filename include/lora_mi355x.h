@@ -102,15 +102,26 @@ typedef struct {
   int32_t hidden;
   int32_t n_q;        /* query heads */
   int32_t n_kv;       /* key/value heads; n_q % n_kv == 0 (GQA) */
-  int32_t head_dim;   /* d: 32, 64 or 128 */
+  int32_t head_dim;   /* d: 64 or 128 */
   int32_t rank;       /* r, 1..LORA_MAX_RANK */
   int32_t dtype;      /* LORA_F32 | LORA_BF16 */
   double rope_theta;  /* RoPE base theta > 0 */
 } lora_qkv_desc_t;
 
+/* One LoRA linear (e.g. an attention output projection): X [N, in] -> Y [N, out]. */
+typedef struct {
+  int64_t n_tokens;      /* N */
+  int32_t in_features;   /* in */
+  int32_t out_features;  /* out */
+  int32_t rank;          /* r, 1..LORA_MAX_RANK */
+  int32_t dtype;         /* LORA_F32 | LORA_BF16 */
+} lora_linear_desc_t;
+
 /* ---- workspace queries (pass: 0 = forward, 1 = backward) ---------------- */
 size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass);
 size_t lora_qkv_workspace_bytes(const lora_qkv_desc_t* desc, int pass);
+/* 0 for the forward (which needs none; workspace may then be NULL). */
+size_t lora_linear_workspace_bytes(const lora_linear_desc_t* desc, int pass);
 
 /*
  * MLP forward.
@@ -158,6 +169,25 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
                  const lora_proj_t* q, const lora_proj_t* k, const lora_proj_t* v,
                  void* dX, void* dA_q, void* dB_q, void* dA_k, void* dB_k, void* dA_v, void* dB_v,
                  void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * LoRA linear forward (Opake, "Model Patches and Kernels", "Fused LoRA
+ * operations": the single adapted projection, opake_lora_w; Axolotl,
+ * "monkeypatch.lora_kernels", original_apply_o for the attention output).
+ *   X [N, in]; proj: W [out, in], A [r, in], B [out, r].
+ *   Writes Y [N, out] = X W^T + s (X A^T) B^T and T [N, r] float32 = X A^T.
+ */
+int lora_linear_fwd(const lora_linear_desc_t* desc, const void* X, const lora_proj_t* proj,
+                    void* Y, void* T, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * LoRA linear backward for the loss <dY, Y>, W frozen.
+ *   dY [N, out]; X and T as for the forward.
+ *   Writes dX [N, in], dA [r, in], dB [out, r] (call dtype, float32 accumulation).
+ */
+int lora_linear_bwd(const lora_linear_desc_t* desc, const void* dY, const void* X, const void* T,
+                    const lora_proj_t* proj, void* dX, void* dA, void* dB,
+                    void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---- diagnostics --------------------------------------------------------- */
 const char* lora_status_string(int status);

@@ -41,6 +41,11 @@ class QkvDesc(ctypes.Structure):
                 ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32), ("rope_theta", ctypes.c_double)]
 
 
+class LinearDesc(ctypes.Structure):
+    _fields_ = [("n_tokens", ctypes.c_int64), ("in_features", ctypes.c_int32), ("out_features", ctypes.c_int32),
+                ("rank", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
 class Proj(ctypes.Structure):
     _fields_ = [("W", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("scale", ctypes.c_float)]
 
@@ -59,6 +64,11 @@ _SIGS = {
     "lora_qkv_bwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, _P, _P, _P, _P, ctypes.POINTER(Proj),
                                     ctypes.POINTER(Proj), ctypes.POINTER(Proj), _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
+    "lora_linear_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(LinearDesc), ctypes.c_int]),
+    "lora_linear_fwd": (ctypes.c_int, [ctypes.POINTER(LinearDesc), _P, ctypes.POINTER(Proj), _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
+    "lora_linear_bwd": (ctypes.c_int, [ctypes.POINTER(LinearDesc), _P, _P, _P, ctypes.POINTER(Proj), _P, _P, _P,
+                                       _P, ctypes.c_size_t, _P]),
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_last_error_message": (ctypes.c_char_p, []),
     "lora_version": (ctypes.c_char_p, []),
@@ -119,6 +129,10 @@ def qkv_desc(batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta) -> Qkv
                    DTYPE_CODES[dtype], float(theta))
 
 
+def linear_desc(n_tokens, in_features, out_features, rank, dtype) -> LinearDesc:
+    return LinearDesc(int(n_tokens), int(in_features), int(out_features), int(rank), DTYPE_CODES[dtype])
+
+
 # ---- raw entry points (same names as the C ABI) ------------------------------
 
 def lora_mlp_workspace_bytes(desc: MlpDesc, pass_: int) -> int:
@@ -155,6 +169,20 @@ def lora_qkv_bwd(desc, dQ, dK, dV, X, T, q: Proj, k: Proj, v: Proj, dX, dA_q, dB
                               ctypes.byref(k), ctypes.byref(v), _ptr(dX), _ptr(dA_q), _ptr(dB_q), _ptr(dA_k),
                               _ptr(dB_k), _ptr(dA_v), _ptr(dB_v), _ptr(workspace), workspace.numel(),
                               _stream(stream)))
+
+
+def lora_linear_workspace_bytes(desc: LinearDesc, pass_: int) -> int:
+    return int(lib().lora_linear_workspace_bytes(ctypes.byref(desc), int(pass_)))
+
+
+def lora_linear_fwd(desc, X, p: Proj, Y, T, workspace=None, stream=None):
+    _check(lib().lora_linear_fwd(ctypes.byref(desc), _ptr(X), ctypes.byref(p), _ptr(Y), _ptr(T), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), _stream(stream)))
+
+
+def lora_linear_bwd(desc, dY, X, T, p: Proj, dX, dA, dB, workspace, stream=None):
+    _check(lib().lora_linear_bwd(ctypes.byref(desc), _ptr(dY), _ptr(X), _ptr(T), ctypes.byref(p), _ptr(dX), _ptr(dA),
+                                 _ptr(dB), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
 # ---- timing -------------------------------------------------------------------
@@ -259,4 +287,31 @@ class QKV:
         g = self.grads
         lora_qkv_bwd(self.desc, dQ, dK, dV, self.t["X"], self.T, self.q, self.k, self.v, self.dX, g["dA_q"],
                      g["dB_q"], g["dA_k"], g["dB_k"], g["dA_v"], g["dB_v"], self.ws_bwd, stream)
+        return self.dX
+
+
+class Linear:
+    """One LoRA linear's weights on the device plus the buffers one fwd+bwd needs."""
+
+    def __init__(self, t: Dict[str, torch.Tensor], n_tokens, in_features, out_features, rank, dtype, scale=2.0):
+        self.t = t
+        self.desc = linear_desc(n_tokens, in_features, out_features, rank, dtype)
+        self.dtype = t["X"].dtype
+        dev = t["X"].device
+        self.N, self.k, self.o, self.r = int(n_tokens), int(in_features), int(out_features), int(rank)
+        self.p = proj(t["W"], t["A"], t["B"], scale)
+        e = dict(device=dev, dtype=self.dtype)
+        self.Y = torch.empty(self.N, self.o, **e)
+        self.T = torch.empty(self.N, self.r, device=dev, dtype=torch.float32)
+        self.dX = torch.empty(self.N, self.k, **e)
+        self.grads = {"dA": torch.empty(self.r, self.k, **e), "dB": torch.empty(self.o, self.r, **e)}
+        self.ws_bwd = torch.empty(max(1, lora_linear_workspace_bytes(self.desc, 1)), device=dev, dtype=torch.uint8)
+
+    def forward(self, stream=None):
+        lora_linear_fwd(self.desc, self.t["X"], self.p, self.Y, self.T, None, stream)
+        return self.Y
+
+    def backward(self, dY, stream=None):
+        lora_linear_bwd(self.desc, dY, self.t["X"], self.T, self.p, self.dX, self.grads["dA"], self.grads["dB"],
+                        self.ws_bwd, stream)
         return self.dX

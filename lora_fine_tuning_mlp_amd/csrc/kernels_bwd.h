@@ -17,7 +17,8 @@
 //                   epilogue, plus row-block partials of dA_d, dB_g, dB_u.
 //   k_mlp_dx_bwd    dX = [dG|dU] [W_g; W_u] + dT_g A_g + dT_u A_u (K = 2i);
 //                   dT_g, dT_u ride the K-loop; partials of dA_g, dA_u.
-//   k_qkv_dx_bwd    dX = dP [W_q; W_k; W_v] + sum_p dT_p A_p; partials of dA_p.
+//   k_proj_dx_bwd   dX = dP [W_q; W_k; W_v] + sum_p dT_p A_p (or one LoRA linear's
+//                   dX = dY W + dT A); partials of dA_p.
 //   k_reduce        fixed-order sum of partials -> dA / dB in the call dtype.
 #pragma once
 
@@ -699,10 +700,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
 }
 
 // ===========================================================================
-// QKV dX
+// Projection dX over NP projections stacked along K (QKV: NP = 3; one LoRA
+// linear: NP = 1): dX = dP [W_1; ...; W_NP] + sum_p dT_p A_p; partials of dA_p.
 // ===========================================================================
-struct QkvDxArgs {
-  const void* dP;
+struct ProjDxArgs {
+  const void* dP;                 // [N][O], projection p in columns off[p] .. off[p+1]
   const void* W[3]; const void* A[3];
   const float* dT;                // [3][N][16]
   const void* X;
@@ -714,8 +716,8 @@ struct QkvDxArgs {
   int R, NC;
 };
 
-template <class T, bool FAST>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
+template <class T, bool FAST, int NP>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_proj_dx_bwd(ProjDxArgs a) {
   constexpr bool TR = sizeof(T) == 2;
   __shared__ __align__(16) char smem[kGemmLds];
   int rb, cb;
@@ -726,8 +728,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
   const T* dP = static_cast<const T*>(a.dP);
   KRow3<T> kr;
   kr.W0 = static_cast<const T*>(a.W[0]);
-  kr.W1 = static_cast<const T*>(a.W[1]);
-  kr.W2 = static_cast<const T*>(a.W[2]);
+  kr.W1 = static_cast<const T*>(a.W[NP > 1 ? 1 : 0]);
+  kr.W2 = static_cast<const T*>(a.W[NP > 2 ? 2 : 0]);
   kr.o1 = a.off[1]; kr.o2 = a.off[2]; kr.o3 = a.off[3]; kr.ld = h;
 
   f32x4 acc[kMB][8];
@@ -749,22 +751,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_dx_bwd(QkvDxArgs a) {
     kloop<T, 0>(smem, nkt, ld, acc, sacc);
   }
 
-  load_dT(smem, a.dT, a.N, m0, 3);
+  load_dT(smem, a.dT, a.N, m0, NP);
   auto fb = [&](int R, int slot, int t0, float* v) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;
-    const T* src = static_cast<const T*>(a.A[0]);
-    if (slot == 1) src = static_cast<const T*>(a.A[1]);
-    if (slot == 2) src = static_cast<const T*>(a.A[2]);
+    const T* src = static_cast<const T*>(a.A[slot < NP ? slot : 0]);
     for (int e = 0; e < ET<T>::VEC; ++e)
       if (t0 + e < a.r) v[e] = to_f<T>(src[(long)(t0 + e) * h + n]);
   };
   const float fs[kMaxSide] = {1.f, 1.f, 1.f};
-  fold<T>(smem, acc, 3, fs, fb);
+  fold<T>(smem, acc, NP, fs, fb);
 
-  float* const parts[3] = {a.pA[0] + (long)rb * h * 16, a.pA[1] + (long)rb * h * 16, a.pA[2] + (long)rb * h * 16};
-  dx_epilogue<T, 3, TR>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
-                        a.vecO);
+  const long po = (long)rb * h * 16;
+  if constexpr (NP == 1) {
+    float* const parts[1] = {a.pA[0] + po};
+    dx_epilogue<T, 1, TR>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                          a.vecO);
+  } else {
+    static_assert(NP == 3, "one or three stacked projections");
+    float* const parts[3] = {a.pA[0] + po, a.pA[1] + po, a.pA[2] + po};
+    dx_epilogue<T, 3, TR>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
+                          a.vecO);
+  }
 }
 
 // ===========================================================================

@@ -38,7 +38,7 @@ int ok() {
 
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
-                        "k_down_bwd",   "k_mlp_dx_bwd", "k_qkv_dx_bwd", "k_reduce",    "k_dt_sum"};
+                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -198,6 +198,31 @@ QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
   return w;
 }
 
+// LoRA linear workspace (backward only).
+struct LinWs {
+  float *dT_part, *dT, *pA, *dB_part;
+  int NCR, NCH, CPC;
+  size_t bytes;
+};
+LinWs lin_ws(const lora_linear_desc_t& d, int pass, void* base) {
+  LinWs w{};
+  Carver c(base);
+  const long N = d.n_tokens, in = d.in_features, out = d.out_features;
+  const long R = cdiv(N, kBM);
+  const int BK = d.dtype == LORA_BF16 ? PT<bf16>::BK : PT<float>::BK;   // prologue column chunk
+  w.NCH = (int)cdiv(out, BK);
+  w.NCR = w.NCH < 8 ? w.NCH : 8;
+  w.CPC = (int)cdiv(w.NCH, w.NCR);
+  if (pass == 1) {
+    w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    w.dT = c.take<float>((size_t)3 * N * 16 * 4);
+    w.pA = c.take<float>(R * in * 16 * 4);
+    w.dB_part = c.take<float>(R * out * 16 * 4);
+  }
+  w.bytes = c.off;
+  return w;
+}
+
 // ---- validation ---------------------------------------------------------------
 int check_mlp(const lora_mlp_desc_t* d) {
   if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
@@ -230,6 +255,18 @@ int check_qkv(const lora_qkv_desc_t* d) {
     return fail(LORA_ERR_UNSUPPORTED, "head_dim %d not supported (64 or 128)", d->head_dim);
   if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
   if ((long)d->batch * d->seq > (1L << 30)) return fail(LORA_ERR_UNSUPPORTED, "too many tokens");
+  return LORA_OK;
+}
+
+int check_linear(const lora_linear_desc_t* d) {
+  if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
+  if (d->n_tokens <= 0 || d->in_features <= 0 || d->out_features <= 0 || d->rank <= 0)
+    return fail(LORA_ERR_SHAPE, "sizes must be positive (n_tokens=%lld in=%d out=%d rank=%d)",
+                (long long)d->n_tokens, d->in_features, d->out_features, d->rank);
+  if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
+  if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
+  if (d->n_tokens > (1L << 30) || (long)d->in_features * d->out_features > (1L << 31))
+    return fail(LORA_ERR_UNSUPPORTED, "sizes beyond the 32-bit tile index range");
   return LORA_OK;
 }
 
@@ -471,7 +508,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     if (rc) return rc;
   }
   {
-    QkvDxArgs a{};
+    ProjDxArgs a{};
     a.dP = w.dP;
     bool wal = true;
     for (int p = 0; p < 3; ++p) {
@@ -487,7 +524,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
     const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0;
-    rc = LORA_LAUNCH_FAST(7, fast, (k_qkv_dx_bwd<T, true>), (k_qkv_dx_bwd<T, false>), dim3(a.R * a.NC),
+    rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 3>), (k_proj_dx_bwd<T, false, 3>), dim3(a.R * a.NC),
                           dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
@@ -509,6 +546,84 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
   return ok();
 }
 
+// ---- LoRA linear ----------------------------------------------------------------
+template <class T>
+int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_t& p, void* Y, void* Tsv,
+                    hipStream_t st) {
+  const long N = d.n_tokens;
+  const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
+  LinearArgs a{};
+  a.Z = X; a.W = p.W; a.A = p.A; a.B = p.B; a.s = p.scale;
+  a.Y = Y; a.T = static_cast<float*>(Tsv);
+  a.N = N; a.K = in; a.O = out; a.r = r;
+  a.vecA = (in % V == 0) && al16(X);
+  a.vecW = (in % V == 0) && al16(p.W);
+  a.vecS = (in % V == 0) && al16(p.A);
+  a.vecO = (out % 8 == 0) && al16(Y);
+  a.R = (int)cdiv(N, kBM); a.NC = (int)cdiv(out, kBN);
+  const bool fast = fast_ok(DT<T>::code, in, N, {X, p.W, p.A}) && in % 64 == 0;
+  const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
+                                  dim3(kGemmThreads), st, a);
+  if (rc) return rc;
+  return ok();
+}
+
+template <class T>
+int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, const void* Tsv,
+                    const lora_proj_t& p, void* dX, void* dA, void* dB, const LinWs& w, hipStream_t st) {
+  const long N = d.n_tokens;
+  const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
+  const int R = (int)cdiv(N, kBM);
+  {
+    ProArgs a{};
+    a.qkv = 0;
+    a.P = dY;
+    a.Bp[0] = p.B; a.Tp[0] = static_cast<const float*>(Tsv); a.s[0] = p.scale;
+    a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
+    a.nadp = 1;
+    a.dT_part = w.dT_part; a.dB_part = w.dB_part;
+    a.N = N; a.O = out; a.r = r;
+    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+    a.vecP = (out % V == 0) && al16(dY);
+    a.vecB = (r % V == 0) && al16(p.B);
+    int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+    if (rc) return rc;
+    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
+                w.NCR, N);
+    if (rc) return rc;
+  }
+  {
+    ProjDxArgs a{};
+    a.dP = dY;
+    a.W[0] = a.W[1] = a.W[2] = p.W;
+    a.A[0] = a.A[1] = a.A[2] = p.A;
+    a.pA[0] = a.pA[1] = a.pA[2] = w.pA;
+    a.dT = w.dT;
+    a.X = X; a.dX = dX;
+    a.N = N; a.h = in; a.O = out; a.r = r;
+    a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
+    a.vecA = (out % V == 0) && al16(dY);
+    a.vecW = (in % V == 0) && al16(p.W);
+    a.vecO = (in % 8 == 0) && al16(dX) && al16(X);
+    a.R = R; a.NC = (int)cdiv(in, kBN);
+    const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0;
+    const int rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 1>), (k_proj_dx_bwd<T, false, 1>),
+                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+    if (rc) return rc;
+  }
+  {
+    RedArgs a{};
+    a.r = r;
+    a.njobs = 2;
+    const long si = (long)in * 16, so = (long)out * 16;
+    a.job[0] = RedJob{w.pA, si, si, R, in, 1, dA};
+    a.job[1] = RedJob{w.dB_part, so, so, R, out, 0, dB};
+    const int rc = launch(8, k_reduce<T>, dim3((unsigned)cdiv(si > so ? si : so, 256), 2), dim3(256), st, a);
+    if (rc) return rc;
+  }
+  return ok();
+}
+
 }  // namespace
 
 // =============================================================================
@@ -524,6 +639,11 @@ size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass) {
 size_t lora_qkv_workspace_bytes(const lora_qkv_desc_t* desc, int pass) {
   if (check_qkv(desc) != LORA_OK || (pass != 0 && pass != 1)) return 0;
   return qkv_ws(*desc, pass, nullptr).bytes;
+}
+
+size_t lora_linear_workspace_bytes(const lora_linear_desc_t* desc, int pass) {
+  if (check_linear(desc) != LORA_OK || (pass != 0 && pass != 1)) return 0;
+  return lin_ws(*desc, pass, nullptr).bytes;
 }
 
 int lora_mlp_fwd(const lora_mlp_desc_t* desc, const void* X, const lora_proj_t* gate, const lora_proj_t* up,
@@ -610,6 +730,35 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
   void* const dB[3] = {dB_q, dB_k, dB_v};
   if (desc->dtype == LORA_BF16) return qkv_bwd_impl<bf16>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
   return qkv_bwd_impl<float>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
+}
+
+int lora_linear_fwd(const lora_linear_desc_t* desc, const void* X, const lora_proj_t* proj, void* Y, void* T,
+                    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_linear(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(proj, "proj"))) return rc;
+  if (!X || !Y || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  (void)workspace;
+  (void)workspace_bytes;
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (desc->dtype == LORA_BF16) return linear_fwd_impl<bf16>(*desc, X, *proj, Y, T, st);
+  return linear_fwd_impl<float>(*desc, X, *proj, Y, T, st);
+}
+
+int lora_linear_bwd(const lora_linear_desc_t* desc, const void* dY, const void* X, const void* T,
+                    const lora_proj_t* proj, void* dX, void* dA, void* dB, void* workspace, size_t workspace_bytes,
+                    void* hip_stream) {
+  int rc = check_linear(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(proj, "proj"))) return rc;
+  if (!dY || !X || !T || !dX || !dA || !dB) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const LinWs probe = lin_ws(*desc, 1, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const LinWs w = lin_ws(*desc, 1, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  if (desc->dtype == LORA_BF16) return linear_bwd_impl<bf16>(*desc, dY, X, T, *proj, dX, dA, dB, w, st);
+  return linear_bwd_impl<float>(*desc, dY, X, T, *proj, dX, dA, dB, w, st);
 }
 
 const char* lora_status_string(int status) {

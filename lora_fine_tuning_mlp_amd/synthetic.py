@@ -42,6 +42,7 @@ QKV_IDS = {
     "W_v": 27, "A_v": 28, "B_v": 29,
     "dQ": 30, "dK": 31, "dV": 32,
 }
+LINEAR_IDS = {"X": 40, "W": 41, "A": 42, "B": 43, "dY": 44}
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -134,6 +135,36 @@ class QKVConfig:
         return 2 * N * h * O + 12 * N * h * r + 4 * N * r * O
 
 
+@dataclasses.dataclass(frozen=True)
+class LinearConfig:
+    """One LoRA linear workload: X [n_tokens, in_features] -> Y [n_tokens, out_features]."""
+    name: str
+    n_tokens: int
+    in_features: int
+    out_features: int
+    rank: int
+    scale: float
+    dtype: str
+    w_std: float = 0.02
+    b_std: float = 0.02
+    a_std: Optional[float] = None
+
+    def a_std_for(self, in_dim: int) -> float:
+        return self.a_std if self.a_std is not None else 1.0 / math.sqrt(in_dim)
+
+    def flops_fwd(self) -> int:
+        N, k, o, r = self.n_tokens, self.in_features, self.out_features, self.rank
+        return 2 * N * k * o + 2 * N * k * r + 2 * N * r * o
+
+    def flops_bwd(self) -> int:
+        """dX: 2Nok + 2Nrk; dT: 2Nor; dB: 2Nor; dA: 2Nrk."""
+        N, k, o, r = self.n_tokens, self.in_features, self.out_features, self.rank
+        return 2 * N * k * o + 4 * N * r * k + 4 * N * r * o
+
+    def flops(self) -> int:
+        return self.flops_fwd() + self.flops_bwd()
+
+
 # The benchmark workloads.  C0 takes "A ~ N(0, 1/64)" literally for all
 # three adapters (variance 1/64, std 1/8).
 C0 = MLPConfig("tiny_mlp_swiglu_f32", 2 * 16, 64, 172, 4, 2.0, "swiglu", "f32", a_std=1.0 / 8.0)
@@ -143,7 +174,10 @@ C3 = MLPConfig("mlp_geglu_tanh_h3072_i24576_bf16", 4 * 2048, 3072, 24576, 16, 2.
 C4_QKV = QKVConfig("qkv_rope_h896_gqa14x2_d64_bf16", 4, 1024, 896, 14, 2, 64, 16, 2.0, 1.0e6, "bf16")
 C4_MLP = MLPConfig("mlp_swiglu_h896_i4864_bf16", 4 * 1024, 896, 4864, 16, 2.0, "swiglu", "bf16")
 
-CONFIGS = {c.name: c for c in (C0, C1, C2, C3, C4_QKV, C4_MLP)}
+# The attention output projection of the 8B-class model (n_q * head_dim -> hidden).
+C_OPROJ = LinearConfig("oproj_h4096_bf16", 4 * 2048, 4096, 4096, 16, 2.0, "bf16")
+
+CONFIGS = {c.name: c for c in (C0, C1, C2, C3, C4_QKV, C4_MLP, C_OPROJ)}
 
 
 def mlp_inputs(cfg: MLPConfig, seed: int, with_grad: bool = True) -> Dict[str, torch.Tensor]:
@@ -176,6 +210,16 @@ def qkv_inputs(cfg: QKVConfig, seed: int, with_grad: bool = True) -> Dict[str, t
         shapes["dK"] = ((B, cfg.n_kv, S, d), 1.0)
         shapes["dV"] = ((B, cfg.n_kv, S, d), 1.0)
     return {k: normal(s, std, seed, QKV_IDS[k], dt) for k, (s, std) in shapes.items()}
+
+
+def linear_inputs(cfg: LinearConfig, seed: int, with_grad: bool = True) -> Dict[str, torch.Tensor]:
+    """LoRA linear tensors on the CPU: X [N,in], W [out,in], A [r,in], B [out,r], dY [N,out]."""
+    N, k, o, r, dt = cfg.n_tokens, cfg.in_features, cfg.out_features, cfg.rank, cfg.dtype
+    shapes = {"X": ((N, k), 1.0), "W": ((o, k), cfg.w_std), "A": ((r, k), cfg.a_std_for(k)),
+              "B": ((o, r), cfg.b_std)}
+    if with_grad:
+        shapes["dY"] = ((N, o), 1.0)
+    return {key: normal(s, std, seed, LINEAR_IDS[key], dt) for key, (s, std) in shapes.items()}
 
 
 def to_f64(t: Dict[str, torch.Tensor]) -> Dict[str, np.ndarray]:

@@ -57,6 +57,16 @@ QKV_CASES = [
 ]
 
 
+LINEAR_CASES = [
+    S.LinearConfig("linear_bf16_ragged", 600, 384, 640, 16, 2.0, "bf16"),
+    S.LinearConfig("linear_bf16_unaligned", 300, 196, 300, 5, 1.5, "bf16"),
+    S.LinearConfig("linear_bf16_long_k", 256, 1024, 512, 8, 2.0, "bf16"),
+    S.LinearConfig("linear_f32_mid", 520, 256, 384, 8, 2.0, "f32"),
+    S.LinearConfig("linear_f32_ragged", 100, 72, 150, 3, 0.5, "f32"),
+    S.LinearConfig("linear_bf16_tiny", 7, 8, 16, 1, 2.0, "bf16"),
+]
+
+
 def mlp_scales(cfg):
     return (cfg.scale, cfg.scale, cfg.scale)
 
@@ -125,6 +135,30 @@ def run_qkv_oracle(cfg: S.QKVConfig, t_cpu, grads_cpu=None, scales=None):
         ref["dA_" + n] = g["dA_" + n]
         ref["dB_" + n] = g["dB_" + n]
     return ref
+
+
+def run_linear_gpu(cfg: S.LinearConfig, t_cpu, dY_cpu=None):
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev).contiguous() for k, v in t_cpu.items() if k != "dY"}
+    m = B.Linear(t, cfg.n_tokens, cfg.in_features, cfg.out_features, cfg.rank, cfg.dtype, cfg.scale)
+    m.forward()
+    dY = (dY_cpu if dY_cpu is not None else t_cpu["dY"]).to(dev).contiguous()
+    m.backward(dY)
+    torch.cuda.synchronize()
+    out = {"Y": to64(m.Y), "T": to64(m.T), "dX": to64(m.dX)}
+    out.update({k: to64(v) for k, v in m.grads.items()})
+    return out
+
+
+def run_linear_oracle(cfg: S.LinearConfig, t_cpu, dY_cpu=None, rows=None):
+    p = S.to_f64({k: v for k, v in t_cpu.items() if k != "dY"})
+    dY = (dY_cpu if dY_cpu is not None else t_cpu["dY"]).to(torch.float64).numpy()
+    X = p["X"]
+    if rows is not None:
+        X, dY = X[rows], dY[rows]
+    Y, T = orc.lora_linear(X, p["W"], p["A"], p["B"], cfg.scale)
+    dX, dA, dB, _ = orc.lora_linear_bwd(dY, X, T, p["W"], p["A"], p["B"], cfg.scale)
+    return {"Y": Y, "T": T, "dX": dX, "dA": dA, "dB": dB}
 
 
 def compare(name: str, gpu, ref, tol: float, keys=None):

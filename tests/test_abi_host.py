@@ -24,8 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
-    for n in ("lora_mlp_fwd", "lora_mlp_bwd", "lora_qkv_fwd", "lora_qkv_bwd",
-              "lora_mlp_workspace_bytes", "lora_qkv_workspace_bytes", "lora_status_string"):
+    for n in ("lora_mlp_fwd", "lora_mlp_bwd", "lora_qkv_fwd", "lora_qkv_bwd", "lora_linear_fwd", "lora_linear_bwd",
+              "lora_mlp_workspace_bytes", "lora_qkv_workspace_bytes", "lora_linear_workspace_bytes",
+              "lora_status_string"):
         assert n in names
 
 
@@ -114,7 +115,45 @@ def test_qkv_validation_codes():
     assert _call_qkv_bwd(_qkv(), need - 256) == 4
 
 
+def _lin(**kw):
+    d = dict(n_tokens=64, in_features=128, out_features=96, rank=8, dtype="bf16")
+    d.update(kw)
+    return B.linear_desc(**d)
+
+
+def test_linear_workspace_queries():
+    assert B.lora_linear_workspace_bytes(_lin(), 0) == 0          # the forward needs none
+    need = B.lora_linear_workspace_bytes(_lin(), 1)
+    # at least the per-row-block dA partials [ceil(N/256)][in][16] and dB partials in float32
+    assert need >= (128 + 96) * 16 * 4
+    assert B.lora_linear_workspace_bytes(_lin(rank=0), 1) == 0
+    assert B.lora_linear_workspace_bytes(_lin(), 3) == 0
+
+
+def _call_linear_bwd(desc, ws_bytes, ws=FAKE):
+    lib = B.lib()
+    pr = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0)
+    f = FAKE
+    return lib.lora_linear_bwd(ctypes.byref(desc) if desc is not None else None, f, f, f, ctypes.byref(pr), f, f, f,
+                               ws, ws_bytes, None)
+
+
+def test_linear_validation_codes():
+    lib = B.lib()
+    assert _call_linear_bwd(None, 1 << 40) == 1
+    assert _call_linear_bwd(_lin(out_features=0), 1 << 40) == 2
+    assert _call_linear_bwd(_lin(rank=B.LORA_MAX_RANK + 1), 1 << 40) == 3
+    bad = _lin()
+    bad.dtype = 9
+    assert _call_linear_bwd(bad, 1 << 40) == 3
+    need = B.lora_linear_workspace_bytes(_lin(), 1)
+    assert _call_linear_bwd(_lin(), need - 1) == 4
+    assert _call_linear_bwd(_lin(), need, ws=None) == 4
+    pr = B.Proj(None, FAKE.value, FAKE.value, 2.0)
+    assert lib.lora_linear_fwd(ctypes.byref(_lin()), FAKE, ctypes.byref(pr), FAKE, FAKE, None, 0, None) == 1
+
+
 def test_kernel_names_listed():
     names = B.kernel_names()
-    for k in ("k_gateup_fwd", "k_linear_fwd", "k_qkv_fwd", "k_down_bwd", "k_mlp_dx_bwd", "k_qkv_dx_bwd"):
+    for k in ("k_gateup_fwd", "k_linear_fwd", "k_qkv_fwd", "k_down_bwd", "k_mlp_dx_bwd", "k_proj_dx_bwd"):
         assert k in names

@@ -109,3 +109,22 @@ def test_qkv_c4_full():
     t = S.qkv_inputs(cfg, 0)
     gc.say("full-size qkv C4: GPU + full oracle")
     gc.compare(cfg.name, gc.run_qkv_gpu(cfg, t), gc.run_qkv_oracle(cfg, t), gc.TOL[cfg.dtype])
+
+
+def test_oproj_full_size():
+    cfg = S.C_OPROJ
+    gc.say(f"full-size linear {cfg.name}: generating inputs")
+    t = S.linear_inputs(cfg, 0)
+    rows = sample_rows(cfg.n_tokens, 12)
+    mask = torch.zeros(cfg.n_tokens, 1, dtype=t["dY"].dtype)
+    mask[torch.from_numpy(rows)] = 1
+    dY = t["dY"] * mask
+    gc.say(f"full-size linear {cfg.name}: GPU")
+    out = gc.run_linear_gpu(cfg, t, dY_cpu=dY)
+    gc.say(f"full-size linear {cfg.name}: oracle on {len(rows)} rows")
+    ref = gc.run_linear_oracle(cfg, t, dY_cpu=dY, rows=rows)
+    sampled = {k: out[k][rows] for k in ("Y", "T", "dX")}
+    sampled.update({k: out[k] for k in ("dA", "dB")})
+    gc.compare(f"{cfg.name}/sampled", sampled, ref, gc.TOL[cfg.dtype])
+    others = np.setdiff1d(np.arange(cfg.n_tokens), rows)
+    assert not np.any(out["dX"][others]), "dX non-zero where dY is zero"
