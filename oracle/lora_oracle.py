@@ -16,7 +16,8 @@ Sources (the pages' titles and sections):
     single LoRA linear ``x @ W.T + x @ A @ B * s`` (opake_lora_w), the fused
     Q+K+V call sharing one input (opake_lora_qkv) and the fused gate+up+down
     call with the activation (opake_lora_mlp); fusion only without active
-    LoRA dropout and, for the MLP, without bias.
+    LoRA dropout and, for the MLP, without bias.  The fused QKV call may
+    carry frozen biases of the base projections (no gradient).
   * Same page, section "Activation functions": SwiGLU ``silu(gate) * up``,
     GeGLU approx ``gelu_tanh(gate) * up``, GeGLU exact (erf).
   * Same page, section "Rotary position embeddings (RoPE)": RoPE on Q and K
@@ -40,7 +41,7 @@ design notes):
 from __future__ import annotations
 
 import math
-from typing import Dict
+from typing import Dict, Optional
 
 import numpy as np
 
@@ -117,10 +118,17 @@ def activation(name: str):
 # LoRA linear (Opake "Model Patches and Kernels", "Fused LoRA operations")
 # ---------------------------------------------------------------------------
 
-def lora_linear(Z: np.ndarray, W: np.ndarray, A: np.ndarray, B: np.ndarray, s: float):
-    """Y = Z W^T + s (Z A^T) B^T; returns (Y, T) with T = Z A^T."""
+def lora_linear(Z: np.ndarray, W: np.ndarray, A: np.ndarray, B: np.ndarray, s: float,
+                bias: Optional[np.ndarray] = None):
+    """Y = Z W^T + b + s (Z A^T) B^T; returns (Y, T) with T = Z A^T.
+
+    b is the base layer's frozen bias (absent: zero).  It only shifts Y, so
+    lora_linear_bwd is the same with or without it.
+    """
     T = Z @ A.T
     Y = Z @ W.T + s * (T @ B.T)
+    if bias is not None:
+        Y = Y + bias[None, :]
     return Y, T
 
 
@@ -231,13 +239,17 @@ _QKV = ("q", "k", "v")
 def qkv_fwd(p: Dict[str, np.ndarray], batch: int, seq: int, n_q: int, n_kv: int,
             head_dim: int, theta: float, scales) -> Dict[str, np.ndarray]:
     """Q, K, V [B, heads, S, d] from X [B*S, h]: LoRA linear per projection,
-    head split, RoPE on Q and K (not V).  Also returns T_q, T_k, T_v."""
+    head split, RoPE on Q and K (not V).  Also returns T_q, T_k, T_v.
+
+    Optional frozen biases b_q, b_k, b_v ([out]) are part of the base
+    projection, so they are added before the rotation.  qkv_bwd does not read
+    them: a frozen bias has no gradient and does not change the others."""
     X = p["X"]
     heads = {"q": n_q, "k": n_kv, "v": n_kv}
     ang = rope_angles(seq, head_dim, theta)
     out = {}
     for name, s in zip(_QKV, scales):
-        P, T = lora_linear(X, p["W_" + name], p["A_" + name], p["B_" + name], s)
+        P, T = lora_linear(X, p["W_" + name], p["A_" + name], p["B_" + name], s, p.get("b_" + name))
         Z = head_split(P, batch, seq, heads[name], head_dim)
         if name != "v":
             Z = rope_rotate(Z, ang)

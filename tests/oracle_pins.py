@@ -131,6 +131,27 @@ def check_lora_linear_vs_autograd(orc):
     assert _rel(dB, tB.grad.numpy()) < 1e-12
 
 
+def check_lora_linear_bias_vs_torch(orc):
+    """Frozen base bias: Y against torch F.linear(Z, W, b) plus the adapter;
+    gradients against autograd with b a constant (they do not depend on b)."""
+    g = _rng(3)
+    N, i, o, r, s = 5, 6, 4, 2, 1.25
+    Z, W = g.standard_normal((N, i)), g.standard_normal((o, i))
+    A, B = g.standard_normal((r, i)), g.standard_normal((o, r))
+    b, dY = g.standard_normal(o) * 3.0, g.standard_normal((N, o))
+    tZ, tA, tB = (torch.tensor(v, requires_grad=True) for v in (Z, A, B))
+    Yt = F.linear(tZ, torch.tensor(W), torch.tensor(b)) + s * F.linear(F.linear(tZ, tA), tB)
+    Yt.backward(torch.tensor(dY))
+    Y, T = orc.lora_linear(Z, W, A, B, s, b)
+    assert _rel(Y, Yt.detach().numpy()) < 1e-12
+    Y0, _ = orc.lora_linear(Z, W, A, B, s)
+    assert _rel(Y - Y0, np.broadcast_to(b, Y.shape)) < 1e-12
+    dZ, dA, dB, _ = orc.lora_linear_bwd(dY, Z, T, W, A, B, s)
+    assert _rel(dZ, tZ.grad.numpy()) < 1e-12
+    assert _rel(dA, tA.grad.numpy()) < 1e-12
+    assert _rel(dB, tB.grad.numpy()) < 1e-12
+
+
 # ---------------------------------------------------------------------------
 # Activations
 # ---------------------------------------------------------------------------
@@ -370,7 +391,8 @@ def _torch_qkv(tp, shape, scales):
     rot = torch.polar(torch.ones_like(ang), ang)
     out = {}
     for name, heads, s in zip("qkv", (nq, nkv, nkv), scales):
-        P = F.linear(tp["X"], tp["W_" + name]) + s * F.linear(F.linear(tp["X"], tp["A_" + name]), tp["B_" + name])
+        P = F.linear(tp["X"], tp["W_" + name], tp.get("b_" + name)) + \
+            s * F.linear(F.linear(tp["X"], tp["A_" + name]), tp["B_" + name])
         Z = P.reshape(B, S, heads, d).permute(0, 2, 1, 3)
         if name != "v":
             c = torch.complex(Z[..., : d // 2], Z[..., d // 2:]) * rot
@@ -404,6 +426,37 @@ def check_qkv_vs_autograd(orc):
     for n in "qkv":
         assert _rel(g["dA_" + n], tp["A_" + n].grad.numpy()) < 1e-12, n
         assert _rel(g["dB_" + n], tp["B_" + n].grad.numpy()) < 1e-12, n
+
+
+def check_qkv_bias_vs_autograd(orc):
+    """Frozen q/k/v biases go in before RoPE (torch's F.linear bias, then the
+    complex rotation); the backward, which ignores them, still matches
+    autograd through the biased forward."""
+    p, gr = tiny_qkv(19, batch=2, seq=4, h=6, n_q=4, n_kv=2, d=6, r=2)
+    shape = dict(batch=2, seq=4, n_q=4, n_kv=2, head_dim=6, theta=30.0)
+    g = _rng(20)
+    for n, o in (("q", 24), ("k", 12), ("v", 12)):
+        p["b_" + n] = g.standard_normal(o) * 2.0
+    tp = {k: torch.tensor(v, requires_grad=(k[0] in "XAB")) for k, v in p.items()}
+    ref = _torch_qkv(tp, shape, QKV_SCALES)
+    loss = sum((ref[k] * torch.tensor(gr["d" + k])).sum() for k in "QKV")
+    loss.backward()
+    o = orc.qkv_fwd(p, scales=QKV_SCALES, **shape)
+    for k in "QKV":
+        assert _rel(o[k], ref[k].detach().numpy()) < 1e-12, k
+    # V has no rotation: its bias shifts every position by the same vector.
+    nob = {k: v for k, v in p.items() if not k.startswith("b_")}
+    o0 = orc.qkv_fwd(nob, scales=QKV_SCALES, **shape)
+    bv = p["b_v"].reshape(2, 6)[None, :, None, :]
+    assert _rel(o["V"] - o0["V"], np.broadcast_to(bv, o["V"].shape)) < 1e-12
+    # Q at position 0 is unrotated: its bias shows up unchanged there.
+    bq = p["b_q"].reshape(4, 6)[None, :, :]
+    assert _rel(o["Q"][:, :, 0] - o0["Q"][:, :, 0], np.broadcast_to(bq, o["Q"][:, :, 0].shape)) < 1e-12
+    gq = orc.qkv_bwd(p, gr["dQ"], gr["dK"], gr["dV"], scales=QKV_SCALES, **shape)
+    assert _rel(gq["dX"], tp["X"].grad.numpy()) < 1e-12
+    for n in "qkv":
+        assert _rel(gq["dA_" + n], tp["A_" + n].grad.numpy()) < 1e-12, n
+        assert _rel(gq["dB_" + n], tp["B_" + n].grad.numpy()) < 1e-12, n
 
 
 def check_qkv_finite_differences(orc):

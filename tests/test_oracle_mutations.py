@@ -33,6 +33,17 @@ MUTATIONS = [
     ("head split order", ".transpose(0, 2, 1, 3).copy()\n\n\ndef head_unsplit", ".transpose(0, 2, 1, 3)[:, ::-1].copy()\n\n\ndef head_unsplit"),
     ("rope on V", "if name != \"v\":\n            Z = rope_rotate", "if True:\n            Z = rope_rotate"),
     ("no RoPE adjoint in backward", "grads = {\"q\": rope_rotate_transpose(dQ, ang)", "grads = {\"q\": dQ"),
+    ("gelu_erf' drops density", " + g * np.exp(-0.5 * g * g) / math.sqrt(2.0 * math.pi)", ""),
+    ("gelu_erf without 1/sqrt2", "_erf(g / math.sqrt(2.0)))\n\n\ndef gelu_erf_grad", "_erf(g))\n\n\ndef gelu_erf_grad"),
+    ("bias dropped", "Y = Y + bias[None, :]", "Y = Y"),
+    ("bias scaled with adapter", "Y = Y + bias[None, :]", "Y = Y + s * bias[None, :]"),
+    ("qkv bias after RoPE",
+     "p[\"B_\" + name], s, p.get(\"b_\" + name))\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n"
+     "        if name != \"v\":\n            Z = rope_rotate(Z, ang)\n",
+     "p[\"B_\" + name], s)\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n"
+     "        if name != \"v\":\n            Z = rope_rotate(Z, ang)\n"
+     "        if p.get(\"b_\" + name) is not None:\n"
+     "            Z = Z + head_split(np.broadcast_to(p[\"b_\" + name], P.shape), batch, seq, heads[name], head_dim)\n"),
 ]
 
 
