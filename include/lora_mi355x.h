@@ -7,8 +7,9 @@
  *     Q+K+V call sharing one input (opake_lora_qkv) and the fused
  *     gate+up+down call with the activation (opake_lora_mlp). Fusion applies
  *     only without active LoRA dropout and, for the MLP, without bias.
- *   - Same page, "Activation functions": SwiGLU silu(gate)*up and GeGLU with
- *     the tanh approximation gelu_tanh(gate)*up; the backward of the
+ *   - Same page, "Activation functions": SwiGLU silu(gate)*up, GeGLU with
+ *     the tanh approximation gelu_tanh(gate)*up and the exact (erf) GeGLU
+ *     gelu(gate)*up; the backward of the
  *     activation reads the upstream gradient, gate and up and writes the two
  *     input gradients in one pass.
  *   - Same page, "Rotary position embeddings (RoPE)": RoPE applied to Q and K
@@ -72,16 +73,24 @@ extern "C" {
 
 #define LORA_SWIGLU 0            /* silu(gate) * up */
 #define LORA_GEGLU_TANH 1        /* gelu_tanh(gate) * up */
+#define LORA_GEGLU_ERF 2         /* gelu(gate) * up, exact GELU g * Phi(g) with the error function */
 
 #define LORA_MAX_RANK 16         /* largest adapter rank the kernels are built for */
 
 /* One adapted projection: frozen base W [out, in], adapter A [r, in],
- * B [out, r] (same dtype as the call), scale s (alpha / r). */
+ * B [out, r] (same dtype as the call), scale s (alpha / r), and an optional
+ * frozen base-layer bias [out] (same dtype; NULL for none).  The bias is
+ * added in the forward only and gets no gradient.  The QKV and single-linear
+ * calls accept it (Opake, "Model Patches and Kernels", "Fused LoRA
+ * operations": the fused QKV call allows frozen base biases); the MLP call
+ * requires NULL (its fusion is for bias-free projections) and returns
+ * LORA_ERR_UNSUPPORTED otherwise. */
 typedef struct {
   const void* W;
   const void* A;
   const void* B;
   float scale;
+  const void* bias;
 } lora_proj_t;
 
 /* LoRA MLP: gate/up [hidden -> inter], GLU, down [inter -> hidden]. */
@@ -91,7 +100,7 @@ typedef struct {
   int32_t inter;      /* i */
   int32_t rank;       /* r, 1..LORA_MAX_RANK */
   int32_t dtype;      /* LORA_F32 | LORA_BF16 */
-  int32_t act;        /* LORA_SWIGLU | LORA_GEGLU_TANH */
+  int32_t act;        /* LORA_SWIGLU | LORA_GEGLU_TANH | LORA_GEGLU_ERF */
   int32_t reserved;   /* must be 0 */
 } lora_mlp_desc_t;
 

@@ -17,10 +17,10 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "liblora_mi355x.so")
 
 LORA_F32, LORA_BF16 = 0, 1
-LORA_SWIGLU, LORA_GEGLU_TANH = 0, 1
+LORA_SWIGLU, LORA_GEGLU_TANH, LORA_GEGLU_ERF = 0, 1, 2
 LORA_MAX_RANK = 16
 DTYPE_CODES = {"f32": LORA_F32, "bf16": LORA_BF16, torch.float32: LORA_F32, torch.bfloat16: LORA_BF16}
-ACT_CODES = {"swiglu": LORA_SWIGLU, "geglu_tanh": LORA_GEGLU_TANH}
+ACT_CODES = {"swiglu": LORA_SWIGLU, "geglu_tanh": LORA_GEGLU_TANH, "geglu_erf": LORA_GEGLU_ERF}
 
 
 class LoraError(RuntimeError):
@@ -47,7 +47,8 @@ class LinearDesc(ctypes.Structure):
 
 
 class Proj(ctypes.Structure):
-    _fields_ = [("W", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("scale", ctypes.c_float)]
+    _fields_ = [("W", ctypes.c_void_p), ("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("scale", ctypes.c_float),
+                ("bias", ctypes.c_void_p)]
 
 
 _P = ctypes.c_void_p
@@ -116,8 +117,9 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream
 
 
-def proj(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, scale: float) -> Proj:
-    return Proj(_ptr(W), _ptr(A), _ptr(B), float(scale))
+def proj(W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, scale: float,
+         bias: Optional[torch.Tensor] = None) -> Proj:
+    return Proj(_ptr(W), _ptr(A), _ptr(B), float(scale), _ptr(bias))
 
 
 def mlp_desc(n_tokens, hidden, inter, rank, dtype, act) -> MlpDesc:
@@ -249,7 +251,8 @@ class MLP:
 
 
 class QKV:
-    """LoRA QKV weights on the device plus the buffers one fwd+bwd needs."""
+    """LoRA QKV weights on the device plus the buffers one fwd+bwd needs
+    (optional frozen biases under the keys b_q, b_k, b_v)."""
 
     def __init__(self, t: Dict[str, torch.Tensor], batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta,
                  scales=(2.0, 2.0, 2.0)):
@@ -260,9 +263,9 @@ class QKV:
         self.B, self.S, self.h, self.r, self.d = int(batch), int(seq), int(hidden), int(rank), int(head_dim)
         self.nq, self.nkv = int(n_q), int(n_kv)
         N = self.B * self.S
-        self.q = proj(t["W_q"], t["A_q"], t["B_q"], scales[0])
-        self.k = proj(t["W_k"], t["A_k"], t["B_k"], scales[1])
-        self.v = proj(t["W_v"], t["A_v"], t["B_v"], scales[2])
+        self.q = proj(t["W_q"], t["A_q"], t["B_q"], scales[0], t.get("b_q"))
+        self.k = proj(t["W_k"], t["A_k"], t["B_k"], scales[1], t.get("b_k"))
+        self.v = proj(t["W_v"], t["A_v"], t["B_v"], scales[2], t.get("b_v"))
         e = dict(device=dev, dtype=self.dtype)
         self.Q = torch.empty(self.B, self.nq, self.S, self.d, **e)
         self.K = torch.empty(self.B, self.nkv, self.S, self.d, **e)
@@ -291,7 +294,8 @@ class QKV:
 
 
 class Linear:
-    """One LoRA linear's weights on the device plus the buffers one fwd+bwd needs."""
+    """One LoRA linear's weights on the device plus the buffers one fwd+bwd needs
+    (optional frozen bias under the key "bias")."""
 
     def __init__(self, t: Dict[str, torch.Tensor], n_tokens, in_features, out_features, rank, dtype, scale=2.0):
         self.t = t
@@ -299,7 +303,7 @@ class Linear:
         self.dtype = t["X"].dtype
         dev = t["X"].device
         self.N, self.k, self.o, self.r = int(n_tokens), int(in_features), int(out_features), int(rank)
-        self.p = proj(t["W"], t["A"], t["B"], scale)
+        self.p = proj(t["W"], t["A"], t["B"], scale, t.get("bias"))
         e = dict(device=dev, dtype=self.dtype)
         self.Y = torch.empty(self.N, self.o, **e)
         self.T = torch.empty(self.N, self.r, device=dev, dtype=torch.float32)

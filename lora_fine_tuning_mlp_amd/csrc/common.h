@@ -209,15 +209,18 @@ __device__ __forceinline__ int perm_row(int lg, int w) {
 // ---- activations (fp32) --------------------------------------------------------
 #define LORA_ACT_SWIGLU 0
 #define LORA_ACT_GEGLU_TANH 1
+#define LORA_ACT_GEGLU_ERF 2
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
 template <int ACT> __device__ __forceinline__ float act_fwd(float g) {
   if constexpr (ACT == LORA_ACT_SWIGLU) {
     return g * sigmoidf_(g);
-  } else {
+  } else if constexpr (ACT == LORA_ACT_GEGLU_TANH) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;   // sqrt(2/pi), cubic coefficient
     return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+  } else {
+    return 0.5f * g * (1.0f + erff(g * 0.7071067811865476f));   // exact GELU: g * Phi(g)
   }
 }
 // phi(g) and phi'(g) together.
@@ -226,11 +229,16 @@ template <int ACT> __device__ __forceinline__ void act_both(float g, float& phi,
     const float s = sigmoidf_(g);
     phi = g * s;
     dphi = s * (1.0f + g * (1.0f - s));
-  } else {
+  } else if constexpr (ACT == LORA_ACT_GEGLU_TANH) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;
     const float t = tanhf(k0 * (g + k1 * g * g * g));
     phi = 0.5f * g * (1.0f + t);
     dphi = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * k0 * (1.0f + 3.0f * k1 * g * g);
+  } else {
+    // Phi(g) = (1 + erf(g / sqrt 2)) / 2; phi'(g) = Phi(g) + g * exp(-g^2/2) / sqrt(2 pi).
+    const float cdf = 0.5f * (1.0f + erff(g * 0.7071067811865476f));
+    phi = g * cdf;
+    dphi = cdf + g * 0.3989422804014327f * expf(-0.5f * g * g);
   }
 }
 

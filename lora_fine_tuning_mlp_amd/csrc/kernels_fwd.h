@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
 // ===========================================================================
 struct LinearArgs {
   const void* Z; const void* W; const void* A; const void* B;
+  const void* bias;    // frozen base bias [O] or nullptr
   float s;
   void* Y; float* T;
   long N; int K, O, r;
@@ -220,6 +221,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   T* Y = static_cast<T*>(a.Y);
   const long c0 = n0 + q.wn * 128 + 8 * q.r16;
   const int nvalid = (int)min(8L, a.O - c0);
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (a.bias) {
+    const T* bp = static_cast<const T*>(a.bias) + c0;
+    for (int nb = 0; nb < nvalid; ++nb) bv[nb] = to_f<T>(bp[nb]);
+  }
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
       if (row >= a.N || nvalid <= 0) continue;
       float v[8];
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j];
+      for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j] + bv[nb];
       store_row8<T>(Y + row * a.O + c0, v, nvalid, a.vecO);
     }
 }
@@ -252,6 +258,7 @@ __global__ void k_rope_table(float* cs, float* sn, int S, int half, double theta
 struct QKVFwdArgs {
   const void* X;
   const void* W[3]; const void* A[3]; const void* B[3];
+  const void* bias[3]; // frozen base biases [O_p] or nullptr, added before RoPE
   float s[3];
   void* out[3];        // Q, K, V
   float* T[3];
@@ -377,6 +384,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       v[0] = t.x; v[1] = t.y;
     }
   };
+  // Bias of the lane's columns (the same for every row): pair halves x1, x2.
+  float b1v[NG][cw], b2v[NG][cw];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+    const T* bp = nullptr;
+    int oo = 0;
+    if (o1 < O) {
+      const int p = proj_of(o1);
+      bp = static_cast<const T*>(p == 0 ? a.bias[0] : (p == 1 ? a.bias[1] : a.bias[2]));
+      oo = o1 - a.off[p];
+    }
+#pragma unroll
+    for (int e = 0; e < cw; ++e) {
+      b1v[gi][e] = bp ? to_f<T>(bp[oo + e]) : 0.f;
+      b2v[gi][e] = bp ? to_f<T>(bp[oo + half + e]) : 0.f;
+    }
+  }
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
     float cc[4][NG][cw], ss[4][NG][cw];
@@ -414,8 +439,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
         float y1[cw], y2[cw];
 #pragma unroll
         for (int e = 0; e < cw; ++e) {
-          const float x1 = acc[mb][b1 + e][j];
-          const float x2 = acc[mb][b1 + cw + e][j];
+          const float x1 = acc[mb][b1 + e][j] + b1v[gi][e];
+          const float x2 = acc[mb][b1 + cw + e][j] + b2v[gi][e];
           if (p < 2) {
             y1[e] = x1 * cc[j][gi][e] - x2 * ss[j][gi][e];
             y2[e] = x2 * cc[j][gi][e] + x1 * ss[j][gi][e];

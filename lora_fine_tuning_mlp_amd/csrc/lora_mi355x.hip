@@ -231,7 +231,7 @@ int check_mlp(const lora_mlp_desc_t* d) {
                 (long long)d->n_tokens, d->hidden, d->inter, d->rank);
   if (d->reserved != 0) return fail(LORA_ERR_SHAPE, "reserved field must be 0");
   if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
-  if (d->act != LORA_SWIGLU && d->act != LORA_GEGLU_TANH)
+  if (d->act != LORA_SWIGLU && d->act != LORA_GEGLU_TANH && d->act != LORA_GEGLU_ERF)
     return fail(LORA_ERR_UNSUPPORTED, "unsupported activation %d", d->act);
   if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
   if (d->n_tokens > (1L << 30) || (long)d->hidden * d->inter > (1L << 31))
@@ -240,6 +240,12 @@ int check_mlp(const lora_mlp_desc_t* d) {
 }
 int check_proj(const lora_proj_t* p, const char* name) {
   if (!p || !p->W || !p->A || !p->B) return fail(LORA_ERR_NULL, "projection %s has a NULL pointer", name);
+  return LORA_OK;
+}
+int check_proj_nobias(const lora_proj_t* p, const char* name) {
+  const int rc = check_proj(p, name);
+  if (rc) return rc;
+  if (p->bias) return fail(LORA_ERR_UNSUPPORTED, "projection %s has a bias; the fused MLP is bias-free", name);
   return LORA_OK;
 }
 int check_qkv(const lora_qkv_desc_t* d) {
@@ -428,7 +434,7 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
   a.X = X;
   bool wal = true, aal = true, oal = true;
   for (int p = 0; p < 3; ++p) {
-    a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.B[p] = pr[p]->B; a.s[p] = pr[p]->scale;
+    a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.B[p] = pr[p]->B; a.s[p] = pr[p]->scale; a.bias[p] = pr[p]->bias;
     a.out[p] = out[p];
     a.T[p] = static_cast<float*>(Tsv) + p * N * r;
     wal = wal && al16(pr[p]->W);
@@ -553,7 +559,7 @@ int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_
   const long N = d.n_tokens;
   const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
   LinearArgs a{};
-  a.Z = X; a.W = p.W; a.A = p.A; a.B = p.B; a.s = p.scale;
+  a.Z = X; a.W = p.W; a.A = p.A; a.B = p.B; a.bias = p.bias; a.s = p.scale;
   a.Y = Y; a.T = static_cast<float*>(Tsv);
   a.N = N; a.K = in; a.O = out; a.r = r;
   a.vecA = (in % V == 0) && al16(X);
@@ -651,19 +657,25 @@ int lora_mlp_fwd(const lora_mlp_desc_t* desc, const void* X, const lora_proj_t* 
                  size_t workspace_bytes, void* hip_stream) {
   int rc = check_mlp(desc);
   if (rc) return rc;
-  if ((rc = check_proj(gate, "gate")) || (rc = check_proj(up, "up")) || (rc = check_proj(down, "down"))) return rc;
+  if ((rc = check_proj_nobias(gate, "gate")) || (rc = check_proj_nobias(up, "up")) ||
+      (rc = check_proj_nobias(down, "down")))
+    return rc;
   if (!X || !Y || !G || !U || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const MlpWs probe = mlp_ws(*desc, 0, nullptr);
   if (!workspace || workspace_bytes < probe.bytes)
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const MlpWs w = mlp_ws(*desc, 0, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
+#define LORA_MLP_FWD(TT, AA) return mlp_fwd_impl<TT, AA>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st)
   if (desc->dtype == LORA_BF16) {
-    if (desc->act == LORA_SWIGLU) return mlp_fwd_impl<bf16, 0>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
-    return mlp_fwd_impl<bf16, 1>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+    if (desc->act == LORA_SWIGLU) LORA_MLP_FWD(bf16, LORA_ACT_SWIGLU);
+    if (desc->act == LORA_GEGLU_TANH) LORA_MLP_FWD(bf16, LORA_ACT_GEGLU_TANH);
+    LORA_MLP_FWD(bf16, LORA_ACT_GEGLU_ERF);
   }
-  if (desc->act == LORA_SWIGLU) return mlp_fwd_impl<float, 0>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
-  return mlp_fwd_impl<float, 1>(*desc, X, *gate, *up, *down, Y, G, U, T, w, st);
+  if (desc->act == LORA_SWIGLU) LORA_MLP_FWD(float, LORA_ACT_SWIGLU);
+  if (desc->act == LORA_GEGLU_TANH) LORA_MLP_FWD(float, LORA_ACT_GEGLU_TANH);
+  LORA_MLP_FWD(float, LORA_ACT_GEGLU_ERF);
+#undef LORA_MLP_FWD
 }
 
 int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X, const void* G, const void* U,
@@ -672,7 +684,9 @@ int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X, con
                  void* workspace, size_t workspace_bytes, void* hip_stream) {
   int rc = check_mlp(desc);
   if (rc) return rc;
-  if ((rc = check_proj(gate, "gate")) || (rc = check_proj(up, "up")) || (rc = check_proj(down, "down"))) return rc;
+  if ((rc = check_proj_nobias(gate, "gate")) || (rc = check_proj_nobias(up, "up")) ||
+      (rc = check_proj_nobias(down, "down")))
+    return rc;
   if (!dY || !X || !G || !U || !T || !dX || !dA_gate || !dB_gate || !dA_up || !dB_up || !dA_down || !dB_down)
     return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const MlpWs probe = mlp_ws(*desc, 1, nullptr);
@@ -684,11 +698,13 @@ int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X, con
   return mlp_bwd_impl<TT, AA>(*desc, dY, X, G, U, T, *gate, *up, *down, dX, dA_gate, dB_gate, dA_up, dB_up, \
                               dA_down, dB_down, w, st)
   if (desc->dtype == LORA_BF16) {
-    if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(bf16, 0);
-    LORA_MLP_BWD(bf16, 1);
+    if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(bf16, LORA_ACT_SWIGLU);
+    if (desc->act == LORA_GEGLU_TANH) LORA_MLP_BWD(bf16, LORA_ACT_GEGLU_TANH);
+    LORA_MLP_BWD(bf16, LORA_ACT_GEGLU_ERF);
   }
-  if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(float, 0);
-  LORA_MLP_BWD(float, 1);
+  if (desc->act == LORA_SWIGLU) LORA_MLP_BWD(float, LORA_ACT_SWIGLU);
+  if (desc->act == LORA_GEGLU_TANH) LORA_MLP_BWD(float, LORA_ACT_GEGLU_TANH);
+  LORA_MLP_BWD(float, LORA_ACT_GEGLU_ERF);
 #undef LORA_MLP_BWD
 }
 

@@ -15,7 +15,7 @@ to float64, so both sides see bit-identical inputs.
 Distributions follow the benchmark configurations: activations and upstream
 gradients ~N(0,1), frozen base weights std 0.02, LoRA A with variance
 1/in_dim (std in_dim**-0.5), LoRA B std 0.02 (non-zero, so the adapter path is
-visible in every output and gradient).
+visible in every output and gradient), optional frozen base biases std 0.5.
 """
 from __future__ import annotations
 
@@ -41,8 +41,9 @@ QKV_IDS = {
     "W_k": 24, "A_k": 25, "B_k": 26,
     "W_v": 27, "A_v": 28, "B_v": 29,
     "dQ": 30, "dK": 31, "dV": 32,
+    "b_q": 33, "b_k": 34, "b_v": 35,
 }
-LINEAR_IDS = {"X": 40, "W": 41, "A": 42, "B": 43, "dY": 44}
+LINEAR_IDS = {"X": 40, "W": 41, "A": 42, "B": 43, "dY": 44, "bias": 45}
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -66,7 +67,7 @@ class MLPConfig:
     inter: int
     rank: int
     scale: float
-    act: str            # "swiglu" | "geglu_tanh"
+    act: str            # "swiglu" | "geglu_tanh" | "geglu_erf"
     dtype: str          # "f32" | "bf16"
     w_std: float = 0.02
     b_std: float = 0.02
@@ -107,6 +108,8 @@ class QKVConfig:
     w_std: float = 0.02
     b_std: float = 0.02
     a_std: Optional[float] = None
+    bias: bool = False     # frozen base biases b_q, b_k, b_v (std bias_std)
+    bias_std: float = 0.5
 
     @property
     def n_tokens(self) -> int:
@@ -148,6 +151,8 @@ class LinearConfig:
     w_std: float = 0.02
     b_std: float = 0.02
     a_std: Optional[float] = None
+    bias: bool = False     # frozen base bias (std bias_std)
+    bias_std: float = 0.5
 
     def a_std_for(self, in_dim: int) -> float:
         return self.a_std if self.a_std is not None else 1.0 / math.sqrt(in_dim)
@@ -204,6 +209,8 @@ def qkv_inputs(cfg: QKVConfig, seed: int, with_grad: bool = True) -> Dict[str, t
         "W_k": ((Ok, h), cfg.w_std), "A_k": ((r, h), cfg.a_std_for(h)), "B_k": ((Ok, r), cfg.b_std),
         "W_v": ((Ov, h), cfg.w_std), "A_v": ((r, h), cfg.a_std_for(h)), "B_v": ((Ov, r), cfg.b_std),
     }
+    if cfg.bias:
+        shapes.update({"b_q": ((Oq,), cfg.bias_std), "b_k": ((Ok,), cfg.bias_std), "b_v": ((Ov,), cfg.bias_std)})
     if with_grad:
         B, S, d = cfg.batch, cfg.seq, cfg.head_dim
         shapes["dQ"] = ((B, cfg.n_q, S, d), 1.0)
@@ -217,6 +224,8 @@ def linear_inputs(cfg: LinearConfig, seed: int, with_grad: bool = True) -> Dict[
     N, k, o, r, dt = cfg.n_tokens, cfg.in_features, cfg.out_features, cfg.rank, cfg.dtype
     shapes = {"X": ((N, k), 1.0), "W": ((o, k), cfg.w_std), "A": ((r, k), cfg.a_std_for(k)),
               "B": ((o, r), cfg.b_std)}
+    if cfg.bias:
+        shapes["bias"] = ((o,), cfg.bias_std)
     if with_grad:
         shapes["dY"] = ((N, o), 1.0)
     return {key: normal(s, std, seed, LINEAR_IDS[key], dt) for key, (s, std) in shapes.items()}

@@ -47,6 +47,8 @@ MLP_CASES = [
     S.MLPConfig("mlp_f32_mid", 520, 256, 384, 8, 2.0, "swiglu", "f32"),
     S.MLPConfig("mlp_f32_geglu_ragged", 100, 72, 150, 3, 1.5, "geglu_tanh", "f32"),
     S.MLPConfig("mlp_bf16_long_k", 256, 1024, 512, 16, 2.0, "geglu_tanh", "bf16"),
+    S.MLPConfig("mlp_bf16_geglu_erf", 520, 256, 640, 16, 2.0, "geglu_erf", "bf16"),
+    S.MLPConfig("mlp_f32_geglu_erf_ragged", 130, 96, 200, 7, 2.0, "geglu_erf", "f32"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
@@ -54,6 +56,9 @@ QKV_CASES = [
     S.QKVConfig("qkv_f32_d64", 2, 100, 192, 4, 4, 64, 4, 2.0, 1.0e4, "f32"),
     S.QKVConfig("qkv_bf16_c4heads_ragged", 3, 77, 200, 14, 2, 64, 16, 2.0, 1.0e6, "bf16"),
     S.QKVConfig("qkv_f32_d128", 1, 40, 128, 2, 1, 128, 16, 0.5, 1.0e4, "f32"),
+    S.QKVConfig("qkv_bf16_bias_c4heads", 2, 300, 896, 14, 2, 64, 16, 2.0, 1.0e6, "bf16", bias=True),
+    S.QKVConfig("qkv_bf16_bias_d128", 1, 260, 256, 4, 2, 128, 8, 2.0, 1.0e4, "bf16", bias=True),
+    S.QKVConfig("qkv_f32_bias_d64", 2, 50, 128, 4, 2, 64, 4, 1.5, 1.0e4, "f32", bias=True),
 ]
 
 
@@ -64,6 +69,8 @@ LINEAR_CASES = [
     S.LinearConfig("linear_f32_mid", 520, 256, 384, 8, 2.0, "f32"),
     S.LinearConfig("linear_f32_ragged", 100, 72, 150, 3, 0.5, "f32"),
     S.LinearConfig("linear_bf16_tiny", 7, 8, 16, 1, 2.0, "bf16"),
+    S.LinearConfig("linear_bf16_bias", 520, 512, 384, 16, 2.0, "bf16", bias=True),
+    S.LinearConfig("linear_f32_bias_ragged", 90, 40, 70, 4, 2.0, "f32", bias=True),
 ]
 
 
@@ -156,7 +163,7 @@ def run_linear_oracle(cfg: S.LinearConfig, t_cpu, dY_cpu=None, rows=None):
     X = p["X"]
     if rows is not None:
         X, dY = X[rows], dY[rows]
-    Y, T = orc.lora_linear(X, p["W"], p["A"], p["B"], cfg.scale)
+    Y, T = orc.lora_linear(X, p["W"], p["A"], p["B"], cfg.scale, p.get("bias"))
     dX, dA, dB, _ = orc.lora_linear_bwd(dY, X, T, p["W"], p["A"], p["B"], cfg.scale)
     return {"Y": Y, "T": T, "dX": dX, "dA": dA, "dB": dB}
 

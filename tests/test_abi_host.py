@@ -90,11 +90,17 @@ def test_mlp_validation_codes():
     bad_dtype.dtype = 7
     assert _call_mlp_fwd(bad_dtype, 1 << 40) == 3
     bad_act = _mlp()
-    bad_act.act = 5
+    bad_act.act = 3
     assert _call_mlp_fwd(bad_act, 1 << 40) == 3
     need = B.lora_mlp_workspace_bytes(_mlp(), 0)
     assert _call_mlp_fwd(_mlp(), need - 1) == 4
     assert b"workspace" in lib.lora_last_error_message()
+    # the fused MLP is bias-free: a projection carrying a bias is refused
+    pb = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0, FAKE.value)
+    pr = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0)
+    assert lib.lora_mlp_fwd(ctypes.byref(_mlp()), FAKE, ctypes.byref(pr), ctypes.byref(pb), ctypes.byref(pr), FAKE,
+                            FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 3
+    assert b"bias" in lib.lora_last_error_message()
 
 
 def _call_qkv_bwd(desc, ws_bytes):

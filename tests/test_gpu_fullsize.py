@@ -9,6 +9,8 @@ sampled rows only: per-token outputs are compared on the sample, adapter
 gradients in full (they are then exact sums over the sample).  For QKV the
 sample is one whole sequence, so RoPE positions are unchanged.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -38,7 +40,10 @@ PER_TOKEN_MLP = ("Y", "G", "U", "T_gate", "T_up", "T_down", "dX")
 GRADS_MLP = ("dA_gate", "dB_gate", "dA_up", "dB_up", "dA_down", "dB_down")
 
 
-@pytest.mark.parametrize("cfg", [S.C2, S.C3, S.C4_MLP], ids=lambda c: c.name)
+C3_ERF = dataclasses.replace(S.C3, name="mlp_geglu_erf_h3072_i24576_bf16", act="geglu_erf")
+
+
+@pytest.mark.parametrize("cfg", [S.C2, S.C3, S.C4_MLP, C3_ERF], ids=lambda c: c.name)
 def test_mlp_full_size(cfg):
     gc.say(f"full-size mlp {cfg.name}: generating inputs")
     t = S.mlp_inputs(cfg, 0)
