@@ -15,7 +15,8 @@ to float64, so both sides see bit-identical inputs.
 Distributions follow the benchmark configurations: activations and upstream
 gradients ~N(0,1), frozen base weights std 0.02, LoRA A with variance
 1/in_dim (std in_dim**-0.5), LoRA B std 0.02 (non-zero, so the adapter path is
-visible in every output and gradient), optional frozen base biases std 0.5.
+visible in every output and gradient), optional frozen base biases std 0.5,
+optional q/k RMSNorm weights N(1, 0.2^2).
 """
 from __future__ import annotations
 
@@ -42,19 +43,22 @@ QKV_IDS = {
     "W_v": 27, "A_v": 28, "B_v": 29,
     "dQ": 30, "dK": 31, "dV": 32,
     "b_q": 33, "b_k": 34, "b_v": 35,
+    "qn_w": 36, "kn_w": 37,
 }
 LINEAR_IDS = {"X": 40, "W": 41, "A": 42, "B": 43, "dY": 44, "bias": 45}
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
-def normal(shape, std: float, seed: int, tensor_id: int, dtype: str) -> torch.Tensor:
-    """Seeded N(0, std^2) tensor on the CPU, rounded once to ``dtype``."""
+def normal(shape, std: float, seed: int, tensor_id: int, dtype: str, mean: float = 0.0) -> torch.Tensor:
+    """Seeded N(mean, std^2) tensor on the CPU, rounded once to ``dtype``."""
     g = torch.Generator("cpu")
     g.manual_seed(1000 * int(seed) + int(tensor_id))
     x = torch.randn(tuple(int(s) for s in shape), generator=g, dtype=torch.float32)
     if std != 1.0:
         x.mul_(float(std))
+    if mean != 0.0:
+        x.add_(float(mean))
     return x.to(TORCH_DTYPES[dtype])
 
 
@@ -110,6 +114,9 @@ class QKVConfig:
     a_std: Optional[float] = None
     bias: bool = False     # frozen base biases b_q, b_k, b_v (std bias_std)
     bias_std: float = 0.5
+    qk_norm: bool = False  # per-head RMSNorm weights qn_w, kn_w ~ N(1, norm_std^2)
+    norm_std: float = 0.2
+    norm_eps: float = 1e-6
 
     @property
     def n_tokens(self) -> int:
@@ -216,7 +223,11 @@ def qkv_inputs(cfg: QKVConfig, seed: int, with_grad: bool = True) -> Dict[str, t
         shapes["dQ"] = ((B, cfg.n_q, S, d), 1.0)
         shapes["dK"] = ((B, cfg.n_kv, S, d), 1.0)
         shapes["dV"] = ((B, cfg.n_kv, S, d), 1.0)
-    return {k: normal(s, std, seed, QKV_IDS[k], dt) for k, (s, std) in shapes.items()}
+    out = {k: normal(s, std, seed, QKV_IDS[k], dt) for k, (s, std) in shapes.items()}
+    if cfg.qk_norm:
+        for k in ("qn_w", "kn_w"):
+            out[k] = normal((cfg.head_dim,), cfg.norm_std, seed, QKV_IDS[k], dt, mean=1.0)
+    return out
 
 
 def linear_inputs(cfg: LinearConfig, seed: int, with_grad: bool = True) -> Dict[str, torch.Tensor]:

@@ -24,6 +24,10 @@ Sources (the pages' titles and sections):
     together, GQA with different head counts, following RoFormer.
   * Same page, section "Fused linear cross-entropy", "Key design decisions":
     frozen weights get no weight gradient.
+  * Same page, "Model compatibility" and "Fused LoRA operations": Qwen3 /
+    Gemma3 attention keeps its per-head q_norm / k_norm RMSNorm (between the
+    projection and RoPE) under QKV fusion; RMSNorm is one of the primary
+    papers the page's introduction names.
   * Axolotl, "monkeypatch.lora_kernels", section "apply_lora_kernel_patches"
     (note: no dropout, no bias) and section "original_apply_qkv" (input
     hidden_states [batch, seq, hidden] -> (query, key, value)).
@@ -50,7 +54,7 @@ __all__ = [
     "activation", "lora_linear", "lora_linear_bwd",
     "mlp_fwd", "mlp_bwd",
     "rope_angles", "rope_rotate", "rope_rotate_transpose", "head_split", "head_unsplit",
-    "qkv_fwd", "qkv_bwd",
+    "rms_norm", "rms_norm_bwd", "qkv_fwd", "qkv_bwd",
 ]
 
 _SQRT_2_OVER_PI = math.sqrt(2.0 / math.pi)
@@ -230,20 +234,49 @@ def head_unsplit(Q: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Per-head RMSNorm of Q and K (q_norm / k_norm; Zhang & Sennrich's RMSNorm)
+# ---------------------------------------------------------------------------
+
+def rms_norm(x: np.ndarray, w: np.ndarray, eps: float):
+    """y = x / sqrt(mean(x^2) + eps) * w over the last axis.  Returns (y, rinv)
+    with rinv = 1 / sqrt(mean(x^2) + eps) (one value per row)."""
+    rinv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return x * rinv * w, rinv[..., 0]
+
+
+def rms_norm_bwd(dy: np.ndarray, x: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """dx of <dy, rms_norm(x)> for fixed w:
+    rinv * (w dy - xhat * mean(w dy xhat)), xhat = x rinv."""
+    rinv = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    xhat = x * rinv
+    gw = dy * w
+    return rinv * (gw - xhat * np.mean(gw * xhat, axis=-1, keepdims=True))
+
+
+# ---------------------------------------------------------------------------
 # LoRA QKV with GQA split and RoPE (opake_lora_qkv; Axolotl original_apply_qkv)
 # ---------------------------------------------------------------------------
 
 _QKV = ("q", "k", "v")
 
 
+_NORM_KEYS = {"q": "qn_w", "k": "kn_w"}
+
+
 def qkv_fwd(p: Dict[str, np.ndarray], batch: int, seq: int, n_q: int, n_kv: int,
-            head_dim: int, theta: float, scales) -> Dict[str, np.ndarray]:
+            head_dim: int, theta: float, scales, norm_eps: float = 1e-6) -> Dict[str, np.ndarray]:
     """Q, K, V [B, heads, S, d] from X [B*S, h]: LoRA linear per projection,
     head split, RoPE on Q and K (not V).  Also returns T_q, T_k, T_v.
 
     Optional frozen biases b_q, b_k, b_v ([out]) are part of the base
     projection, so they are added before the rotation.  qkv_bwd does not read
-    them: a frozen bias has no gradient and does not change the others."""
+    them: a frozen bias has no gradient and does not change the others.
+
+    Optional per-head RMSNorm weights qn_w, kn_w ([head_dim], shared by the
+    heads of Q resp. K) normalise each head of the projection after the
+    split and before the rotation (Qwen3 / Gemma3 q_norm, k_norm); then
+    P_q / P_k (the projection before the norm, [B*S, out]) and rinv_q /
+    rinv_k ([B*S, heads]) are returned too."""
     X = p["X"]
     heads = {"q": n_q, "k": n_kv, "v": n_kv}
     ang = rope_angles(seq, head_dim, theta)
@@ -251,6 +284,10 @@ def qkv_fwd(p: Dict[str, np.ndarray], batch: int, seq: int, n_q: int, n_kv: int,
     for name, s in zip(_QKV, scales):
         P, T = lora_linear(X, p["W_" + name], p["A_" + name], p["B_" + name], s, p.get("b_" + name))
         Z = head_split(P, batch, seq, heads[name], head_dim)
+        if _NORM_KEYS.get(name) in p:
+            Z, rinv = rms_norm(Z, p[_NORM_KEYS[name]], norm_eps)
+            out["P_" + name] = P
+            out["rinv_" + name] = head_unsplit(rinv[..., None])
         if name != "v":
             Z = rope_rotate(Z, ang)
         out[name.upper()] = Z
@@ -260,19 +297,27 @@ def qkv_fwd(p: Dict[str, np.ndarray], batch: int, seq: int, n_q: int, n_kv: int,
 
 def qkv_bwd(p: Dict[str, np.ndarray], dQ: np.ndarray, dK: np.ndarray, dV: np.ndarray,
             batch: int, seq: int, n_q: int, n_kv: int, head_dim: int, theta: float,
-            scales) -> Dict[str, np.ndarray]:
+            scales, norm_eps: float = 1e-6) -> Dict[str, np.ndarray]:
     """Backward of qkv_fwd for the loss <dQ,Q> + <dK,K> + <dV,V>, W frozen.
 
     dP_q = unsplit(R^T dQ), dP_k = unsplit(R^T dK), dP_v = unsplit(dV); then the
     LoRA linear backward per projection; dX sums the three input gradients.
+    With q/k norm weights, R^T dQ is first pulled back through the per-head
+    RMSNorm of the (recomputed) projection.
     """
     X = p["X"]
     ang = rope_angles(seq, head_dim, theta)
     grads = {"q": rope_rotate_transpose(dQ, ang), "k": rope_rotate_transpose(dK, ang), "v": dV}
+    heads = {"q": n_q, "k": n_kv, "v": n_kv}
     out = {}
     dX = np.zeros_like(X)
     for name, s in zip(_QKV, scales):
-        dP = head_unsplit(grads[name])
+        g = grads[name]
+        if _NORM_KEYS.get(name) in p:
+            P, _ = lora_linear(X, p["W_" + name], p["A_" + name], p["B_" + name], s, p.get("b_" + name))
+            Z = head_split(P, batch, seq, heads[name], head_dim)
+            g = rms_norm_bwd(g, Z, p[_NORM_KEYS[name]], norm_eps)
+        dP = head_unsplit(g)
         T = X @ p["A_" + name].T
         dXp, dA, dB, _ = lora_linear_bwd(dP, X, T, p["W_" + name], p["A_" + name], p["B_" + name], s)
         dX = dX + dXp

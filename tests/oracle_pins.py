@@ -383,8 +383,9 @@ def check_head_split_bruteforce(orc):
 # QKV
 # ---------------------------------------------------------------------------
 
-def _torch_qkv(tp, shape, scales):
-    """QKV written with torch ops; RoPE as complex multiplication."""
+def _torch_qkv(tp, shape, scales, eps=1e-6):
+    """QKV written with torch ops; RoPE as complex multiplication; optional
+    q/k norm with torch's F.rms_norm over the head dimension."""
     B, S, nq, nkv, d, theta = (shape[k] for k in ("batch", "seq", "n_q", "n_kv", "head_dim", "theta"))
     j = torch.arange(d // 2, dtype=torch.float64)
     ang = torch.arange(S, dtype=torch.float64)[:, None] * torch.exp(-(2.0 * j / d) * math.log(theta))[None, :]
@@ -394,6 +395,9 @@ def _torch_qkv(tp, shape, scales):
         P = F.linear(tp["X"], tp["W_" + name], tp.get("b_" + name)) + \
             s * F.linear(F.linear(tp["X"], tp["A_" + name]), tp["B_" + name])
         Z = P.reshape(B, S, heads, d).permute(0, 2, 1, 3)
+        wn = tp.get({"q": "qn_w", "k": "kn_w"}.get(name, ""))
+        if wn is not None:
+            Z = F.rms_norm(Z, (d,), weight=wn, eps=eps)
         if name != "v":
             c = torch.complex(Z[..., : d // 2], Z[..., d // 2:]) * rot
             Z = torch.cat([c.real, c.imag], dim=-1)
@@ -457,6 +461,52 @@ def check_qkv_bias_vs_autograd(orc):
     for n in "qkv":
         assert _rel(gq["dA_" + n], tp["A_" + n].grad.numpy()) < 1e-12, n
         assert _rel(gq["dB_" + n], tp["B_" + n].grad.numpy()) < 1e-12, n
+
+
+def check_rms_norm_vs_torch(orc):
+    g = _rng(21)
+    x, w, dy = g.standard_normal((3, 5, 8)), g.standard_normal(8), g.standard_normal((3, 5, 8))
+    for eps in (1e-6, 0.3):
+        tx = torch.tensor(x, requires_grad=True)
+        y = F.rms_norm(tx, (8,), weight=torch.tensor(w), eps=eps)
+        y.backward(torch.tensor(dy))
+        yo, rinv = orc.rms_norm(x, w, eps)
+        assert _rel(yo, y.detach().numpy()) < 1e-13
+        # rinv is the inverse root mean square: rinv^2 (mean x^2 + eps) = 1
+        assert np.max(np.abs(rinv ** 2 * (np.mean(x * x, axis=-1) + eps) - 1.0)) < 1e-13
+        assert _rel(orc.rms_norm_bwd(dy, x, w, eps), tx.grad.numpy()) < 1e-13
+
+
+def check_qkv_norm_vs_autograd(orc):
+    """q/k norm (F.rms_norm) between the head split and RoPE, forward and
+    backward, against torch autograd; with eps = 0 Q is also invariant under
+    scaling the whole q projection (W_q, B_q, b_q) by a positive constant."""
+    p, gr = tiny_qkv(22, batch=2, seq=4, h=6, n_q=4, n_kv=2, d=8, r=2)
+    shape = dict(batch=2, seq=4, n_q=4, n_kv=2, head_dim=8, theta=20.0)
+    g = _rng(23)
+    p["qn_w"], p["kn_w"] = 1.0 + 0.5 * g.standard_normal(8), 1.0 + 0.5 * g.standard_normal(8)
+    p["b_q"] = g.standard_normal(32)
+    eps = 1e-5
+    tp = {k: torch.tensor(v, requires_grad=(k[0] in "XAB")) for k, v in p.items()}
+    ref = _torch_qkv(tp, shape, QKV_SCALES, eps)
+    loss = sum((ref[k] * torch.tensor(gr["d" + k])).sum() for k in "QKV")
+    loss.backward()
+    o = orc.qkv_fwd(p, scales=QKV_SCALES, norm_eps=eps, **shape)
+    gq = orc.qkv_bwd(p, gr["dQ"], gr["dK"], gr["dV"], scales=QKV_SCALES, norm_eps=eps, **shape)
+    for k in "QKV":
+        assert _rel(o[k], ref[k].detach().numpy()) < 1e-12, k
+    assert _rel(gq["dX"], tp["X"].grad.numpy()) < 1e-12
+    for n in "qkv":
+        assert _rel(gq["dA_" + n], tp["A_" + n].grad.numpy()) < 1e-12, n
+        assert _rel(gq["dB_" + n], tp["B_" + n].grad.numpy()) < 1e-12, n
+    assert o["rinv_q"].shape == (8, 4) and o["rinv_k"].shape == (8, 2) and "rinv_v" not in o
+    p0 = dict(p)
+    o0 = orc.qkv_fwd(p0, scales=QKV_SCALES, norm_eps=0.0, **shape)
+    for k in ("W_q", "B_q", "b_q"):
+        p0[k] = p[k] * 3.5
+    o1 = orc.qkv_fwd(p0, scales=QKV_SCALES, norm_eps=0.0, **shape)
+    assert _rel(o1["Q"], o0["Q"]) < 1e-13
+    assert not np.allclose(o1["P_q"], o0["P_q"])
 
 
 def check_qkv_finite_differences(orc):

@@ -33,25 +33,42 @@ MUTATIONS = [
     ("head split order", ".transpose(0, 2, 1, 3).copy()\n\n\ndef head_unsplit", ".transpose(0, 2, 1, 3)[:, ::-1].copy()\n\n\ndef head_unsplit"),
     ("rope on V", "if name != \"v\":\n            Z = rope_rotate", "if True:\n            Z = rope_rotate"),
     ("no RoPE adjoint in backward", "grads = {\"q\": rope_rotate_transpose(dQ, ang)", "grads = {\"q\": dQ"),
+    ("rms eps outside sqrt", "1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)\n    return",
+     "1.0 / (np.sqrt(np.mean(x * x, axis=-1, keepdims=True)) + eps)\n    return"),
+    ("rms norm drops weight", "return x * rinv * w, rinv[..., 0]", "return x * rinv, rinv[..., 0]"),
+    ("rms backward drops mean term", "return rinv * (gw - xhat * np.mean(gw * xhat, axis=-1, keepdims=True))",
+     "return rinv * gw"),
+    ("qk norm after RoPE",
+     ("            Z, rinv = rms_norm(Z, p[_NORM_KEYS[name]], norm_eps)\n",
+      "        out[name.upper()] = Z\n"),
+     ("            _, rinv = rms_norm(Z, p[_NORM_KEYS[name]], norm_eps)\n",
+      "        if _NORM_KEYS.get(name) in p:\n"
+      "            Z, _ = rms_norm(Z, p[_NORM_KEYS[name]], norm_eps)\n"
+      "        out[name.upper()] = Z\n")),
     ("gelu_erf' drops density", " + g * np.exp(-0.5 * g * g) / math.sqrt(2.0 * math.pi)", ""),
     ("gelu_erf without 1/sqrt2", "_erf(g / math.sqrt(2.0)))\n\n\ndef gelu_erf_grad", "_erf(g))\n\n\ndef gelu_erf_grad"),
     ("bias dropped", "Y = Y + bias[None, :]", "Y = Y"),
     ("bias scaled with adapter", "Y = Y + bias[None, :]", "Y = Y + s * bias[None, :]"),
     ("qkv bias after RoPE",
-     "p[\"B_\" + name], s, p.get(\"b_\" + name))\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n"
-     "        if name != \"v\":\n            Z = rope_rotate(Z, ang)\n",
-     "p[\"B_\" + name], s)\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n"
-     "        if name != \"v\":\n            Z = rope_rotate(Z, ang)\n"
-     "        if p.get(\"b_\" + name) is not None:\n"
-     "            Z = Z + head_split(np.broadcast_to(p[\"b_\" + name], P.shape), batch, seq, heads[name], head_dim)\n"),
+     ("p[\"B_\" + name], s, p.get(\"b_\" + name))\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n",
+      "        out[name.upper()] = Z\n"),
+     ("p[\"B_\" + name], s)\n        Z = head_split(P, batch, seq, heads[name], head_dim)\n",
+      "        if p.get(\"b_\" + name) is not None:\n"
+      "            Z = Z + head_split(np.broadcast_to(p[\"b_\" + name], P.shape), batch, seq, heads[name], head_dim)\n"
+      "        out[name.upper()] = Z\n")),
 ]
 
 
 def _mutant(old, new):
+    """A copy of the oracle with `old` replaced by `new` (or, for tuples, each
+    old[i] by new[i]); every anchor must occur exactly once."""
     src = open(SRC_PATH).read()
-    assert src.count(old) == 1, f"mutation anchor not unique/found: {old!r}"
+    olds, news = (old, new) if isinstance(old, tuple) else ((old,), (new,))
+    for o, n in zip(olds, news):
+        assert src.count(o) == 1, f"mutation anchor not unique/found: {o!r}"
+        src = src.replace(o, n)
     mod = types.ModuleType("lora_oracle_mutant")
-    exec(compile(src.replace(old, new), "lora_oracle_mutant", "exec"), mod.__dict__)
+    exec(compile(src, "lora_oracle_mutant", "exec"), mod.__dict__)
     return mod
 
 
