@@ -179,6 +179,45 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
                  void* dX, void* dA_q, void* dB_q, void* dA_k, void* dB_k, void* dA_v, void* dB_v,
                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* Per-head RMSNorm of Q and K (q_norm / k_norm) between the projection and
+ * RoPE: each head x [head_dim] becomes x / sqrt(mean(x^2) + eps) * w, with
+ * one weight vector w [head_dim] (call dtype) for all Q heads and one for all
+ * K heads.  Weights are frozen (no gradient).  For Gemma-style (1 + w) norms
+ * pass 1 + w. */
+typedef struct {
+  const void* q_weight;   /* [head_dim] */
+  const void* k_weight;   /* [head_dim] */
+  float eps;              /* >= 0 */
+} lora_qk_norm_t;
+
+/*
+ * LoRA QKV forward with q/k norm (Opake, "Model Patches and Kernels",
+ * "Fused LoRA operations" and "Model compatibility": the Qwen3 / Gemma3
+ * attention wrappers keep q_norm / k_norm under QKV fusion; Zhang & Sennrich
+ * RMSNorm).  As lora_qkv_fwd, with the norm applied to each Q and K head after
+ * the bias and before RoPE.  It also writes, for the backward:
+ *   Pn   [N, (n_q + n_kv) * head_dim]  the Q|K projections before the norm (call dtype);
+ *   rinv [N, n_q + n_kv] float32       1 / sqrt(mean(x^2) + eps) per token and head.
+ * The norm weights and Pn must be 16-byte aligned (LORA_ERR_UNSUPPORTED otherwise).
+ * Workspace: lora_qkv_workspace_bytes(desc, 0).
+ */
+int lora_qkv_norm_fwd(const lora_qkv_desc_t* desc, const void* X,
+                      const lora_proj_t* q, const lora_proj_t* k, const lora_proj_t* v,
+                      const lora_qk_norm_t* norm, void* Q, void* K, void* V, void* T, void* Pn, float* rinv,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * Backward of lora_qkv_norm_fwd: as lora_qkv_bwd, pulling R^T dQ and R^T dK
+ * back through the norm with the saved Pn and rinv.  dQ, dK, dV, Pn and the
+ * norm weights must be 16-byte aligned.  Workspace: lora_qkv_workspace_bytes(desc, 1).
+ */
+int lora_qkv_norm_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, const void* dV,
+                      const void* X, const void* T, const void* Pn, const float* rinv,
+                      const lora_proj_t* q, const lora_proj_t* k, const lora_proj_t* v,
+                      const lora_qk_norm_t* norm,
+                      void* dX, void* dA_q, void* dB_q, void* dA_k, void* dB_k, void* dA_v, void* dB_v,
+                      void* workspace, size_t workspace_bytes, void* hip_stream);
+
 /*
  * LoRA linear forward (Opake, "Model Patches and Kernels", "Fused LoRA
  * operations": the single adapted projection, opake_lora_w; Axolotl,

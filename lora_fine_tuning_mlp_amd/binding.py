@@ -51,6 +51,10 @@ class Proj(ctypes.Structure):
                 ("bias", ctypes.c_void_p)]
 
 
+class QkNorm(ctypes.Structure):
+    _fields_ = [("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 _P = ctypes.c_void_p
 _SIGS = {
     "lora_mlp_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(MlpDesc), ctypes.c_int]),
@@ -70,6 +74,12 @@ _SIGS = {
                                        ctypes.c_size_t, _P]),
     "lora_linear_bwd": (ctypes.c_int, [ctypes.POINTER(LinearDesc), _P, _P, _P, ctypes.POINTER(Proj), _P, _P, _P,
                                        _P, ctypes.c_size_t, _P]),
+    "lora_qkv_norm_fwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, ctypes.POINTER(Proj), ctypes.POINTER(Proj),
+                                         ctypes.POINTER(Proj), ctypes.POINTER(QkNorm), _P, _P, _P, _P, _P, _P, _P,
+                                         ctypes.c_size_t, _P]),
+    "lora_qkv_norm_bwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(Proj),
+                                         ctypes.POINTER(Proj), ctypes.POINTER(Proj), ctypes.POINTER(QkNorm), _P, _P,
+                                         _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "lora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "lora_last_error_message": (ctypes.c_char_p, []),
     "lora_version": (ctypes.c_char_p, []),
@@ -187,6 +197,21 @@ def lora_linear_bwd(desc, dY, X, T, p: Proj, dX, dA, dB, workspace, stream=None)
                                  _ptr(dB), _ptr(workspace), workspace.numel(), _stream(stream)))
 
 
+def lora_qkv_norm_fwd(desc, X, q: Proj, k: Proj, v: Proj, norm: QkNorm, Q, K, V, T, Pn, rinv, workspace,
+                      stream=None):
+    _check(lib().lora_qkv_norm_fwd(ctypes.byref(desc), _ptr(X), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
+                                   ctypes.byref(norm), _ptr(Q), _ptr(K), _ptr(V), _ptr(T), _ptr(Pn), _ptr(rinv),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
+def lora_qkv_norm_bwd(desc, dQ, dK, dV, X, T, Pn, rinv, q: Proj, k: Proj, v: Proj, norm: QkNorm, dX, dA_q, dB_q,
+                      dA_k, dB_k, dA_v, dB_v, workspace, stream=None):
+    _check(lib().lora_qkv_norm_bwd(ctypes.byref(desc), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(X), _ptr(T), _ptr(Pn),
+                                   _ptr(rinv), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v), ctypes.byref(norm),
+                                   _ptr(dX), _ptr(dA_q), _ptr(dB_q), _ptr(dA_k), _ptr(dB_k), _ptr(dA_v), _ptr(dB_v),
+                                   _ptr(workspace), workspace.numel(), _stream(stream)))
+
+
 # ---- timing -------------------------------------------------------------------
 
 def timing_enable(on: bool = True) -> None:
@@ -252,10 +277,11 @@ class MLP:
 
 class QKV:
     """LoRA QKV weights on the device plus the buffers one fwd+bwd needs
-    (optional frozen biases under the keys b_q, b_k, b_v)."""
+    (optional frozen biases under the keys b_q, b_k, b_v; optional q/k norm
+    weights under qn_w, kn_w, which select the norm entry points)."""
 
     def __init__(self, t: Dict[str, torch.Tensor], batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta,
-                 scales=(2.0, 2.0, 2.0)):
+                 scales=(2.0, 2.0, 2.0), norm_eps: float = 1e-6):
         self.t = t
         self.desc = qkv_desc(batch, seq, hidden, n_q, n_kv, head_dim, rank, dtype, theta)
         self.dtype = t["X"].dtype
@@ -280,16 +306,30 @@ class QKV:
         }
         self.ws_fwd = torch.empty(max(1, lora_qkv_workspace_bytes(self.desc, 0)), device=dev, dtype=torch.uint8)
         self.ws_bwd = torch.empty(max(1, lora_qkv_workspace_bytes(self.desc, 1)), device=dev, dtype=torch.uint8)
+        self.norm = None
+        if "qn_w" in t:
+            self.norm = QkNorm(_ptr(t["qn_w"]), _ptr(t["kn_w"]), float(norm_eps))
+            self.Pn = torch.empty(N, Oq + Ok, **e)
+            self.rinv = torch.empty(N, self.nq + self.nkv, device=dev, dtype=torch.float32)
 
     def forward(self, stream=None):
-        lora_qkv_fwd(self.desc, self.t["X"], self.q, self.k, self.v, self.Q, self.K, self.V, self.T, self.ws_fwd,
-                     stream)
+        if self.norm is not None:
+            lora_qkv_norm_fwd(self.desc, self.t["X"], self.q, self.k, self.v, self.norm, self.Q, self.K, self.V,
+                              self.T, self.Pn, self.rinv, self.ws_fwd, stream)
+        else:
+            lora_qkv_fwd(self.desc, self.t["X"], self.q, self.k, self.v, self.Q, self.K, self.V, self.T,
+                         self.ws_fwd, stream)
         return self.Q, self.K, self.V
 
     def backward(self, dQ, dK, dV, stream=None):
         g = self.grads
-        lora_qkv_bwd(self.desc, dQ, dK, dV, self.t["X"], self.T, self.q, self.k, self.v, self.dX, g["dA_q"],
-                     g["dB_q"], g["dA_k"], g["dB_k"], g["dA_v"], g["dB_v"], self.ws_bwd, stream)
+        if self.norm is not None:
+            lora_qkv_norm_bwd(self.desc, dQ, dK, dV, self.t["X"], self.T, self.Pn, self.rinv, self.q, self.k, self.v,
+                              self.norm, self.dX, g["dA_q"], g["dB_q"], g["dA_k"], g["dB_k"], g["dA_v"], g["dB_v"],
+                              self.ws_bwd, stream)
+        else:
+            lora_qkv_bwd(self.desc, dQ, dK, dV, self.t["X"], self.T, self.q, self.k, self.v, self.dX, g["dA_q"],
+                         g["dB_q"], g["dA_k"], g["dB_k"], g["dA_v"], g["dB_v"], self.ws_bwd, stream)
         return self.dX
 
 

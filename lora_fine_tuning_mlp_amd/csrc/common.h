@@ -206,6 +206,21 @@ __device__ __forceinline__ int perm_row(int lg, int w) {
   return ((gg * cw + rem % cw) << 4) + rem / cw;
 }
 
+// ---- lane-group sums (DPP, within one 16-lane row) -----------------------------
+template <int CTRL> __device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of N lanes (N = 4, 8 or 16); every lane of a group
+// gets the group's sum.  All lanes of the group must be active.
+template <int N> __device__ __forceinline__ float lane_group_sum(float v) {
+  static_assert(N == 4 || N == 8 || N == 16, "groups of 4, 8 or 16 lanes");
+  v += dpp_f<0xB1>(v);                           // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);                           // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) v += dpp_f<0x141>(v);    // row_half_mirror: lane i <- 7 - i
+  if constexpr (N >= 16) v += dpp_f<0x140>(v);   // row_mirror: lane i <- 15 - i
+  return v;
+}
+
 // ---- activations (fp32) --------------------------------------------------------
 #define LORA_ACT_SWIGLU 0
 #define LORA_ACT_GEGLU_TANH 1

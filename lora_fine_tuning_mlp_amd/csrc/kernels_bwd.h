@@ -148,6 +148,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
     } else {
       base_lo = (long)ch * BK;
       base_hi = base_lo + HW;
+      // Adapter of this chunk by column range (ranges are whole chunks).
+      p = (a.nadp > 1 && base_lo >= a.off[1]) ? ((a.nadp > 2 && base_lo >= a.off[2]) ? 2 : 1) : 0;
     }
     const T* Bsrc = static_cast<const T*>(a.Bp[p]);
 
@@ -229,7 +231,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
       const int tpr = (sizeof(T) == 2) ? 2 : 4;   // threads per kk
       const int kk = q.tid / tpr, t0 = (q.tid % tpr) * VEC;
       const long col = (kk < HW) ? base_lo + kk : base_hi + (kk - HW);
-      const long lim = a.qkv ? (long)a.off[p + 1] : (long)a.O;
+      const long lim = (long)a.off[p + 1];
       const T* brow = (col < lim) ? Bsrc + (col - a.off[p]) * a.r : nullptr;
       const u32x4 v = gload<T>(brow, t0, a.r, a.vecB);
       const unsigned* wv = reinterpret_cast<const unsigned*>(&v);
@@ -287,6 +289,82 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
         const long n = m0 + (4 * q.w + i) * 16 + 4 * q.g + j;
         if (n < a.N) a.dT_part[(((long)cr * 3 + p) * a.N + n) * 16 + q.r16] = a.s[p] * dT[p][i][j];
       }
+}
+
+// ===========================================================================
+// q/k norm backward: dP (token-major [N][O]) from dQ/dK/dV.  For q and k heads
+// g = R^T dQ is pulled back through the per-head RMSNorm,
+//   dP = rinv * (w g - xhat * mean(w g xhat)),  xhat = Pn * rinv,
+// with Pn and rinv saved by the forward; v heads are copied.  One group of
+// TPH lanes per (token, head); each lane holds E elements of the head's first
+// half and the E matching elements of its second half (the RoPE pairs).
+// ===========================================================================
+struct NormBwdArgs {
+  const void* src[3];           // dQ, dK, dV as [B][heads][S][d]
+  const void* Pn;               // [N][off[2]]
+  const float* rinv;            // [N][nh[0] + nh[1]]
+  const void* nw[2];            // q_norm / k_norm weights [d]
+  const float* cs; const float* sn;
+  void* dP;                     // [N][O]
+  long N; int S, d;
+  int nh[3];
+  int off[4];
+};
+
+template <class T, int TPH>
+__global__ __launch_bounds__(256) void k_qk_norm_bwd(NormBwdArgs a) {
+  constexpr int E = ET<T>::VEC;                  // 8 bf16 or 4 fp32: one 16-byte chunk
+  constexpr int IPB = 256 / TPH;                 // (token, head) items per block
+  const int gh = blockIdx.y;                     // head over q | k | v
+  const int p = (gh < a.nh[0]) ? 0 : ((gh < a.nh[0] + a.nh[1]) ? 1 : 2);
+  const int hd = gh - ((p == 0) ? 0 : ((p == 1) ? a.nh[0] : a.nh[0] + a.nh[1]));
+  const long n = (long)blockIdx.x * IPB + threadIdx.x / TPH;
+  const int t = threadIdx.x % TPH;
+  const int half = a.d >> 1;
+  const int jl = t * E;                          // < d/2
+  const bool live = n < a.N;                     // whole lane groups share n
+  const long nn = live ? n : 0;
+  const int s = (int)(nn % a.S);
+  const long b = nn / a.S;
+  const T* src = static_cast<const T*>(a.src[p]) + ((b * a.nh[p] + hd) * a.S + s) * (long)a.d;
+  float gl[E], gh2[E];
+  unpack(*reinterpret_cast<const u32x4*>(src + jl), gl);
+  unpack(*reinterpret_cast<const u32x4*>(src + jl + half), gh2);
+  T* dst = static_cast<T*>(a.dP) + nn * (long)a.off[3] + a.off[p] + (long)hd * a.d;
+  if (p < 2) {
+    const float* __restrict__ cs = a.cs + (long)s * half + jl;
+    const float* __restrict__ sn = a.sn + (long)s * half + jl;
+    const T* pn = static_cast<const T*>(a.Pn) + nn * (long)a.off[2] + a.off[p] + (long)hd * a.d;
+    const T* w = static_cast<const T*>(a.nw[p]);
+    float xl[E], xh[E], wl[E], wh[E];
+    unpack(*reinterpret_cast<const u32x4*>(pn + jl), xl);
+    unpack(*reinterpret_cast<const u32x4*>(pn + jl + half), xh);
+    unpack(*reinterpret_cast<const u32x4*>(w + jl), wl);
+    unpack(*reinterpret_cast<const u32x4*>(w + jl + half), wh);
+    const float ri = a.rinv[nn * (a.nh[0] + a.nh[1]) + (p == 0 ? 0 : a.nh[0]) + hd];
+    float dot = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float c = cs[e], sv = sn[e];
+      const float ul = gl[e] * c + gh2[e] * sv;  // R^T: rotate by -angle
+      const float uh = gh2[e] * c - gl[e] * sv;
+      gl[e] = ul * wl[e];                        // w g
+      gh2[e] = uh * wh[e];
+      xl[e] *= ri;                               // xhat
+      xh[e] *= ri;
+      dot += gl[e] * xl[e] + gh2[e] * xh[e];
+    }
+    const float m = lane_group_sum<TPH>(dot) / (float)a.d;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      gl[e] = ri * (gl[e] - xl[e] * m);
+      gh2[e] = ri * (gh2[e] - xh[e] * m);
+    }
+  }
+  if (live) {
+    *reinterpret_cast<u32x4*>(dst + jl) = pack(gl);
+    *reinterpret_cast<u32x4*>(dst + jl + half) = pack(gh2);
+  }
 }
 
 // dT[p][n][t] = sum over the prologue's column ranges c (fixed order) of its

@@ -259,6 +259,12 @@ struct QKVFwdArgs {
   const void* X;
   const void* W[3]; const void* A[3]; const void* B[3];
   const void* bias[3]; // frozen base biases [O_p] or nullptr, added before RoPE
+  const void* nw[2];   // q_norm / k_norm weights [d] (used when norm != 0)
+  void* Pn;            // norm: pre-norm q|k projections [N][off[2]]
+  float* rinv;         // norm: inverse RMS per token and q/k head [N][nh[0] + nh[1]]
+  float eps;
+  int norm;
+  int vecN;
   float s[3];
   void* out[3];        // Q, K, V
   float* T[3];
@@ -402,6 +408,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       b2v[gi][e] = bp ? to_f<T>(bp[oo + half + e]) : 0.f;
     }
   }
+  // q/k norm weights of the lane's columns (index within the head).
+  float w1v[NG][cw], w2v[NG][cw];
+#pragma unroll
+  for (int gi = 0; gi < NG; ++gi) {
+    const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+    const T* wp = nullptr;
+    int jj = 0;
+    if (a.norm && o1 < a.off[2]) {
+      const int p = proj_of(o1);
+      wp = static_cast<const T*>(p == 0 ? a.nw[0] : a.nw[1]);
+      jj = (o1 - a.off[p]) % a.d;
+    }
+#pragma unroll
+    for (int e = 0; e < cw; ++e) {
+      w1v[gi][e] = wp ? to_f<T>(wp[jj + e]) : 1.f;
+      w2v[gi][e] = wp ? to_f<T>(wp[jj + half + e]) : 1.f;
+    }
+  }
+  const float inv_d = 1.0f / (float)a.d;
+  const int nhqk = a.nh[0] + a.nh[1];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
     float cc[4][NG][cw], ss[4][NG][cw];
@@ -436,17 +462,41 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
         const int p = proj_of(o1);
         const int oo = o1 - a.off[p];
         const int hd = oo / a.d, jj = oo % a.d;      // jj < d/2, jj .. jj+cw-1 consecutive
+        float x1[cw], x2[cw];
+#pragma unroll
+        for (int e = 0; e < cw; ++e) {
+          x1[e] = acc[mb][b1 + e][j] + b1v[gi][e];
+          x2[e] = acc[mb][b1 + cw + e][j] + b2v[gi][e];
+        }
+        if (a.norm && p < 2) {
+          // Per-head RMSNorm: the head's d columns of this row sit in the 16
+          // lanes that share the row (cw pairs per lane), so the sum of
+          // squares is one 16-lane reduction.  The whole group takes this
+          // branch together: row, projection and head are the same for all.
+          float sq = 0.f;
+#pragma unroll
+          for (int e = 0; e < cw; ++e) sq += x1[e] * x1[e] + x2[e] * x2[e];
+          sq = lane_group_sum<16>(sq);
+          const float ri = rsqrtf(sq * inv_d + a.eps);
+          T* pn = static_cast<T*>(a.Pn) + row * (long)a.off[2] + o1;
+          gstore<T, cw>(pn, x1, cw, a.vecN);
+          gstore<T, cw>(pn + half, x2, cw, a.vecN);
+          if (q.r16 == 0) a.rinv[row * nhqk + (p == 0 ? 0 : a.nh[0]) + hd] = ri;
+#pragma unroll
+          for (int e = 0; e < cw; ++e) {
+            x1[e] *= ri * w1v[gi][e];
+            x2[e] *= ri * w2v[gi][e];
+          }
+        }
         float y1[cw], y2[cw];
 #pragma unroll
         for (int e = 0; e < cw; ++e) {
-          const float x1 = acc[mb][b1 + e][j] + b1v[gi][e];
-          const float x2 = acc[mb][b1 + cw + e][j] + b2v[gi][e];
           if (p < 2) {
-            y1[e] = x1 * cc[j][gi][e] - x2 * ss[j][gi][e];
-            y2[e] = x2 * cc[j][gi][e] + x1 * ss[j][gi][e];
+            y1[e] = x1[e] * cc[j][gi][e] - x2[e] * ss[j][gi][e];
+            y2[e] = x2[e] * cc[j][gi][e] + x1[e] * ss[j][gi][e];
           } else {
-            y1[e] = x1;
-            y2[e] = x2;
+            y1[e] = x1[e];
+            y2[e] = x2[e];
           }
         }
         T* dst = static_cast<T*>(a.out[p]) + ((bidx * a.nh[p] + hd) * a.S + s) * (long)a.d + jj;

@@ -38,7 +38,7 @@ int ok() {
 
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
-                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum"};
+                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum", "k_qk_norm_bwd"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -423,9 +423,17 @@ int rope_table(const lora_qkv_desc_t& d, const QkvWs& w, hipStream_t st) {
                 d.rope_theta);
 }
 
+// q/k norm: the weights and what the forward saves for the backward.
+struct NormIo {
+  const void* w[2];
+  float eps;
+  void* Pn;        // [N][Oq + Ok], call dtype
+  float* rinv;     // [N][n_q + n_kv]
+};
+
 template <class T>
 int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* const (&pr)[3], void* const (&out)[3],
-                 void* Tsv, const QkvWs& w, hipStream_t st) {
+                 void* Tsv, const QkvWs& w, hipStream_t st, const NormIo* nio = nullptr) {
   const long N = (long)d.batch * d.seq;
   const int h = d.hidden, r = d.rank, V = vecw(DT<T>::code);
   int rc = rope_table(d, w, st);
@@ -448,6 +456,13 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
   a.vecW = (h % V == 0) && wal;
   a.vecS = (h % V == 0) && aal;
   a.vecO = oal;
+  if (nio) {
+    a.norm = 1;
+    a.nw[0] = nio->w[0]; a.nw[1] = nio->w[1];
+    a.eps = nio->eps;
+    a.Pn = nio->Pn; a.rinv = nio->rinv;
+    a.vecN = al16(nio->Pn);
+  }
   a.R = (int)cdiv(N, kBM);
   a.NC = (int)cdiv(a.off[3], kBN);
   const bool fast = fast_ok(DT<T>::code, h, N, {X, pr[0]->W, pr[1]->W, pr[2]->W, pr[0]->A, pr[1]->A, pr[2]->A}) &&
@@ -476,7 +491,7 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
 template <class T>
 int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const void* X, const void* Tsv,
                  const lora_proj_t* const (&pr)[3], void* dX, void* const (&dA)[3], void* const (&dB)[3],
-                 const QkvWs& w, hipStream_t st) {
+                 const QkvWs& w, hipStream_t st, const NormIo* nio = nullptr) {
   const long N = (long)d.batch * d.seq;
   const int h = d.hidden, r = d.rank, V = vecw(DT<T>::code);
   const int R = (int)cdiv(N, kBM);
@@ -485,9 +500,30 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
   const int O = off[3];
   int rc = rope_table(d, w, st);
   if (rc) return rc;
+  if (nio) {
+    // dP through RoPE^T and the per-head norm, then the prologue reads it as a
+    // plain token-major upstream gradient over the three adapters.
+    NormBwdArgs a{};
+    for (int p = 0; p < 3; ++p) { a.src[p] = dO[p]; a.nh[p] = nh[p]; }
+    a.Pn = nio->Pn; a.rinv = nio->rinv;
+    a.nw[0] = nio->w[0]; a.nw[1] = nio->w[1];
+    a.cs = w.cs; a.sn = w.sn;
+    a.dP = w.dP;
+    a.N = N; a.S = d.seq; a.d = d.head_dim;
+    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+    constexpr int E = ET<T>::VEC;
+    const int tph = d.head_dim / 2 / E;
+    const dim3 blk(256);
+    const unsigned gy = (unsigned)(nh[0] + nh[1] + nh[2]);
+    if (tph == 4) rc = launch(10, k_qk_norm_bwd<T, 4>, dim3((unsigned)cdiv(N, 64), gy), blk, st, a);
+    else if (tph == 8) rc = launch(10, k_qk_norm_bwd<T, 8>, dim3((unsigned)cdiv(N, 32), gy), blk, st, a);
+    else rc = launch(10, k_qk_norm_bwd<T, 16>, dim3((unsigned)cdiv(N, 16), gy), blk, st, a);
+    if (rc) return rc;
+  }
   {
     ProArgs a{};
-    a.qkv = 1;
+    a.qkv = nio ? 0 : 1;
+    a.P = w.dP;
     bool sal = true, bal = true;
     for (int p = 0; p < 3; ++p) {
       a.src[p] = dO[p];
@@ -505,7 +541,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.dT_part = w.dT_part; a.dB_part = w.dB_part;
     a.N = N; a.O = O; a.r = r;
     a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
-    a.vecP = sal;
+    a.vecP = nio ? true : sal;
     a.vecB = (r % V == 0) && bal;
     rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
     if (rc) return rc;
@@ -635,6 +671,23 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
 // =============================================================================
 // C ABI
 // =============================================================================
+namespace {
+int check_norm(const lora_qkv_desc_t* desc, const lora_qk_norm_t* norm, const void* Pn, const float* rinv,
+               std::initializer_list<const void*> vec_ptrs, NormIo& nio) {
+  if (!norm || !norm->q_weight || !norm->k_weight || !Pn || !rinv)
+    return fail(LORA_ERR_NULL, "q/k norm weights, Pn or rinv is NULL");
+  if (!(norm->eps >= 0.f)) return fail(LORA_ERR_SHAPE, "norm eps must be >= 0");
+  for (const void* p : vec_ptrs)
+    if (!al16(p)) return fail(LORA_ERR_UNSUPPORTED, "the q/k norm path needs 16-byte aligned tensors");
+  (void)desc;
+  nio.w[0] = norm->q_weight; nio.w[1] = norm->k_weight;
+  nio.eps = norm->eps;
+  nio.Pn = const_cast<void*>(Pn);
+  nio.rinv = const_cast<float*>(rinv);
+  return LORA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass) {
@@ -746,6 +799,55 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
   void* const dB[3] = {dB_q, dB_k, dB_v};
   if (desc->dtype == LORA_BF16) return qkv_bwd_impl<bf16>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
   return qkv_bwd_impl<float>(*desc, dO, X, T, pr, dX, dA, dB, w, st);
+}
+
+int lora_qkv_norm_fwd(const lora_qkv_desc_t* desc, const void* X, const lora_proj_t* q, const lora_proj_t* k,
+                      const lora_proj_t* v, const lora_qk_norm_t* norm, void* Q, void* K, void* V, void* T, void* Pn,
+                      float* rinv, void* workspace, size_t workspace_bytes, void* hip_stream) {
+  int rc = check_qkv(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
+  if (!X || !Q || !K || !V || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  NormIo nio{};
+  if ((rc = check_norm(desc, norm, Pn, rinv, {norm ? norm->q_weight : nullptr, norm ? norm->k_weight : nullptr, Pn},
+                       nio)))
+    return rc;
+  const QkvWs probe = qkv_ws(*desc, 0, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const QkvWs w = qkv_ws(*desc, 0, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const lora_proj_t* const pr[3] = {q, k, v};
+  void* const out[3] = {Q, K, V};
+  if (desc->dtype == LORA_BF16) return qkv_fwd_impl<bf16>(*desc, X, pr, out, T, w, st, &nio);
+  return qkv_fwd_impl<float>(*desc, X, pr, out, T, w, st, &nio);
+}
+
+int lora_qkv_norm_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, const void* dV, const void* X,
+                      const void* T, const void* Pn, const float* rinv, const lora_proj_t* q, const lora_proj_t* k,
+                      const lora_proj_t* v, const lora_qk_norm_t* norm, void* dX, void* dA_q, void* dB_q,
+                      void* dA_k, void* dB_k, void* dA_v, void* dB_v, void* workspace, size_t workspace_bytes,
+                      void* hip_stream) {
+  int rc = check_qkv(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
+  if (!dQ || !dK || !dV || !X || !T || !dX || !dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v)
+    return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  NormIo nio{};
+  if ((rc = check_norm(desc, norm, Pn, rinv,
+                       {norm ? norm->q_weight : nullptr, norm ? norm->k_weight : nullptr, Pn, dQ, dK, dV}, nio)))
+    return rc;
+  const QkvWs probe = qkv_ws(*desc, 1, nullptr);
+  if (!workspace || workspace_bytes < probe.bytes)
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const QkvWs w = qkv_ws(*desc, 1, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const lora_proj_t* const pr[3] = {q, k, v};
+  const void* const dO[3] = {dQ, dK, dV};
+  void* const dA[3] = {dA_q, dA_k, dA_v};
+  void* const dB[3] = {dB_q, dB_k, dB_v};
+  if (desc->dtype == LORA_BF16) return qkv_bwd_impl<bf16>(*desc, dO, X, T, pr, dX, dA, dB, w, st, &nio);
+  return qkv_bwd_impl<float>(*desc, dO, X, T, pr, dX, dA, dB, w, st, &nio);
 }
 
 int lora_linear_fwd(const lora_linear_desc_t* desc, const void* X, const lora_proj_t* proj, void* Y, void* T,

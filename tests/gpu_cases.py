@@ -59,6 +59,11 @@ QKV_CASES = [
     S.QKVConfig("qkv_bf16_bias_c4heads", 2, 300, 896, 14, 2, 64, 16, 2.0, 1.0e6, "bf16", bias=True),
     S.QKVConfig("qkv_bf16_bias_d128", 1, 260, 256, 4, 2, 128, 8, 2.0, 1.0e4, "bf16", bias=True),
     S.QKVConfig("qkv_f32_bias_d64", 2, 50, 128, 4, 2, 64, 4, 1.5, 1.0e4, "f32", bias=True),
+    S.QKVConfig("qkv_bf16_norm_d128", 2, 260, 256, 4, 2, 128, 8, 2.0, 1.0e6, "bf16", qk_norm=True),
+    S.QKVConfig("qkv_bf16_norm_bias_d64_odd", 1, 300, 384, 7, 1, 64, 16, 2.0, 1.0e4, "bf16", bias=True,
+                qk_norm=True),
+    S.QKVConfig("qkv_f32_norm_d64", 2, 70, 128, 4, 2, 64, 4, 1.5, 1.0e4, "f32", qk_norm=True, norm_eps=1e-5),
+    S.QKVConfig("qkv_f32_norm_d128", 1, 40, 64, 2, 2, 128, 16, 2.0, 1.0e4, "f32", qk_norm=True, norm_eps=0.5),
 ]
 
 
@@ -117,13 +122,17 @@ def run_qkv_gpu(cfg: S.QKVConfig, t_cpu, grads_cpu=None, scales=None):
     dev = torch.device("cuda:0")
     t = {k: v.to(dev).contiguous() for k, v in t_cpu.items() if k not in ("dQ", "dK", "dV")}
     m = B.QKV(t, cfg.batch, cfg.seq, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.rank, cfg.dtype, cfg.theta,
-              scales)
+              scales, cfg.norm_eps)
     m.forward()
     gc = grads_cpu if grads_cpu is not None else t_cpu
     m.backward(gc["dQ"].to(dev).contiguous(), gc["dK"].to(dev).contiguous(), gc["dV"].to(dev).contiguous())
     torch.cuda.synchronize()
     out = {"Q": to64(m.Q), "K": to64(m.K), "V": to64(m.V), "T_q": to64(m.T[0]), "T_k": to64(m.T[1]),
            "T_v": to64(m.T[2]), "dX": to64(m.dX)}
+    if m.norm is not None:
+        Oq = cfg.n_q * cfg.head_dim
+        out.update({"P_q": to64(m.Pn[:, :Oq]), "P_k": to64(m.Pn[:, Oq:]), "rinv_q": to64(m.rinv[:, :cfg.n_q]),
+                    "rinv_k": to64(m.rinv[:, cfg.n_q:])})
     out.update({k: to64(v) for k, v in m.grads.items()})
     return out
 
@@ -134,10 +143,13 @@ def run_qkv_oracle(cfg: S.QKVConfig, t_cpu, grads_cpu=None, scales=None):
     gc = grads_cpu if grads_cpu is not None else t_cpu
     dQ, dK, dV = (gc[k].to(torch.float64).numpy() for k in ("dQ", "dK", "dV"))
     shape = dict(batch=cfg.batch, seq=cfg.seq, n_q=cfg.n_q, n_kv=cfg.n_kv, head_dim=cfg.head_dim, theta=cfg.theta)
-    f = orc.qkv_fwd(p, scales=scales, **shape)
-    g = orc.qkv_bwd(p, dQ, dK, dV, scales=scales, **shape)
+    f = orc.qkv_fwd(p, scales=scales, norm_eps=cfg.norm_eps, **shape)
+    g = orc.qkv_bwd(p, dQ, dK, dV, scales=scales, norm_eps=cfg.norm_eps, **shape)
     ref = {"Q": f["Q"], "K": f["K"], "V": f["V"], "T_q": f["T_q"], "T_k": f["T_k"], "T_v": f["T_v"],
            "dX": g["dX"]}
+    for k in ("P_q", "P_k", "rinv_q", "rinv_k"):
+        if k in f:
+            ref[k] = f[k]
     for n in "qkv":
         ref["dA_" + n] = g["dA_" + n]
         ref["dB_" + n] = g["dB_" + n]

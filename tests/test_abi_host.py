@@ -159,7 +159,26 @@ def test_linear_validation_codes():
     assert lib.lora_linear_fwd(ctypes.byref(_lin()), FAKE, ctypes.byref(pr), FAKE, FAKE, None, 0, None) == 1
 
 
+def test_qkv_norm_validation_codes():
+    lib = B.lib()
+    pr = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0)
+    f = FAKE
+    ws = B.lora_qkv_workspace_bytes(_qkv(), 0)
+
+    def fwd(norm, Pn=FAKE, rinv=FAKE):
+        return lib.lora_qkv_norm_fwd(ctypes.byref(_qkv()), f, ctypes.byref(pr), ctypes.byref(pr), ctypes.byref(pr),
+                                     ctypes.byref(norm) if norm is not None else None, f, f, f, f, Pn, rinv, f, ws,
+                                     None)
+    assert fwd(None) == 1
+    assert fwd(B.QkNorm(None, FAKE.value, 1e-6)) == 1
+    assert fwd(B.QkNorm(FAKE.value, FAKE.value, 1e-6), Pn=None) == 1
+    assert fwd(B.QkNorm(FAKE.value, FAKE.value, -1.0)) == 2
+    assert fwd(B.QkNorm(FAKE.value, 0x1002, 1e-6)) == 3          # misaligned weight
+    assert b"aligned" in lib.lora_last_error_message()
+
+
 def test_kernel_names_listed():
     names = B.kernel_names()
-    for k in ("k_gateup_fwd", "k_linear_fwd", "k_qkv_fwd", "k_down_bwd", "k_mlp_dx_bwd", "k_proj_dx_bwd"):
+    for k in ("k_gateup_fwd", "k_linear_fwd", "k_qkv_fwd", "k_down_bwd", "k_mlp_dx_bwd", "k_proj_dx_bwd",
+              "k_qk_norm_bwd"):
         assert k in names

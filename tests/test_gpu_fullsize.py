@@ -76,15 +76,19 @@ def test_mlp_full_size_deterministic():
 def qkv_batch_view(cfg: S.QKVConfig, out: dict, b: int) -> dict:
     s0, s1 = b * cfg.seq, (b + 1) * cfg.seq
     v = {k: out[k][b:b + 1] for k in ("Q", "K", "V")}
-    for k in ("T_q", "T_k", "T_v", "dX"):
-        v[k] = out[k][s0:s1]
+    for k in ("T_q", "T_k", "T_v", "dX", "P_q", "P_k", "rinv_q", "rinv_k"):
+        if k in out:
+            v[k] = out[k][s0:s1]
     for p in "qkv":
         v["dA_" + p] = out["dA_" + p]
         v["dB_" + p] = out["dB_" + p]
     return v
 
 
-@pytest.mark.parametrize("cfg", [S.C1], ids=lambda c: c.name)
+C1_NORM = dataclasses.replace(S.C1, name="qkv_rope_qknorm_h4096_gqa32x8_d128_bf16", qk_norm=True)
+
+
+@pytest.mark.parametrize("cfg", [S.C1, C1_NORM], ids=lambda c: c.name)
 def test_qkv_full_size_one_sequence(cfg):
     b = cfg.batch - 1
     gc.say(f"full-size qkv {cfg.name}: generating inputs")
@@ -97,8 +101,7 @@ def test_qkv_full_size_one_sequence(cfg):
     gc.say(f"full-size qkv {cfg.name}: GPU")
     out = gc.run_qkv_gpu(cfg, t, grads_cpu=grads)
     gc.say(f"full-size qkv {cfg.name}: oracle on sequence {b}")
-    one = S.QKVConfig(cfg.name + "_seq", 1, cfg.seq, cfg.hidden, cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.rank,
-                      cfg.scale, cfg.theta, cfg.dtype)
+    one = dataclasses.replace(cfg, name=cfg.name + "_seq", batch=1)
     s0, s1 = b * cfg.seq, (b + 1) * cfg.seq
     t1 = {k: v for k, v in t.items() if k not in ("X", "dQ", "dK", "dV")}
     t1["X"] = t["X"][s0:s1]
