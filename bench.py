@@ -7,8 +7,9 @@ inputs resident in HBM.  Throughput is algorithmic FLOPs (frozen base weights:
 no dW; elementwise work not counted) per second.
 
 Prints one JSON line.  Besides the headline value it carries
-  oproj:         a separate leg, outside `value`: one LoRA linear fwd+bwd at
-                 the attention output projection's shape (8192 x 4096 -> 4096);
+  legs:          separate legs, outside `value`: one LoRA linear fwd+bwd at
+                 the attention output projection's shape (8192 x 4096 -> 4096)
+                 and the headline QKV shape with per-head q/k RMSNorm;
   roofline:      the dominant kernel's achieved TFLOP/s against the bf16
                  dense MFMA peak, timed live with HIP events around each launch
                  on the stream it runs on;
@@ -18,6 +19,7 @@ Prints one JSON line.  Besides the headline value it carries
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -53,8 +55,37 @@ def linear_kernel_flops(cfg):
             "k_proj_dx_bwd": 2 * N * o * k + 4 * N * r * k}
 
 
+def time_leg(step, steps: int, warmup: int, kflops=None):
+    """Warm up, then time `steps` calls of `step` with HIP events on the
+    current stream; per-kernel averages from the library's launch events."""
+    import torch
+    from lora_fine_tuning_mlp_amd import binding as B
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    B.timing_reset()
+    B.timing_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    B.timing_enable(False)
+    kernels = {}
+    for name in B.kernel_names():
+        tot, n = B.timing_query(name)
+        if n:
+            kernels[name] = {"avg_us": round(1e3 * tot / n, 2), "launches_per_step": n // steps}
+            if kflops and name in kflops:
+                kernels[name]["tflops"] = round(kflops[name] / (1e-3 * tot / n) / 1e12, 1)
+    return e0.elapsed_time(e1) / steps, kernels
+
+
 def bench_linear(cfg, steps: int, warmup: int):
-    """Time one LoRA linear (fwd+bwd) on its own, after the headline step: the
+    """One LoRA linear (fwd+bwd) on its own, after the headline step: the
     attention output projection of the same model.  Not part of `value`."""
     import torch
     from lora_fine_tuning_mlp_amd import binding as B
@@ -70,31 +101,132 @@ def bench_linear(cfg, steps: int, warmup: int):
         lin.forward()
         lin.backward(dY)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    B.timing_reset()
-    B.timing_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    B.timing_enable(False)
-    ms = e0.elapsed_time(e1) / steps
-    kf = linear_kernel_flops(cfg)
-    kernels = {}
-    for name in B.kernel_names():
-        tot, n = B.timing_query(name)
-        if n:
-            kernels[name] = {"avg_us": round(1e3 * tot / n, 2)}
-            if name in kf:
-                kernels[name]["tflops"] = round(kf[name] / (1e-3 * tot / n) / 1e12, 1)
+    ms, kernels = time_leg(step, steps, warmup, linear_kernel_flops(cfg))
     return {"workload": cfg.name, "tokens": cfg.n_tokens, "in": cfg.in_features, "out": cfg.out_features,
             "rank": cfg.rank, "ms_per_step": round(ms, 4), "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
             "kernels": kernels}
+
+
+def bench_qkv(cfg, steps: int, warmup: int):
+    """LoRA QKV fwd+bwd at `cfg` (used for the q/k-norm variant of the
+    headline QKV shape).  Not part of `value`."""
+    import torch
+    from lora_fine_tuning_mlp_amd import binding as B
+    from lora_fine_tuning_mlp_amd import synthetic as S
+
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev) for k, v in S.qkv_inputs(cfg, 0).items()}
+    m = B.QKV({k: v for k, v in t.items() if k not in ("dQ", "dK", "dV")}, cfg.batch, cfg.seq, cfg.hidden, cfg.n_q,
+              cfg.n_kv, cfg.head_dim, cfg.rank, cfg.dtype, cfg.theta, (cfg.scale,) * 3, cfg.norm_eps)
+    dQ, dK, dV = t["dQ"], t["dK"], t["dV"]
+
+    def step():
+        m.forward()
+        m.backward(dQ, dK, dV)
+
+    ms, kernels = time_leg(step, steps, warmup)
+    return {"workload": cfg.name, "qk_norm": cfg.qk_norm, "bias": cfg.bias, "ms_per_step": round(ms, 4),
+            "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
+
+
+def _unfused_mlp(t, act: str, s: float):
+    """The same LoRA MLP as separate torch ops (hipBLASLt GEMMs + elementwise
+    kernels, autograd for the backward, W frozen): what a caller runs when
+    the fused call is skipped."""
+    import torch
+    import torch.nn.functional as F
+
+    phi = {"swiglu": F.silu, "geglu_tanh": lambda g: F.gelu(g, approximate="tanh"), "geglu_erf": F.gelu}[act]
+    X = t["X"].detach().requires_grad_(True)
+    ad = {k: t[k].detach().requires_grad_(True) for k in t if k[0] in "AB" and "_" in k}
+
+    def lin(Z, n):
+        return F.linear(Z, t["W_" + n]) + s * F.linear(F.linear(Z, ad["A_" + n]), ad["B_" + n])
+
+    def step():
+        Y = lin(phi(lin(X, "gate")) * lin(X, "up"), "down")
+        Y.backward(t["dY"])
+        return Y
+    return step
+
+
+def _unfused_qkv(t, cfg):
+    """LoRA QKV + head split + RoPE as separate torch ops with autograd."""
+    import math
+    import torch
+    import torch.nn.functional as F
+
+    B, S, d = cfg.batch, cfg.seq, cfg.head_dim
+    dev = t["X"].device
+    j = torch.arange(d // 2, device=dev, dtype=torch.float64)
+    ang = torch.arange(S, device=dev, dtype=torch.float64)[:, None] * torch.exp(-(2.0 * j / d) * math.log(cfg.theta))
+    cos, sin = ang.cos().to(t["X"].dtype), ang.sin().to(t["X"].dtype)
+    X = t["X"].detach().requires_grad_(True)
+    ad = {k: t[k].detach().requires_grad_(True) for k in t if k[:2] in ("A_", "B_")}
+
+    def proj(n, heads):
+        P = F.linear(X, t["W_" + n]) + cfg.scale * F.linear(F.linear(X, ad["A_" + n]), ad["B_" + n])
+        return P.view(B, S, heads, d).transpose(1, 2)
+
+    def rope(Z):
+        x1, x2 = Z[..., : d // 2], Z[..., d // 2:]
+        return torch.cat([x1 * cos - x2 * sin, x2 * cos + x1 * sin], dim=-1)
+
+    def step():
+        Q, K, V = rope(proj("q", cfg.n_q)), rope(proj("k", cfg.n_kv)), proj("v", cfg.n_kv)
+        torch.autograd.backward([Q, K, V], [t["dQ"], t["dK"], t["dV"]])
+    return step
+
+
+def crossover(steps: int, warmup: int):
+    """Fused calls against the unfused torch sequence over a ladder of token
+    counts at two model widths: where does fusion start to pay?"""
+    import torch
+    from lora_fine_tuning_mlp_amd import binding as B
+    from lora_fine_tuning_mlp_amd import synthetic as S
+
+    dev = torch.device("cuda:0")
+
+    def event_ms(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    rows = []
+    for base, tokens in ((S.C4_MLP, (16, 64, 256, 1024, 4096)), (S.C2, (64, 256, 1024, 4096, 8192))):
+        for n in tokens:
+            cfg = dataclasses.replace(base, name=f"{base.name}_n{n}", n_tokens=n)
+            t = {k: v.to(dev) for k, v in S.mlp_inputs(cfg, 0).items()}
+            m = B.MLP({k: v for k, v in t.items() if k != "dY"}, n, cfg.hidden, cfg.inter, cfg.rank, cfg.dtype,
+                      cfg.act, (cfg.scale,) * 3)
+            fused = event_ms(lambda: (m.forward(), m.backward(t["dY"])))
+            unfused = event_ms(_unfused_mlp(t, cfg.act, cfg.scale))
+            rows.append({"op": "mlp", "hidden": cfg.hidden, "inter": cfg.inter, "tokens": n,
+                         "fused_ms": round(fused, 4), "unfused_ms": round(unfused, 4),
+                         "speedup": round(unfused / fused, 3)})
+            print(f"[crossover] {rows[-1]}", file=sys.stderr, flush=True)
+            del m, t
+    for base, seqs in ((S.C4_QKV, (4, 16, 64, 256, 1024)), (S.C1, (16, 64, 256, 1024, 2048))):
+        for sq in seqs:
+            cfg = dataclasses.replace(base, name=f"{base.name}_s{sq}", seq=sq)
+            t = {k: v.to(dev) for k, v in S.qkv_inputs(cfg, 0).items()}
+            m = B.QKV({k: v for k, v in t.items() if k not in ("dQ", "dK", "dV")}, cfg.batch, sq, cfg.hidden,
+                      cfg.n_q, cfg.n_kv, cfg.head_dim, cfg.rank, cfg.dtype, cfg.theta, (cfg.scale,) * 3)
+            fused = event_ms(lambda: (m.forward(), m.backward(t["dQ"], t["dK"], t["dV"])))
+            unfused = event_ms(_unfused_qkv(t, cfg))
+            rows.append({"op": "qkv", "hidden": cfg.hidden, "heads": f"{cfg.n_q}/{cfg.n_kv}x{cfg.head_dim}",
+                         "tokens": cfg.n_tokens, "fused_ms": round(fused, 4), "unfused_ms": round(unfused, 4),
+                         "speedup": round(unfused / fused, 3)})
+            print(f"[crossover] {rows[-1]}", file=sys.stderr, flush=True)
+            del m, t
+    return rows
 
 
 def stored_traffic(kernel: str):
@@ -166,9 +298,12 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the CPU oracle baseline")
     ap.add_argument("--cpu-reps", type=int, default=2, help="repetitions of the CPU oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-oproj", action="store_true", help="skip the separate o_proj LoRA linear leg")
+    ap.add_argument("--no-legs", action="store_true",
+                    help="skip the separate o_proj linear and q/k-norm QKV legs (outside the headline value)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this size (calibrates rocprofv3 byte counters)")
+    ap.add_argument("--crossover", action="store_true",
+                    help="instead of the headline step: fused vs unfused (torch) timings over token counts")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -185,6 +320,11 @@ def main():
     qkv_cfg, mlp_cfg = S.C1, S.C2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.crossover:
+        rows = crossover(max(3, args.steps), max(2, args.warmup))
+        print(json.dumps({"crossover": rows, "unit": "ms per fwd+bwd", "dtype": "bf16", "data": "synthetic"}),
+              flush=True)
+        return
     print(f"[bench] generating inputs ({qkv_cfg.name}, {mlp_cfg.name})", file=sys.stderr, flush=True)
     tq = {k: v.to(dev) for k, v in S.qkv_inputs(qkv_cfg, 0).items()}
     tm = {k: v.to(dev) for k, v in S.mlp_inputs(mlp_cfg, 0).items()}
@@ -243,7 +383,13 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dominant,
                 "flops_per_launch": kf[dominant], "avg_launch_us": round(per_kernel[dominant]["avg_us"], 2)}
 
-    oproj = None if args.no_oproj else bench_linear(S.C_OPROJ, max(1, args.steps // 2), max(1, args.warmup))
+    legs = None
+    if not args.no_legs:
+        print("[bench] separate legs: o_proj linear, q/k-norm QKV", file=sys.stderr, flush=True)
+        ls, lw = max(1, args.steps // 2), max(1, args.warmup)
+        legs = {"oproj": bench_linear(S.C_OPROJ, ls, lw),
+                "qkv_qknorm": bench_qkv(dataclasses.replace(qkv_cfg, name=qkv_cfg.name + "_qknorm", qk_norm=True),
+                                        ls, lw)}
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -265,7 +411,7 @@ def main():
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per_kernel.items()},
-        "oproj": oproj,
+        "legs": legs,
     }
     if not args.no_cpu_baseline:
         print(f"[bench] cpu oracle on {args.cpu_tokens} tokens", file=sys.stderr, flush=True)
