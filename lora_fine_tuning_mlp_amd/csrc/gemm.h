@@ -403,6 +403,123 @@ __device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<N
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward fast path (bf16, weights stored [K][N]): K tiles of 64, two
+// stages.  The A rows (tokens) take the forward's 128-byte layout, so every
+// direct load requests whole cache lines; the [K][N] tile is 64 rows of 512
+// bytes in the transpose-read layout (kn_off; its swizzle repeats every 16
+// rows) and the optional side tile ([K][r], r = 16) is 64 rows of 32 bytes.
+// ---------------------------------------------------------------------------
+constexpr int kStage2TrB = 64 * 512;                                  // 32768
+constexpr int kStage2TrS = 64 * 32;                                   // 2048
+constexpr int kStage2Tr = kStage2A + kStage2TrB + kStage2TrS;         // 67584
+static_assert(2 * kStage2Tr <= kGemmLds, "two transpose-read stages");
+
+// A: rows of [A0 | A1] split along K at K0 (K0 % 64 == 0); B: krow(k) -> row k
+// of the [K][N] matrix, columns n0 .. n0+255 (clamped to the last chunk, never
+// stored); side: srow(0, k) -> the 16 ranks of row k.  Every K tile full, N %
+// 8 == 0, 16-byte aligned rows, 32-bit A offsets.
+template <class KRow, class SRow, int NSIDE>
+struct KNPairLoader {
+  static_assert(NSIDE <= 1, "one direct side block");
+  static constexpr int kLoads = 8 + (NSIDE > 0 ? 1 : 0);
+  const bf16* A0;
+  const bf16* A1;
+  long K0;
+  int aoff[4];
+  KRow krow;
+  SRow srow;
+  long n0, N;
+  __device__ __forceinline__ void init_a(const bf16* a0, const bf16* a1, long k0, long lda, long M, long m0) {
+    A0 = a0;
+    A1 = a1 ? a1 : a0;
+    K0 = a1 ? k0 : (1L << 40);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      long row = m0 + direct2_row(it);
+      if (row > M - 1) row = M - 1;
+      aoff[it] = (int)(row * lda);
+    }
+  }
+  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
+    const int L = threadIdx.x & 63;
+    const long k = (long)kt * 64;
+    const bf16* ab = A0;
+    long ka = k;
+    if (ka >= K0) { ab = A1; ka -= K0; }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(ab + aoff[it] + ka + direct2_chunk(L) * 8, As + direct_blk(it) * 1024);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {              // block = 2 k rows of 512 bytes
+      const int blk = direct_blk(it);
+      const int row = 2 * blk + (L >> 5);
+      const int lseg = (L & 31) ^ ftr(row);
+      const long col = min(n0 + lseg * 8, N - 8);
+      g2lds16(krow(k + row) + col, Bs + blk * 1024);
+    }
+    if constexpr (NSIDE > 0) {
+      if (L < 16) {                               // 128 chunks of 16 bytes: rows ci / 2
+        const int w = threadIdx.x >> 6, ci = 16 * w + L;
+        g2lds16(srow(0, k + (ci >> 1)) + 8 * (ci & 1), Bs + kStage2TrB + 256 * w);
+      }
+    }
+  }
+};
+
+template <int NSIDE, class Loader>
+__device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, f32x4 (&acc)[kMB][8],
+                                         f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
+  constexpr int L = Loader::kLoads;
+  const WaveId q = wave_id();
+  if (nkt <= kt0) return;
+  auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage2Tr; };
+  ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
+  sync_tiles<L>(0);
+  for (int kt = kt0; kt < nkt; ++kt) {
+    const char* As = stage(kt);
+    const char* Bs = As + kStage2A;
+    if (kt + 1 < nkt) {
+      char* An = stage(kt + 1);
+      ld.issue(kt + 1, An, An + kStage2A);
+    }
+#pragma nounroll
+    for (int ks = 0; ks < 2; ++ks) {
+      Frag<bf16> af[kMB];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag2(As, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
+      const char* Bk = Bs + ks * 32 * 512;
+      u32x2 lo[8], hi[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) tr_issue(Bk, nb, q, lo[nb], hi[nb]);
+      lgkm_tie<8>(lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb) {
+        const Frag<bf16> bfr = tr_make(lo[nb], hi[nb]);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      }
+      lgkm_tie<0>(lo[4], hi[4], lo[5], hi[5], lo[6], hi[6], lo[7], hi[7]);
+#pragma unroll
+      for (int nb = 4; nb < 8; ++nb) {
+        const Frag<bf16> bfr = tr_make(lo[nb], hi[nb]);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      }
+      if constexpr (NSIDE > 0) {
+        if (ks == q.wn) {
+          u32x2 slo, shi;
+          tr_side_issue(Bs + kStage2TrB + ks * 1024, q, slo, shi);
+          lgkm_tie0(slo, shi);
+          const Frag<bf16> bfr = tr_make(slo, shi);
+#pragma unroll
+          for (int mb = 0; mb < kMB; ++mb) sacc[0][mb] = mma(sacc[0][mb], af[mb], bfr);
+        }
+      }
+    }
+    sync_tiles<L>(0);
+  }
+}
+
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[kMB][8]) {
 #pragma unroll
   for (int i = 0; i < kMB; ++i)

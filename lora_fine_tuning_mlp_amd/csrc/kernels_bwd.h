@@ -433,9 +433,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
-  if constexpr (TR) {
-    using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-    KNTrLoader<AOp, KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
+  if constexpr (FAST) {
+    static_assert(TR, "the fast path is bf16");
+    KNPairLoader<KRow1<bf16>, SRowNone<bf16>, 0> ld;      // h % 64 == 0
+    ld.init_a(dY, nullptr, h, h, a.N, m0);
+    ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
+    ld.n0 = n0; ld.N = ni;
+    kloop2tr<0>(smem, (int)(h / 64), ld, acc, sacc);
+  } else if constexpr (TR) {
+    KNTrLoader<RowsA<T>, KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
     ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
     ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
     ld.n0 = n0; ld.N = ni; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;
@@ -694,18 +700,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   zero_acc(acc);
   const int nkt = (int)((2 * ni + BK - 1) / BK);
   if constexpr (FAST) {
-    // bf16, i % BK == 0, r == 16: the dG tiles carry only dT_g, the dU tiles
+    // bf16, i % 64 == 0, r == 16: the dG tiles carry only dT_g, the dU tiles
     // only dT_u.  Two K-loop phases with one side accumulator; dT_g parks in
     // the flush slot.
-    KNTrLoader<DirectA<T>, KRow2<T>, SRowLin<T>, SMaskOne, 1> ld;
-    ld.a.init(dG, dU, ni, ni, ni, a.N, m0, a.vecA);
+    KNPairLoader<KRow2<bf16>, SRowLin<bf16>, 1> ld;
+    ld.init_a(dG, dU, ni, ni, a.N, m0);
     ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
     ld.srow.B = Bg; ld.srow.kb = 0; ld.srow.ld = r;          // phase 1: B_g rows
-    ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = a.vecS;
+    ld.n0 = n0; ld.N = h;
     f32x4 sacc[1][kMB];
     zero_side(sacc);
-    const int nk0 = (int)(ni / BK);
-    kloop<T, 1>(smem, nk0, ld, acc, sacc);
+    const int nk0 = (int)(ni / 64), nk2 = 2 * nk0;
+    kloop2tr<1>(smem, nk0, ld, acc, sacc);
     {
       const WaveId q = wave_id();
       float* fl = reinterpret_cast<float*>(smem + kFlushOff);
@@ -724,7 +730,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     zero_side(sacc);
     ld.srow.B = Bu;                                  // phase 2: B_u rows
     ld.srow.kb = ni;
-    kloop<T, 1>(smem, nkt, ld, acc, sacc, nk0);
+    kloop2tr<1>(smem, nk2, ld, acc, sacc, nk0);
     side_reduce<T, 1>(smem, sacc, 1);                // dT_u -> slot 1
     {
       float* Ts = ts_ptr(smem);
@@ -814,9 +820,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_proj_dx_bwd(ProjDxArgs a) {
   f32x4 sacc[1][kMB];
   zero_acc(acc);
   const int nkt = (a.O + ET<T>::BK - 1) / ET<T>::BK;
-  if constexpr (TR) {
-    using AOp = typename std::conditional<FAST, DirectA<T>, RowsA<T>>::type;
-    KNTrLoader<AOp, KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
+  if constexpr (FAST) {
+    static_assert(TR, "the fast path is bf16");
+    KNPairLoader<KRow3<bf16>, SRowNone<bf16>, 0> ld;      // O % 64 == 0
+    ld.init_a(dP, nullptr, a.O, a.O, a.N, m0);
+    ld.krow = kr;
+    ld.n0 = n0; ld.N = h;
+    kloop2tr<0>(smem, a.O / 64, ld, acc, sacc);
+  } else if constexpr (TR) {
+    KNTrLoader<RowsA<T>, KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
     ld.a.init(dP, nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
     ld.krow = kr;
     ld.n0 = n0; ld.N = h; ld.vecB = a.vecW; ld.r = a.r; ld.vecS = false;

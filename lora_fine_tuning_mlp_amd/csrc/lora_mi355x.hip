@@ -369,7 +369,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecW = (i % V == 0) && al16(dn.W);
     a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
     a.R = R; a.NC = (int)cdiv(i, kBN);
-    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0;
+    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0 && h % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -385,7 +385,8 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16;
+    const bool fast =
+        fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 && i % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
                                     dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -565,7 +566,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
     a.vecW = (h % V == 0) && wal;
     a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0;
+    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0 && O % 64 == 0;
     rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 3>), (k_proj_dx_bwd<T, false, 3>), dim3(a.R * a.NC),
                           dim3(kGemmThreads), st, a);
     if (rc) return rc;
@@ -648,7 +649,7 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
     a.vecW = (in % V == 0) && al16(p.W);
     a.vecO = (in % 8 == 0) && al16(dX) && al16(X);
     a.R = R; a.NC = (int)cdiv(in, kBN);
-    const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0;
+    const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0 && out % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 1>), (k_proj_dx_bwd<T, false, 1>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
