@@ -416,9 +416,12 @@ constexpr int kStage2Tr = kStage2A + kStage2TrB + kStage2TrS;         // 67584
 static_assert(2 * kStage2Tr <= kGemmLds, "two transpose-read stages");
 
 // A: rows of [A0 | A1] split along K at K0 (K0 % 64 == 0); B: krow(k) -> row k
-// of the [K][N] matrix, columns n0 .. n0+255 (clamped to the last chunk, never
-// stored); side: srow(0, k) -> the 16 ranks of row k.  Every K tile full, N %
-// 8 == 0, 16-byte aligned rows, 32-bit A offsets.
+// of the [K][N] matrix (row stride ldb), columns n0 .. n0+255 (clamped to the
+// last chunk, never stored); side: srow(0, k) -> the 16 ranks of row k (row
+// stride lds).  Every K tile full and inside one segment of krow / srow, N %
+// 8 == 0, 16-byte aligned rows, 32-bit offsets.  Row pointers are resolved
+// once per tile from the (uniform) tile start; each lane keeps only 32-bit
+// offsets, so the loader's state stays small across the K-loop.
 template <class KRow, class SRow, int NSIDE>
 struct KNPairLoader {
   static_assert(NSIDE <= 1, "one direct side block");
@@ -426,11 +429,12 @@ struct KNPairLoader {
   const bf16* A0;
   const bf16* A1;
   long K0;
-  int aoff[4];
+  int aoff[4], boff[4], soff;
   KRow krow;
   SRow srow;
-  long n0, N;
-  __device__ __forceinline__ void init_a(const bf16* a0, const bf16* a1, long k0, long lda, long M, long m0) {
+  __device__ __forceinline__ void init(const bf16* a0, const bf16* a1, long k0, long lda, long M, long m0, long ldb,
+                                       long n0, long N, long lds) {
+    const int L = threadIdx.x & 63, w = threadIdx.x >> 6;
     A0 = a0;
     A1 = a1 ? a1 : a0;
     K0 = a1 ? k0 : (1L << 40);
@@ -438,34 +442,32 @@ struct KNPairLoader {
     for (int it = 0; it < 4; ++it) {
       long row = m0 + direct2_row(it);
       if (row > M - 1) row = M - 1;
-      aoff[it] = (int)(row * lda);
+      aoff[it] = (int)(row * lda) + direct2_chunk(L) * 8;
     }
-  }
-  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
-    const int L = threadIdx.x & 63;
-    const long k = (long)kt * 64;
-    const bf16* ab = A0;
-    long ka = k;
-    if (ka >= K0) { ab = A1; ka -= K0; }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) g2lds16(ab + aoff[it] + ka + direct2_chunk(L) * 8, As + direct_blk(it) * 1024);
 #pragma unroll
     for (int it = 0; it < 4; ++it) {              // block = 2 k rows of 512 bytes
-      const int blk = direct_blk(it);
-      const int row = 2 * blk + (L >> 5);
+      const int row = 2 * direct_blk(it) + (L >> 5);
       const int lseg = (L & 31) ^ ftr(row);
-      const long col = min(n0 + lseg * 8, N - 8);
-      g2lds16(krow(k + row) + col, Bs + blk * 1024);
+      boff[it] = (int)(row * ldb + min(n0 + lseg * 8, N - 8));
     }
+    const int ci = 16 * w + L;                    // side chunk (lanes < 16): row ci / 2
+    soff = (int)((ci >> 1) * lds) + 8 * (ci & 1);
+  }
+  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
+    const long k = (long)kt * 64;
+    const bf16* ab = (k >= K0) ? A1 + (k - K0) : A0 + k;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(ab + aoff[it], As + direct_blk(it) * 1024);
+    const bf16* bb = krow(k);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(bb + boff[it], Bs + direct_blk(it) * 1024);
     if constexpr (NSIDE > 0) {
-      if (L < 16) {                               // 128 chunks of 16 bytes: rows ci / 2
-        const int w = threadIdx.x >> 6, ci = 16 * w + L;
-        g2lds16(srow(0, k + (ci >> 1)) + 8 * (ci & 1), Bs + kStage2TrB + 256 * w);
-      }
+      if ((threadIdx.x & 63) < 16) g2lds16(srow(0, k) + soff, Bs + kStage2TrB + 256 * (threadIdx.x >> 6));
     }
   }
 };
 
+// Tile kt + 1 is issued at the top of iteration kt and has landed by its end.
 template <int NSIDE, class Loader>
 __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, f32x4 (&acc)[kMB][8],
                                          f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
@@ -482,7 +484,7 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
       char* An = stage(kt + 1);
       ld.issue(kt + 1, An, An + kStage2A);
     }
-#pragma nounroll
+#pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       Frag<bf16> af[kMB];
 #pragma unroll

@@ -436,9 +436,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   if constexpr (FAST) {
     static_assert(TR, "the fast path is bf16");
     KNPairLoader<KRow1<bf16>, SRowNone<bf16>, 0> ld;      // h % 64 == 0
-    ld.init_a(dY, nullptr, h, h, a.N, m0);
     ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
-    ld.n0 = n0; ld.N = ni;
+    ld.init(dY, nullptr, h, h, a.N, m0, ni, n0, ni, 0);
     kloop2tr<0>(smem, (int)(h / 64), ld, acc, sacc);
   } else if constexpr (TR) {
     KNTrLoader<RowsA<T>, KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
@@ -704,10 +703,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     // only dT_u.  Two K-loop phases with one side accumulator; dT_g parks in
     // the flush slot.
     KNPairLoader<KRow2<bf16>, SRowLin<bf16>, 1> ld;
-    ld.init_a(dG, dU, ni, ni, a.N, m0);
     ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
     ld.srow.B = Bg; ld.srow.kb = 0; ld.srow.ld = r;          // phase 1: B_g rows
-    ld.n0 = n0; ld.N = h;
+    ld.init(dG, dU, ni, ni, a.N, m0, h, n0, h, r);
     f32x4 sacc[1][kMB];
     zero_side(sacc);
     const int nk0 = (int)(ni / 64), nk2 = 2 * nk0;
@@ -823,9 +821,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_proj_dx_bwd(ProjDxArgs a) {
   if constexpr (FAST) {
     static_assert(TR, "the fast path is bf16");
     KNPairLoader<KRow3<bf16>, SRowNone<bf16>, 0> ld;      // O % 64 == 0
-    ld.init_a(dP, nullptr, a.O, a.O, a.N, m0);
     ld.krow = kr;
-    ld.n0 = n0; ld.N = h;
+    ld.init(dP, nullptr, a.O, a.O, a.N, m0, h, n0, h, 0);
     kloop2tr<0>(smem, a.O / 64, ld, acc, sacc);
   } else if constexpr (TR) {
     KNTrLoader<RowsA<T>, KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
