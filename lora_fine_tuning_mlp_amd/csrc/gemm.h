@@ -163,6 +163,25 @@ __device__ __forceinline__ Frag<bf16> tr_make(u32x2 lo, u32x2 hi) {
   return f;
 }
 
+// Fragment reads issued as inline asm like the transpose reads: the compiler
+// then tracks no LDS read of the K-loop itself and cannot fall back to
+// lgkmcnt(0) before the first MFMA; each fragment is made valid by an
+// explicit wait that names it (at most N of this wave's LDS reads still
+// outstanding; they complete in issue order).
+__device__ __forceinline__ u32x4 rd128(const char* p) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(lds_addr(p)));
+  return r;
+}
+template <int N>
+__device__ __forceinline__ void tie(u32x4& a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N>
+__device__ __forceinline__ void tie(u32x2& a, u32x2& b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+
 // ---------------------------------------------------------------------------
 // End-of-iteration synchronisation: wait until at most `ahead` tiles of
 // direct loads (L per thread each) are still in flight, finish this wave's
@@ -377,21 +396,47 @@ __device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<N
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
+      // Reads: side (this wave's turn), A 0..3, B 0..7; the waits count
+      // from the end, so they do not depend on the side read.
+      const bool side = NSIDE > 0 && ks == q.wn;
+      u32x4 sv[NSIDE > 0 ? NSIDE : 1];
+      if constexpr (NSIDE > 0) {
+        if (side) {
+#pragma unroll
+          for (int sb = 0; sb < NSIDE; ++sb)
+            if ((ld.smask >> sb) & 1u) sv[sb] = rd128(Bs + lds_off2(kBN + sb * 16 + q.r16, ks * 4 + q.g));
+        }
+      }
+      u32x4 av[kMB], bv[8];
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) av[mb] = rd128(As + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) bv[nb] = rd128(Bs + lds_off2(q.wn * 128 + nb * 16 + q.r16, ks * 4 + q.g));
       Frag<bf16> af[kMB];
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag2(As, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const Frag<bf16> bfr = lds_frag2(Bs, q.wn * 128 + nb * 16 + q.r16, ks, q.g);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      for (int mb = 0; mb < kMB; ++mb) {
+        tie<8>(av[mb]);
+        af[mb].v = av[mb];
       }
+#define LORA_FWD_NB(NB, N)                                                    \
+      {                                                                       \
+        tie<N>(bv[NB]);                                                       \
+        Frag<bf16> bfr;                                                       \
+        bfr.v = bv[NB];                                                       \
+        _Pragma("unroll") for (int mb = 0; mb < kMB; ++mb) acc[mb][NB] = mma(acc[mb][NB], af[mb], bfr); \
+        __builtin_amdgcn_sched_barrier(0);                                    \
+      }
+      LORA_FWD_NB(0, 7) LORA_FWD_NB(1, 6) LORA_FWD_NB(2, 5) LORA_FWD_NB(3, 4)
+      LORA_FWD_NB(4, 3) LORA_FWD_NB(5, 2) LORA_FWD_NB(6, 1) LORA_FWD_NB(7, 0)
+#undef LORA_FWD_NB
       if constexpr (NSIDE > 0) {
-        if (ks == q.wn) {
+        if (side) {
 #pragma unroll
           for (int sb = 0; sb < NSIDE; ++sb) {
             if ((ld.smask >> sb) & 1u) {
-              const Frag<bf16> bfr = lds_frag2(Bs, kBN + sb * 16 + q.r16, ks, q.g);
+              tie<0>(sv[sb]);
+              Frag<bf16> bfr;
+              bfr.v = sv[sb];
 #pragma unroll
               for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = mma(sacc[sb][mb], af[mb], bfr);
             }
@@ -486,32 +531,40 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      Frag<bf16> af[kMB];
+      // Reads: side (this wave's turn), A 0..3, then the two transpose reads
+      // of each B fragment; waits count from the end.
+      const bool side = NSIDE > 0 && ks == q.wn;
+      u32x2 slo, shi;
+      if (side) tr_side_issue(Bs + kStage2TrB + ks * 1024, q, slo, shi);
+      u32x4 av[kMB];
 #pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag2(As, q.wm * 64 + mb * 16 + q.r16, ks, q.g);
+      for (int mb = 0; mb < kMB; ++mb) av[mb] = rd128(As + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
       const char* Bk = Bs + ks * 32 * 512;
       u32x2 lo[8], hi[8];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) tr_issue(Bk, nb, q, lo[nb], hi[nb]);
-      lgkm_tie<8>(lo[0], hi[0], lo[1], hi[1], lo[2], hi[2], lo[3], hi[3]);
+      Frag<bf16> af[kMB];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const Frag<bf16> bfr = tr_make(lo[nb], hi[nb]);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+      for (int mb = 0; mb < kMB; ++mb) {
+        // 16 transpose reads follow the A reads and the counter holds at most
+        // 15 outstanding operations, so A has landed: this only ties the
+        // registers (lgkmcnt is a 4-bit field).
+        tie<15>(av[mb]);
+        af[mb].v = av[mb];
       }
-      lgkm_tie<0>(lo[4], hi[4], lo[5], hi[5], lo[6], hi[6], lo[7], hi[7]);
-#pragma unroll
-      for (int nb = 4; nb < 8; ++nb) {
-        const Frag<bf16> bfr = tr_make(lo[nb], hi[nb]);
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
+#define LORA_TR_NB(NB, N)                                                     \
+      {                                                                       \
+        tie<N>(lo[NB], hi[NB]);                                               \
+        const Frag<bf16> bfr = tr_make(lo[NB], hi[NB]);                       \
+        _Pragma("unroll") for (int mb = 0; mb < kMB; ++mb) acc[mb][NB] = mma(acc[mb][NB], af[mb], bfr); \
+        __builtin_amdgcn_sched_barrier(0);                                    \
       }
+      LORA_TR_NB(0, 14) LORA_TR_NB(1, 12) LORA_TR_NB(2, 10) LORA_TR_NB(3, 8)
+      LORA_TR_NB(4, 6) LORA_TR_NB(5, 4) LORA_TR_NB(6, 2) LORA_TR_NB(7, 0)
+#undef LORA_TR_NB
       if constexpr (NSIDE > 0) {
-        if (ks == q.wn) {
-          u32x2 slo, shi;
-          tr_side_issue(Bs + kStage2TrB + ks * 1024, q, slo, shi);
-          lgkm_tie0(slo, shi);
+        if (side) {
+          tie<0>(slo, shi);
           const Frag<bf16> bfr = tr_make(slo, shi);
 #pragma unroll
           for (int mb = 0; mb < kMB; ++mb) sacc[0][mb] = mma(sacc[0][mb], af[mb], bfr);
