@@ -226,14 +226,23 @@ template <int N> __device__ __forceinline__ float lane_group_sum(float v) {
 #define LORA_ACT_GEGLU_TANH 1
 #define LORA_ACT_GEGLU_ERF 2
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+// The activations use the hardware exponential (v_exp_f32, 2^x) and
+// reciprocal (v_rcp_f32), each within about one ulp, instead of the
+// range-reduced expf and the IEEE division sequence: the GLU epilogues
+// evaluate them for every element of G while no MFMA runs.  Limits hold:
+// e^x -> inf gives rcp -> 0, e^x -> 0 gives rcp(1) = 1.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoidf_(float x) { return rcp_hw(1.0f + exp_hw(-x)); }
+// tanh(y) = 1 - 2 / (1 + e^(2y)).
+__device__ __forceinline__ float tanh_hw(float y) { return 1.0f - 2.0f * rcp_hw(1.0f + exp_hw(2.0f * y)); }
 
 template <int ACT> __device__ __forceinline__ float act_fwd(float g) {
   if constexpr (ACT == LORA_ACT_SWIGLU) {
     return g * sigmoidf_(g);
   } else if constexpr (ACT == LORA_ACT_GEGLU_TANH) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;   // sqrt(2/pi), cubic coefficient
-    return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+    return 0.5f * g * (1.0f + tanh_hw(k0 * (g + k1 * g * g * g)));
   } else {
     return 0.5f * g * (1.0f + erff(g * 0.7071067811865476f));   // exact GELU: g * Phi(g)
   }
@@ -246,14 +255,14 @@ template <int ACT> __device__ __forceinline__ void act_both(float g, float& phi,
     dphi = s * (1.0f + g * (1.0f - s));
   } else if constexpr (ACT == LORA_ACT_GEGLU_TANH) {
     const float k0 = 0.7978845608028654f, k1 = 0.044715f;
-    const float t = tanhf(k0 * (g + k1 * g * g * g));
+    const float t = tanh_hw(k0 * (g + k1 * g * g * g));
     phi = 0.5f * g * (1.0f + t);
     dphi = 0.5f * (1.0f + t) + 0.5f * g * (1.0f - t * t) * k0 * (1.0f + 3.0f * k1 * g * g);
   } else {
     // Phi(g) = (1 + erf(g / sqrt 2)) / 2; phi'(g) = Phi(g) + g * exp(-g^2/2) / sqrt(2 pi).
     const float cdf = 0.5f * (1.0f + erff(g * 0.7071067811865476f));
     phi = g * cdf;
-    dphi = cdf + g * 0.3989422804014327f * expf(-0.5f * g * g);
+    dphi = cdf + g * 0.3989422804014327f * exp_hw(-0.5f * g * g);
   }
 }
 
