@@ -413,8 +413,7 @@ struct DownBwdArgs {
 // (its 64 rows x 128 columns) after Ts slot 0, the only side slot this kernel
 // uses.  That frees the accumulators for the GLU backward and the partials.
 constexpr int kDownParkOff = kBM * kSlot * 4;
-constexpr int kDownPrefOff = kDownParkOff + 8 * 16384;           // 147456
-constexpr int kDownBwdLds = kDownPrefOff + 8 * 1024;              // 155648: + a 1 KB L2-prefetch sink per wave
+constexpr int kDownBwdLds = kDownParkOff + 8 * 16384;            // 147456
 static_assert(kDownBwdLds >= kGemmLds && kDownBwdLds <= 163840, "k_down_bwd LDS");
 
 template <class T, int ACT, bool FAST>
@@ -454,24 +453,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
     kloop<T, 0>(smem, nkt, ld, acc, sacc);
   }
 
-  if constexpr (FAST) {
-    // Pull this tile's G and U rows (256 x 512 bytes each) into L2 before the
-    // fold: direct loads into a per-wave sink nobody reads, so they cost no
-    // registers and all 32 per lane are in flight together.  The GLU fetches
-    // below then hit L2 instead of waiting on HBM one m-block at a time.
-    // Rows past N are clamped to N - 1, chunks past i to the last one.
-    char* sink = smem + kDownPrefOff + q.w * 1024;
-    const long col = min(n0 + (threadIdx.x & 31) * 8, ni - 8);
-    const bf16* G0 = static_cast<const bf16*>(a.G) + col;
-    const bf16* U0 = static_cast<const bf16*>(a.U) + col;
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      long row = m0 + (threadIdx.x >> 5) + 16 * it;
-      if (row > a.N - 1) row = a.N - 1;
-      g2lds16(G0 + row * ni, sink);
-      g2lds16(U0 + row * ni, sink);
-    }
-  }
   load_dT(smem, a.dT, a.N, m0, 1);
   const T* Ad = static_cast<const T*>(a.Ad);
   auto fb = [&](int R, int slot, int t0, float* v) {

@@ -369,7 +369,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
     a.vecW = (i % V == 0) && al16(dn.W);
     a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
     a.R = R; a.NC = (int)cdiv(i, kBN);
-    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W, G, U}) && i % 8 == 0 && h % 64 == 0;
+    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0 && h % 64 == 0;
     const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
                                     dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
     if (rc) return rc;
