@@ -28,6 +28,10 @@
  *   - RoPE pairs column j with j + head_dim/2 of a head (half split), angle
  *     = s * theta^(-2j/head_dim) evaluated in double precision, s = n mod seq.
  *   - Q is [batch, n_q, seq, head_dim], K and V are [batch, n_kv, seq, head_dim].
+ *   - n_tokens = 0 (batch = 0 for QKV) is a valid call: the forward writes
+ *     nothing, the backward writes dA = 0 and dB = 0 (empty sums).  Per-token
+ *     tensors (X, Y, G, U, T, Q, K, V, their gradients, Pn, rinv) may then be
+ *     NULL; weights, adapters and dA / dB may not.
  *   - One dtype per call (LORA_F32 or LORA_BF16) for X, W, A, B, the upstream
  *     gradients and every output except T (always float32). Accumulation is
  *     float32; each stored value is rounded once (round-to-nearest-even).
@@ -95,7 +99,7 @@ typedef struct {
 
 /* LoRA MLP: gate/up [hidden -> inter], GLU, down [inter -> hidden]. */
 typedef struct {
-  int64_t n_tokens;   /* N = batch * seq */
+  int64_t n_tokens;   /* N = batch * seq, >= 0 */
   int32_t hidden;     /* h */
   int32_t inter;      /* i */
   int32_t rank;       /* r, 1..LORA_MAX_RANK */
@@ -106,7 +110,7 @@ typedef struct {
 
 /* LoRA QKV: X [batch*seq, hidden] -> Q, K, V head-split, RoPE on Q and K. */
 typedef struct {
-  int32_t batch;
+  int32_t batch;      /* >= 0 (0: empty batch) */
   int32_t seq;
   int32_t hidden;
   int32_t n_q;        /* query heads */
@@ -119,7 +123,7 @@ typedef struct {
 
 /* One LoRA linear (e.g. an attention output projection): X [N, in] -> Y [N, out]. */
 typedef struct {
-  int64_t n_tokens;      /* N */
+  int64_t n_tokens;      /* N >= 0 */
   int32_t in_features;   /* in */
   int32_t out_features;  /* out */
   int32_t rank;          /* r, 1..LORA_MAX_RANK */

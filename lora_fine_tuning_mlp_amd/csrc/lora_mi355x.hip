@@ -226,8 +226,8 @@ LinWs lin_ws(const lora_linear_desc_t& d, int pass, void* base) {
 // ---- validation ---------------------------------------------------------------
 int check_mlp(const lora_mlp_desc_t* d) {
   if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
-  if (d->n_tokens <= 0 || d->hidden <= 0 || d->inter <= 0 || d->rank <= 0)
-    return fail(LORA_ERR_SHAPE, "sizes must be positive (n_tokens=%lld hidden=%d inter=%d rank=%d)",
+  if (d->n_tokens < 0 || d->hidden <= 0 || d->inter <= 0 || d->rank <= 0)
+    return fail(LORA_ERR_SHAPE, "sizes must be positive, n_tokens >= 0 (n_tokens=%lld hidden=%d inter=%d rank=%d)",
                 (long long)d->n_tokens, d->hidden, d->inter, d->rank);
   if (d->reserved != 0) return fail(LORA_ERR_SHAPE, "reserved field must be 0");
   if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
@@ -250,7 +250,7 @@ int check_proj_nobias(const lora_proj_t* p, const char* name) {
 }
 int check_qkv(const lora_qkv_desc_t* d) {
   if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
-  if (d->batch <= 0 || d->seq <= 0 || d->hidden <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->head_dim <= 0 ||
+  if (d->batch < 0 || d->seq <= 0 || d->hidden <= 0 || d->n_q <= 0 || d->n_kv <= 0 || d->head_dim <= 0 ||
       d->rank <= 0)
     return fail(LORA_ERR_SHAPE, "sizes must be positive");
   if (d->head_dim % 2) return fail(LORA_ERR_SHAPE, "head_dim %d is odd", d->head_dim);
@@ -266,8 +266,8 @@ int check_qkv(const lora_qkv_desc_t* d) {
 
 int check_linear(const lora_linear_desc_t* d) {
   if (!d) return fail(LORA_ERR_NULL, "desc is NULL");
-  if (d->n_tokens <= 0 || d->in_features <= 0 || d->out_features <= 0 || d->rank <= 0)
-    return fail(LORA_ERR_SHAPE, "sizes must be positive (n_tokens=%lld in=%d out=%d rank=%d)",
+  if (d->n_tokens < 0 || d->in_features <= 0 || d->out_features <= 0 || d->rank <= 0)
+    return fail(LORA_ERR_SHAPE, "sizes must be positive, n_tokens >= 0 (n_tokens=%lld in=%d out=%d rank=%d)",
                 (long long)d->n_tokens, d->in_features, d->out_features, d->rank);
   if (d->dtype != LORA_F32 && d->dtype != LORA_BF16) return fail(LORA_ERR_UNSUPPORTED, "unsupported dtype %d", d->dtype);
   if (d->rank > LORA_MAX_RANK) return fail(LORA_ERR_UNSUPPORTED, "rank %d above LORA_MAX_RANK", d->rank);
@@ -292,6 +292,7 @@ template <class T, int ACT>
 int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, const lora_proj_t& u,
                  const lora_proj_t& dn, void* Y, void* G, void* U, void* Tsv, const MlpWs& w, hipStream_t st) {
   const long N = d.n_tokens;
+  if (N == 0) return ok();                         // empty batch: nothing to compute
   const int h = d.hidden, i = d.inter, r = d.rank, V = vecw(DT<T>::code);
   const int R = (int)cdiv(N, kBM);
   float* T3 = static_cast<float*>(Tsv);
@@ -338,59 +339,63 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
   const int h = d.hidden, i = d.inter, r = d.rank, V = vecw(DT<T>::code);
   const int R = (int)cdiv(N, kBM);
   const float* T3 = static_cast<const float*>(Tsv);
-  {
-    ProArgs a{};
-    a.qkv = 0;
-    a.P = dY;
-    a.Bp[0] = dn.B; a.Tp[0] = T3 + 2 * N * r; a.s[0] = dn.scale;
-    a.off[0] = 0; a.off[1] = h; a.off[2] = h; a.off[3] = h;
-    a.nadp = 1;
-    a.dT_part = w.dT_part; a.dB_part = w.pB_d;
-    a.N = N; a.O = h; a.r = r;
-    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
-    a.vecP = (h % V == 0) && al16(dY);
-    a.vecB = (r % V == 0) && al16(dn.B);
-    int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
-    if (rc) return rc;
-    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
-                w.NCR, N);
-    if (rc) return rc;
-  }
-  {
-    DownBwdArgs a{};
-    a.dY = dY; a.Wd = dn.W; a.Ad = dn.A; a.G = G; a.U = U;
-    a.Tg = T3; a.Tu = T3 + N * r;
-    a.dT = w.dT;
-    a.sg = g.scale; a.su = u.scale;
-    a.dG = w.dG; a.dU = w.dU;
-    a.pA_d = w.pA_d; a.pB_g = w.pB_g; a.pB_u = w.pB_u;
-    a.N = N; a.h = h; a.i = i; a.r = r;
-    a.vecA = (h % V == 0) && al16(dY);
-    a.vecW = (i % V == 0) && al16(dn.W);
-    a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
-    a.R = R; a.NC = (int)cdiv(i, kBN);
-    const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0 && h % 64 == 0;
-    const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
-                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
-    if (rc) return rc;
-  }
-  {
-    MlpDxArgs a{};
-    a.dG = w.dG; a.dU = w.dU; a.Wg = g.W; a.Wu = u.W; a.Bg = g.B; a.Bu = u.B; a.Ag = g.A; a.Au = u.A;
-    a.X = X; a.sg = g.scale; a.su = u.scale;
-    a.dX = dX; a.pA_g = w.pA_g; a.pA_u = w.pA_u;
-    a.N = N; a.h = h; a.i = i; a.r = r;
-    a.vecA = (i % V == 0) && al16(w.dG) && al16(w.dU);
-    a.vecW = (h % V == 0) && al16(g.W) && al16(u.W);
-    a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
-    a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
-    a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast =
-        fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 && i % 64 == 0;
-    const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
-                                    dim3(kGemmThreads), st, a);
-    if (rc) return rc;
-  }
+  // No tokens: the adapter gradients are empty sums; only the reduction
+  // runs (over zero row blocks), writing zeros.
+  if (N > 0) {
+    {
+      ProArgs a{};
+      a.qkv = 0;
+      a.P = dY;
+      a.Bp[0] = dn.B; a.Tp[0] = T3 + 2 * N * r; a.s[0] = dn.scale;
+      a.off[0] = 0; a.off[1] = h; a.off[2] = h; a.off[3] = h;
+      a.nadp = 1;
+      a.dT_part = w.dT_part; a.dB_part = w.pB_d;
+      a.N = N; a.O = h; a.r = r;
+      a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+      a.vecP = (h % V == 0) && al16(dY);
+      a.vecB = (r % V == 0) && al16(dn.B);
+      int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      if (rc) return rc;
+      rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
+                  w.NCR, N);
+      if (rc) return rc;
+    }
+    {
+      DownBwdArgs a{};
+      a.dY = dY; a.Wd = dn.W; a.Ad = dn.A; a.G = G; a.U = U;
+      a.Tg = T3; a.Tu = T3 + N * r;
+      a.dT = w.dT;
+      a.sg = g.scale; a.su = u.scale;
+      a.dG = w.dG; a.dU = w.dU;
+      a.pA_d = w.pA_d; a.pB_g = w.pB_g; a.pB_u = w.pB_u;
+      a.N = N; a.h = h; a.i = i; a.r = r;
+      a.vecA = (h % V == 0) && al16(dY);
+      a.vecW = (i % V == 0) && al16(dn.W);
+      a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
+      a.R = R; a.NC = (int)cdiv(i, kBN);
+      const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0 && h % 64 == 0;
+      const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
+                                      dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+      if (rc) return rc;
+    }
+    {
+      MlpDxArgs a{};
+      a.dG = w.dG; a.dU = w.dU; a.Wg = g.W; a.Wu = u.W; a.Bg = g.B; a.Bu = u.B; a.Ag = g.A; a.Au = u.A;
+      a.X = X; a.sg = g.scale; a.su = u.scale;
+      a.dX = dX; a.pA_g = w.pA_g; a.pA_u = w.pA_u;
+      a.N = N; a.h = h; a.i = i; a.r = r;
+      a.vecA = (i % V == 0) && al16(w.dG) && al16(w.dU);
+      a.vecW = (h % V == 0) && al16(g.W) && al16(u.W);
+      a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
+      a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
+      a.R = R; a.NC = (int)cdiv(h, kBN);
+      const bool fast =
+          fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 && i % 64 == 0;
+      const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
+                                      dim3(kGemmThreads), st, a);
+      if (rc) return rc;
+    }
+}
   {
     RedArgs a{};
     a.r = r;
@@ -436,6 +441,7 @@ template <class T>
 int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* const (&pr)[3], void* const (&out)[3],
                  void* Tsv, const QkvWs& w, hipStream_t st, const NormIo* nio = nullptr) {
   const long N = (long)d.batch * d.seq;
+  if (N == 0) return ok();
   const int h = d.hidden, r = d.rank, V = vecw(DT<T>::code);
   int rc = rope_table(d, w, st);
   if (rc) return rc;
@@ -499,78 +505,82 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
   int off[4], nh[3];
   qkv_offsets(d, off, nh);
   const int O = off[3];
-  int rc = rope_table(d, w, st);
-  if (rc) return rc;
-  if (nio) {
-    // dP through RoPE^T and the per-head norm, then the prologue reads it as a
-    // plain token-major upstream gradient over the three adapters.
-    NormBwdArgs a{};
-    for (int p = 0; p < 3; ++p) { a.src[p] = dO[p]; a.nh[p] = nh[p]; }
-    a.Pn = nio->Pn; a.rinv = nio->rinv;
-    a.nw[0] = nio->w[0]; a.nw[1] = nio->w[1];
-    a.cs = w.cs; a.sn = w.sn;
-    a.dP = w.dP;
-    a.N = N; a.S = d.seq; a.d = d.head_dim;
-    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
-    constexpr int E = ET<T>::VEC;
-    const int tph = d.head_dim / 2 / E;
-    const dim3 blk(256);
-    const unsigned gy = (unsigned)(nh[0] + nh[1] + nh[2]);
-    if (tph == 4) rc = launch(10, k_qk_norm_bwd<T, 4>, dim3((unsigned)cdiv(N, 64), gy), blk, st, a);
-    else if (tph == 8) rc = launch(10, k_qk_norm_bwd<T, 8>, dim3((unsigned)cdiv(N, 32), gy), blk, st, a);
-    else rc = launch(10, k_qk_norm_bwd<T, 16>, dim3((unsigned)cdiv(N, 16), gy), blk, st, a);
+  // No tokens: the adapter gradients are empty sums; only the reduction
+  // runs (over zero row blocks), writing zeros.
+  if (N > 0) {
+    int rc = rope_table(d, w, st);
     if (rc) return rc;
-  }
-  {
-    ProArgs a{};
-    a.qkv = nio ? 0 : 1;
-    a.P = w.dP;
-    bool sal = true, bal = true;
-    for (int p = 0; p < 3; ++p) {
-      a.src[p] = dO[p];
-      a.nh[p] = nh[p];
-      a.Bp[p] = pr[p]->B;
-      a.Tp[p] = static_cast<const float*>(Tsv) + p * N * r;
-      a.s[p] = pr[p]->scale;
-      sal = sal && al16(dO[p]);
-      bal = bal && al16(pr[p]->B);
+    if (nio) {
+      // dP through RoPE^T and the per-head norm, then the prologue reads it as a
+      // plain token-major upstream gradient over the three adapters.
+      NormBwdArgs a{};
+      for (int p = 0; p < 3; ++p) { a.src[p] = dO[p]; a.nh[p] = nh[p]; }
+      a.Pn = nio->Pn; a.rinv = nio->rinv;
+      a.nw[0] = nio->w[0]; a.nw[1] = nio->w[1];
+      a.cs = w.cs; a.sn = w.sn;
+      a.dP = w.dP;
+      a.N = N; a.S = d.seq; a.d = d.head_dim;
+      for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+      constexpr int E = ET<T>::VEC;
+      const int tph = d.head_dim / 2 / E;
+      const dim3 blk(256);
+      const unsigned gy = (unsigned)(nh[0] + nh[1] + nh[2]);
+      if (tph == 4) rc = launch(10, k_qk_norm_bwd<T, 4>, dim3((unsigned)cdiv(N, 64), gy), blk, st, a);
+      else if (tph == 8) rc = launch(10, k_qk_norm_bwd<T, 8>, dim3((unsigned)cdiv(N, 32), gy), blk, st, a);
+      else rc = launch(10, k_qk_norm_bwd<T, 16>, dim3((unsigned)cdiv(N, 16), gy), blk, st, a);
+      if (rc) return rc;
     }
-    a.cs = w.cs; a.sn = w.sn; a.S = d.seq; a.d = d.head_dim;
-    a.dP = w.dP;
-    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
-    a.nadp = 3;
-    a.dT_part = w.dT_part; a.dB_part = w.dB_part;
-    a.N = N; a.O = O; a.r = r;
-    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
-    a.vecP = nio ? true : sal;
-    a.vecB = (r % V == 0) && bal;
-    rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
-    if (rc) return rc;
-    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 3), dim3(256), st, (const float*)w.dT_part, w.dT,
-                w.NCR, N);
-    if (rc) return rc;
-  }
-  {
-    ProjDxArgs a{};
-    a.dP = w.dP;
-    bool wal = true;
-    for (int p = 0; p < 3; ++p) {
-      a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.pA[p] = w.pA[p];
-      wal = wal && al16(pr[p]->W);
+    {
+      ProArgs a{};
+      a.qkv = nio ? 0 : 1;
+      a.P = w.dP;
+      bool sal = true, bal = true;
+      for (int p = 0; p < 3; ++p) {
+        a.src[p] = dO[p];
+        a.nh[p] = nh[p];
+        a.Bp[p] = pr[p]->B;
+        a.Tp[p] = static_cast<const float*>(Tsv) + p * N * r;
+        a.s[p] = pr[p]->scale;
+        sal = sal && al16(dO[p]);
+        bal = bal && al16(pr[p]->B);
+      }
+      a.cs = w.cs; a.sn = w.sn; a.S = d.seq; a.d = d.head_dim;
+      a.dP = w.dP;
+      for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+      a.nadp = 3;
+      a.dT_part = w.dT_part; a.dB_part = w.dB_part;
+      a.N = N; a.O = O; a.r = r;
+      a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+      a.vecP = nio ? true : sal;
+      a.vecB = (r % V == 0) && bal;
+      rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      if (rc) return rc;
+      rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 3), dim3(256), st, (const float*)w.dT_part, w.dT,
+                  w.NCR, N);
+      if (rc) return rc;
     }
-    a.dT = w.dT;
-    a.X = X; a.dX = dX;
-    a.N = N; a.h = h; a.O = O; a.r = r;
-    for (int k = 0; k < 4; ++k) a.off[k] = off[k];
-    a.vecA = (O % V == 0);
-    a.vecW = (h % V == 0) && wal;
-    a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
-    a.R = R; a.NC = (int)cdiv(h, kBN);
-    const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0 && O % 64 == 0;
-    rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 3>), (k_proj_dx_bwd<T, false, 3>), dim3(a.R * a.NC),
-                          dim3(kGemmThreads), st, a);
-    if (rc) return rc;
-  }
+    {
+      ProjDxArgs a{};
+      a.dP = w.dP;
+      bool wal = true;
+      for (int p = 0; p < 3; ++p) {
+        a.W[p] = pr[p]->W; a.A[p] = pr[p]->A; a.pA[p] = w.pA[p];
+        wal = wal && al16(pr[p]->W);
+      }
+      a.dT = w.dT;
+      a.X = X; a.dX = dX;
+      a.N = N; a.h = h; a.O = O; a.r = r;
+      for (int k = 0; k < 4; ++k) a.off[k] = off[k];
+      a.vecA = (O % V == 0);
+      a.vecW = (h % V == 0) && wal;
+      a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
+      a.R = R; a.NC = (int)cdiv(h, kBN);
+      const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0 && O % 64 == 0;
+      rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 3>), (k_proj_dx_bwd<T, false, 3>), dim3(a.R * a.NC),
+                            dim3(kGemmThreads), st, a);
+      if (rc) return rc;
+    }
+}
   {
     RedArgs a{};
     a.r = r;
@@ -583,7 +593,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
       a.job[3 + p] = RedJob{w.dB_part + (long)off[p] * 16, so, cnt, R, off[p + 1] - off[p], 0, dB[p]};
       if (cnt > mx) mx = cnt;
     }
-    rc = launch(8, k_reduce<T>, dim3((unsigned)cdiv(mx, 256), 6), dim3(256), st, a);
+    const int rc = launch(8, k_reduce<T>, dim3((unsigned)cdiv(mx, 256), 6), dim3(256), st, a);
     if (rc) return rc;
   }
   return ok();
@@ -594,6 +604,7 @@ template <class T>
 int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_t& p, void* Y, void* Tsv,
                     hipStream_t st) {
   const long N = d.n_tokens;
+  if (N == 0) return ok();
   const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
   LinearArgs a{};
   a.Z = X; a.W = p.W; a.A = p.A; a.B = p.B; a.bias = p.bias; a.s = p.scale;
@@ -617,43 +628,47 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
   const long N = d.n_tokens;
   const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
   const int R = (int)cdiv(N, kBM);
-  {
-    ProArgs a{};
-    a.qkv = 0;
-    a.P = dY;
-    a.Bp[0] = p.B; a.Tp[0] = static_cast<const float*>(Tsv); a.s[0] = p.scale;
-    a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
-    a.nadp = 1;
-    a.dT_part = w.dT_part; a.dB_part = w.dB_part;
-    a.N = N; a.O = out; a.r = r;
-    a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
-    a.vecP = (out % V == 0) && al16(dY);
-    a.vecB = (r % V == 0) && al16(p.B);
-    int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
-    if (rc) return rc;
-    rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
-                w.NCR, N);
-    if (rc) return rc;
-  }
-  {
-    ProjDxArgs a{};
-    a.dP = dY;
-    a.W[0] = a.W[1] = a.W[2] = p.W;
-    a.A[0] = a.A[1] = a.A[2] = p.A;
-    a.pA[0] = a.pA[1] = a.pA[2] = w.pA;
-    a.dT = w.dT;
-    a.X = X; a.dX = dX;
-    a.N = N; a.h = in; a.O = out; a.r = r;
-    a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
-    a.vecA = (out % V == 0) && al16(dY);
-    a.vecW = (in % V == 0) && al16(p.W);
-    a.vecO = (in % 8 == 0) && al16(dX) && al16(X);
-    a.R = R; a.NC = (int)cdiv(in, kBN);
-    const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0 && out % 64 == 0;
-    const int rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 1>), (k_proj_dx_bwd<T, false, 1>),
-                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
-    if (rc) return rc;
-  }
+  // No tokens: the adapter gradients are empty sums; only the reduction
+  // runs (over zero row blocks), writing zeros.
+  if (N > 0) {
+    {
+      ProArgs a{};
+      a.qkv = 0;
+      a.P = dY;
+      a.Bp[0] = p.B; a.Tp[0] = static_cast<const float*>(Tsv); a.s[0] = p.scale;
+      a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
+      a.nadp = 1;
+      a.dT_part = w.dT_part; a.dB_part = w.dB_part;
+      a.N = N; a.O = out; a.r = r;
+      a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
+      a.vecP = (out % V == 0) && al16(dY);
+      a.vecB = (r % V == 0) && al16(p.B);
+      int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      if (rc) return rc;
+      rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
+                  w.NCR, N);
+      if (rc) return rc;
+    }
+    {
+      ProjDxArgs a{};
+      a.dP = dY;
+      a.W[0] = a.W[1] = a.W[2] = p.W;
+      a.A[0] = a.A[1] = a.A[2] = p.A;
+      a.pA[0] = a.pA[1] = a.pA[2] = w.pA;
+      a.dT = w.dT;
+      a.X = X; a.dX = dX;
+      a.N = N; a.h = in; a.O = out; a.r = r;
+      a.off[0] = 0; a.off[1] = out; a.off[2] = out; a.off[3] = out;
+      a.vecA = (out % V == 0) && al16(dY);
+      a.vecW = (in % V == 0) && al16(p.W);
+      a.vecO = (in % 8 == 0) && al16(dX) && al16(X);
+      a.R = R; a.NC = (int)cdiv(in, kBN);
+      const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0 && out % 64 == 0;
+      const int rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 1>), (k_proj_dx_bwd<T, false, 1>),
+                                      dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+      if (rc) return rc;
+    }
+}
   {
     RedArgs a{};
     a.r = r;
@@ -675,12 +690,11 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
 namespace {
 int check_norm(const lora_qkv_desc_t* desc, const lora_qk_norm_t* norm, const void* Pn, const float* rinv,
                std::initializer_list<const void*> vec_ptrs, NormIo& nio) {
-  if (!norm || !norm->q_weight || !norm->k_weight || !Pn || !rinv)
+  if (!norm || !norm->q_weight || !norm->k_weight || (desc->batch > 0 && (!Pn || !rinv)))
     return fail(LORA_ERR_NULL, "q/k norm weights, Pn or rinv is NULL");
   if (!(norm->eps >= 0.f)) return fail(LORA_ERR_SHAPE, "norm eps must be >= 0");
   for (const void* p : vec_ptrs)
     if (!al16(p)) return fail(LORA_ERR_UNSUPPORTED, "the q/k norm path needs 16-byte aligned tensors");
-  (void)desc;
   nio.w[0] = norm->q_weight; nio.w[1] = norm->k_weight;
   nio.eps = norm->eps;
   nio.Pn = const_cast<void*>(Pn);
@@ -714,9 +728,9 @@ int lora_mlp_fwd(const lora_mlp_desc_t* desc, const void* X, const lora_proj_t* 
   if ((rc = check_proj_nobias(gate, "gate")) || (rc = check_proj_nobias(up, "up")) ||
       (rc = check_proj_nobias(down, "down")))
     return rc;
-  if (!X || !Y || !G || !U || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  if (desc->n_tokens > 0 && (!X || !Y || !G || !U || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const MlpWs probe = mlp_ws(*desc, 0, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const MlpWs w = mlp_ws(*desc, 0, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -741,10 +755,11 @@ int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X, con
   if ((rc = check_proj_nobias(gate, "gate")) || (rc = check_proj_nobias(up, "up")) ||
       (rc = check_proj_nobias(down, "down")))
     return rc;
-  if (!dY || !X || !G || !U || !T || !dX || !dA_gate || !dB_gate || !dA_up || !dB_up || !dA_down || !dB_down)
+  if (!dA_gate || !dB_gate || !dA_up || !dB_up || !dA_down || !dB_down ||
+      (desc->n_tokens > 0 && (!dY || !X || !G || !U || !T || !dX)))
     return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const MlpWs probe = mlp_ws(*desc, 1, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const MlpWs w = mlp_ws(*desc, 1, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -768,9 +783,9 @@ int lora_qkv_fwd(const lora_qkv_desc_t* desc, const void* X, const lora_proj_t* 
   int rc = check_qkv(desc);
   if (rc) return rc;
   if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
-  if (!X || !Q || !K || !V || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  if (desc->batch > 0 && (!X || !Q || !K || !V || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const QkvWs probe = qkv_ws(*desc, 0, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const QkvWs w = qkv_ws(*desc, 0, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -787,10 +802,11 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
   int rc = check_qkv(desc);
   if (rc) return rc;
   if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
-  if (!dQ || !dK || !dV || !X || !T || !dX || !dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v)
+  if (!dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v ||
+      (desc->batch > 0 && (!dQ || !dK || !dV || !X || !T || !dX)))
     return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const QkvWs probe = qkv_ws(*desc, 1, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const QkvWs w = qkv_ws(*desc, 1, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -808,13 +824,13 @@ int lora_qkv_norm_fwd(const lora_qkv_desc_t* desc, const void* X, const lora_pro
   int rc = check_qkv(desc);
   if (rc) return rc;
   if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
-  if (!X || !Q || !K || !V || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  if (desc->batch > 0 && (!X || !Q || !K || !V || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   NormIo nio{};
   if ((rc = check_norm(desc, norm, Pn, rinv, {norm ? norm->q_weight : nullptr, norm ? norm->k_weight : nullptr, Pn},
                        nio)))
     return rc;
   const QkvWs probe = qkv_ws(*desc, 0, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const QkvWs w = qkv_ws(*desc, 0, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -832,14 +848,15 @@ int lora_qkv_norm_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* d
   int rc = check_qkv(desc);
   if (rc) return rc;
   if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
-  if (!dQ || !dK || !dV || !X || !T || !dX || !dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v)
+  if (!dA_q || !dB_q || !dA_k || !dB_k || !dA_v || !dB_v ||
+      (desc->batch > 0 && (!dQ || !dK || !dV || !X || !T || !dX)))
     return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   NormIo nio{};
   if ((rc = check_norm(desc, norm, Pn, rinv,
                        {norm ? norm->q_weight : nullptr, norm ? norm->k_weight : nullptr, Pn, dQ, dK, dV}, nio)))
     return rc;
   const QkvWs probe = qkv_ws(*desc, 1, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const QkvWs w = qkv_ws(*desc, 1, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -856,7 +873,7 @@ int lora_linear_fwd(const lora_linear_desc_t* desc, const void* X, const lora_pr
   int rc = check_linear(desc);
   if (rc) return rc;
   if ((rc = check_proj(proj, "proj"))) return rc;
-  if (!X || !Y || !T) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  if (desc->n_tokens > 0 && (!X || !Y || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   (void)workspace;
   (void)workspace_bytes;
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
@@ -870,9 +887,10 @@ int lora_linear_bwd(const lora_linear_desc_t* desc, const void* dY, const void* 
   int rc = check_linear(desc);
   if (rc) return rc;
   if ((rc = check_proj(proj, "proj"))) return rc;
-  if (!dY || !X || !T || !dX || !dA || !dB) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  if (!dA || !dB || (desc->n_tokens > 0 && (!dY || !X || !T || !dX)))
+    return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
   const LinWs probe = lin_ws(*desc, 1, nullptr);
-  if (!workspace || workspace_bytes < probe.bytes)
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const LinWs w = lin_ws(*desc, 1, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);

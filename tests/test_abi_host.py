@@ -83,7 +83,7 @@ def test_mlp_validation_codes():
     lib = B.lib()
     assert _call_mlp_fwd(None, 1 << 40) == 1
     assert _call_mlp_fwd(_mlp(), 1 << 40, null_x=True) == 1
-    assert _call_mlp_fwd(_mlp(n_tokens=0), 1 << 40) == 2
+    assert _call_mlp_fwd(_mlp(n_tokens=-8), 1 << 40) == 2
     assert _call_mlp_fwd(_mlp(hidden=-4), 1 << 40) == 2
     assert _call_mlp_fwd(_mlp(rank=B.LORA_MAX_RANK + 1), 1 << 40) == 3
     bad_dtype = _mlp()
@@ -175,6 +175,25 @@ def test_qkv_norm_validation_codes():
     assert fwd(B.QkNorm(FAKE.value, FAKE.value, -1.0)) == 2
     assert fwd(B.QkNorm(FAKE.value, 0x1002, 1e-6)) == 3          # misaligned weight
     assert b"aligned" in lib.lora_last_error_message()
+
+
+def test_empty_batch_forward_is_a_no_op():
+    """n_tokens = 0 (or batch = 0) is a valid call: the forward has nothing to
+    write and needs no workspace, so it returns OK without touching memory."""
+    lib = B.lib()
+    pr = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0)
+    f = FAKE
+    d = _mlp(n_tokens=0)
+    assert B.lora_mlp_workspace_bytes(d, 0) == 0
+    assert lib.lora_mlp_fwd(ctypes.byref(d), f, ctypes.byref(pr), ctypes.byref(pr), ctypes.byref(pr), f, f, f, f,
+                            None, 0, None) == 0
+    dl = _lin(n_tokens=0)
+    assert lib.lora_linear_fwd(ctypes.byref(dl), f, ctypes.byref(pr), f, f, None, 0, None) == 0
+    dq = _qkv(batch=0)
+    ws = B.lora_qkv_workspace_bytes(dq, 0)
+    assert lib.lora_qkv_fwd(ctypes.byref(dq), f, ctypes.byref(pr), ctypes.byref(pr), ctypes.byref(pr), f, f, f, f,
+                            f, ws, None) == 0
+    assert _call_mlp_fwd(_mlp(n_tokens=-1), 1 << 40) == 2
 
 
 def test_kernel_names_listed():

@@ -131,6 +131,42 @@ def test_linear_matches_mlp_down_projection():
     assert gc.rel_err(gc.to64(m.Y), f["Y"]) <= gc.TOL[cfg.dtype]
 
 
+def test_empty_batch_gradients_are_zero():
+    """No tokens: forward writes nothing, the adapter gradients are empty sums
+    (exactly zero), even where the outputs held NaN before the call."""
+    dev = torch.device("cuda:0")
+    cfg = S.MLPConfig("mlp_empty", 0, 128, 192, 8, 2.0, "swiglu", "bf16")
+    t = {k: v.to(dev) for k, v in S.mlp_inputs(cfg, 0).items()}
+    m = B_.MLP({k: v for k, v in t.items() if k != "dY"}, 0, 128, 192, 8, "bf16", "swiglu")
+    for g in m.grads.values():
+        g.fill_(float("nan"))
+    m.forward()
+    m.backward(t["dY"])
+    torch.cuda.synchronize()
+    for k, g in m.grads.items():
+        assert torch.count_nonzero(g).item() == 0, k
+    qc = S.QKVConfig("qkv_empty", 0, 16, 128, 4, 2, 64, 8, 2.0, 1.0e4, "bf16")
+    tq = {k: v.to(dev) for k, v in S.qkv_inputs(qc, 0).items()}
+    mq = B_.QKV({k: v for k, v in tq.items() if k not in ("dQ", "dK", "dV")}, 0, 16, 128, 4, 2, 64, 8, "bf16", 1.0e4)
+    for g in mq.grads.values():
+        g.fill_(float("nan"))
+    mq.forward()
+    mq.backward(tq["dQ"], tq["dK"], tq["dV"])
+    torch.cuda.synchronize()
+    for k, g in mq.grads.items():
+        assert torch.count_nonzero(g).item() == 0, k
+    lc = S.LinearConfig("linear_empty", 0, 64, 96, 4, 2.0, "f32")
+    tl = {k: v.to(dev) for k, v in S.linear_inputs(lc, 0).items()}
+    ml = B_.Linear({k: v for k, v in tl.items() if k != "dY"}, 0, 64, 96, 4, "f32")
+    for g in ml.grads.values():
+        g.fill_(float("nan"))
+    ml.forward()
+    ml.backward(tl["dY"])
+    torch.cuda.synchronize()
+    for k, g in ml.grads.items():
+        assert torch.count_nonzero(g).item() == 0, k
+
+
 def test_rope_position_zero_identity_on_device():
     """At position 0 RoPE is the identity: Q[:, :, 0] equals the unrotated projection."""
     cfg = gc.QKV_CASES[2]
