@@ -1,6 +1,8 @@
 """GPU parity of the HIP path (through the C ABI) against the CPU oracle on
 seeded inputs: element by element on multi-tile shapes with ragged tails,
 plus the exact special cases and run-to-run determinism."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -129,6 +131,28 @@ def test_linear_matches_mlp_down_projection():
     torch.cuda.synchronize()
     assert gc.rel_err(gc.to64(lin.Y), f["Y"]) <= gc.TOL[cfg.dtype]
     assert gc.rel_err(gc.to64(m.Y), f["Y"]) <= gc.TOL[cfg.dtype]
+
+
+def test_zero_scale_is_the_base_projection():
+    """s = 0: Y is the plain base projection and every adapter gradient
+    (dT = s dY B, dB = s dY^T T, dA = dT^T Z) is exactly zero."""
+    cfg = gc.MLP_CASES[1]
+    t = S.mlp_inputs(cfg, 8)
+    out = gc.run_mlp_gpu(cfg, t, scales=(0.0, 0.0, 0.0))
+    for n in ("gate", "up", "down"):
+        assert not np.any(out["dA_" + n]) and not np.any(out["dB_" + n]), n
+    gc.compare(f"{cfg.name}/s0", out, gc.run_mlp_oracle(cfg, t, scales=(0.0, 0.0, 0.0)), gc.TOL[cfg.dtype])
+    qc = gc.QKV_CASES[0]
+    tq = S.qkv_inputs(qc, 8)
+    out = gc.run_qkv_gpu(qc, tq, scales=(0.0, 0.0, 0.0))
+    for n in "qkv":
+        assert not np.any(out["dA_" + n]) and not np.any(out["dB_" + n]), n
+    gc.compare(f"{qc.name}/s0", out, gc.run_qkv_oracle(qc, tq, scales=(0.0, 0.0, 0.0)), gc.TOL[qc.dtype])
+    lc = dataclasses.replace(gc.LINEAR_CASES[0], scale=0.0)
+    tl = S.linear_inputs(lc, 8)
+    out = gc.run_linear_gpu(lc, tl)
+    assert not np.any(out["dA"]) and not np.any(out["dB"])
+    gc.compare(f"{lc.name}/s0", out, gc.run_linear_oracle(lc, tl), gc.TOL[lc.dtype])
 
 
 def test_empty_batch_gradients_are_zero():
