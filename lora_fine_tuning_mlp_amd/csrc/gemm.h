@@ -11,17 +11,16 @@
 // The side product rides along the base GEMM's K-loop: its operand sits in
 // LDS right after the B tile and reuses the A fragments already in
 // registers, so X (or H, or dG|dU) is read once for both.  The two waves that
-// share a row range take alternate K tiles of the side work; their halves are
-// summed through LDS after the loop.
+// share a row range take alternate K sub-steps (or tiles) of the side work;
+// their halves are summed through LDS after the loop.
 //
-// K-loop pipeline.  LDS holds a ring of four stages of one K tile each
-// (32 bf16 / 16 fp32 along K).  On the fast path every operand travels by
-// direct global -> LDS loads (no staging registers), and the loads for tile
-// kt + 3 are issued while tile kt is computed, so three tiles of loads are in
-// flight per workgroup.  The end of each iteration waits (vmcnt) only until
-// tile kt + 1 has landed and then barriers; a plain __syncthreads() would
-// drain every outstanding load.  Register-staged loaders (fp32, unaligned or
-// ragged shapes) prefetch one tile ahead.
+// K-loops.  Fast path (bf16, 16-byte aligned rows, K % 64 == 0): two LDS
+// stages of K tiles of 64 in 128-byte rows, every operand loaded straight
+// from global memory into LDS (no staging registers); tile kt + 1 is issued
+// at the top of iteration kt and has landed by its end (kloop2 for weights
+// stored [N][K], kloop2tr for [K][N]).  Staged path (fp32, unaligned or
+// ragged shapes): register-staged, masked loads one K tile (32 bf16 / 16
+// fp32, 64-byte rows) ahead (kloop).
 //
 // B operands: weights stored [N][K] (forward) are rows of the tile like A;
 // weights stored [K][N] (backward, bf16) keep that layout in LDS and are read
@@ -46,8 +45,10 @@ constexpr int kABytes = kARows * kRowBytes;                // 16384
 constexpr int kBBytes = kBRows * kRowBytes;                // 19456
 constexpr int kSideOff = kBN * kRowBytes;                  // side operand inside the B region
 constexpr int kStage = kABytes + kBBytes;                  // 35840
-constexpr int kNStage = 4;
-constexpr int kGemmLds = kNStage * kStage;                 // 143360 bytes
+// LDS of a GEMM workgroup: two fast-path stages of 71680 bytes (the staged
+// loop uses two stages of kStage).
+constexpr int kGemmLds = 143360;
+static_assert(2 * kStage <= kGemmLds, "two staged-loop stages");
 
 constexpr int kTsOff = 0;
 constexpr int kTsBytes = kMaxSide * kBM * kSlot * 4;       // 49152
@@ -84,21 +85,14 @@ __device__ __forceinline__ int ts_idx(int slot, int row, int t) { return (slot *
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads (gfx950 global_load_lds_dwordx4): lane l of a
-// wave writes 16 bytes at LDS base + 16 l, so a 1 KB block = 16 tile rows of
-// 64 bytes.  Lanes switched off by the exec mask write nothing.
+// wave writes 16 bytes at LDS base + 16 l, i.e. one 1 KB block per
+// instruction.  Lanes switched off by the exec mask write nothing.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void g2lds16(const void* g, char* lds_wave_base) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
 }
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Logical chunk a lane must fetch so that, written at physical chunk
-// (lane & 3) of row 16*blk + (lane >> 2), the tile obeys lds_off's swizzle.
-__device__ __forceinline__ int direct_chunk(int lane) { return (lane & 3) ^ ((lane >> 3) & 3); }
-// 1 KB block `it` of this wave (wave w fills blocks w + 8 it, it = 0, 1).
+// 1 KB block `it` of this wave (wave w fills blocks w + 8 it).
 __device__ __forceinline__ int direct_blk(int it) { return (int)(threadIdx.x >> 6) + 8 * it; }
-// Tile row this lane fills in its direct block it.
-__device__ __forceinline__ int direct_row(int it) { return 16 * direct_blk(it) + (int)((threadIdx.x & 63) >> 2); }
 
 // ---------------------------------------------------------------------------
 // [K][N] bf16 B tiles in their natural layout (32 rows k x 256 columns, 512
@@ -183,68 +177,36 @@ __device__ __forceinline__ void tie(u32x2& a, u32x2& b) {
 }
 
 // ---------------------------------------------------------------------------
-// End-of-iteration synchronisation: wait until at most `ahead` tiles of
-// direct loads (L per thread each) are still in flight, finish this wave's
-// LDS traffic, then barrier.  Written as one asm statement so the compiler
-// neither adds the fence of __syncthreads (which would wait for every load)
-// nor moves memory accesses across it.
+// End of a K iteration: wait for this wave's direct loads and LDS traffic,
+// then barrier.  Written as one asm statement so the compiler neither adds
+// the fence of __syncthreads() nor moves memory accesses across it.
 // ---------------------------------------------------------------------------
-template <int L>
-__device__ __forceinline__ void sync_tiles(int ahead) {
-  if (ahead >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(2 * L) : "memory");
-  } else if (ahead == 1) {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(L) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  }
-}
+__device__ __forceinline__ void sync_stage() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // ---------------------------------------------------------------------------
-// K-loop.  Loader interface:
-//   kDepth                   tiles issued ahead of the one being computed (3 or 1)
-//   kLoads                   direct loads per thread per tile (kDepth 3)
+// Staged K-loop (fp32, unaligned or ragged shapes).  Loader interface:
 //   kBTr                     B (and side) fragments by transpose reads
-//   issue(kt, As, Bs)        direct global -> LDS loads for K tile kt
 //   load(kt)                 register-staged global loads for K tile kt
 //   store(As, Bs)            registers -> LDS stage
 //   side_mask(kt)            bit sb set when side block sb has data in tile kt
-// K tiles kt0 .. nkt-1 (the ring restarts at stage 0).
+// K tiles kt0 .. nkt-1; the loads of tile kt + 1 are in flight while tile kt
+// is computed.
 // ---------------------------------------------------------------------------
 template <class T, int NSIDE, class Loader>
 __device__ __forceinline__ void kloop(char* smem, int nkt, Loader& ld, f32x4 (&acc)[kMB][8],
                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
-  constexpr int D = Loader::kDepth;
-  constexpr int L = Loader::kLoads;
-  static_assert(D == 1 || D == 3, "pipeline depth");
   const WaveId q = wave_id();
   if (nkt <= kt0) return;
-  auto stage = [&](int kt) { return smem + ((kt - kt0) & (kNStage - 1)) * kStage; };
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    const int kt = kt0 + d;
-    if (kt < nkt) {
-      char* S = stage(kt);
-      ld.issue(kt, S, S + kABytes);
-      ld.load(kt);
-      ld.store(S, S + kABytes);
-    }
-  }
-  if constexpr (D == 3) {
-    sync_tiles<L>(min(nkt - 1, kt0 + 2) - kt0);
-  } else {
-    sync_tiles<L>(0);
-  }
+  auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage; };
+  ld.load(kt0);
+  ld.store(stage(kt0), stage(kt0) + kABytes);
+  sync_stage();
   for (int kt = kt0; kt < nkt; ++kt) {
     const char* As = stage(kt);
     const char* Bs = As + kABytes;
-    const int nx = kt + D;
-    const bool more = nx < nkt;
-    char* Sn = stage(nx);
-    if (more) {
-      ld.issue(nx, Sn, Sn + kABytes);
-      ld.load(nx);
-    }
+    const bool more = kt + 1 < nkt;
+    char* Sn = stage(kt + 1);
+    if (more) ld.load(kt + 1);
     Frag<T> af[kMB];
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<T>(As, q.wm * 64 + mb * 16 + q.r16, q.g);
@@ -296,11 +258,7 @@ __device__ __forceinline__ void kloop(char* smem, int nkt, Loader& ld, f32x4 (&a
       }
     }
     if (more) ld.store(Sn, Sn + kABytes);
-    if constexpr (D == 3) {
-      sync_tiles<L>(min(nkt - 1, kt + D) - (kt + 1));
-    } else {
-      sync_tiles<L>(0);
-    }
+    sync_stage();
   }
 }
 
@@ -315,7 +273,7 @@ __device__ __forceinline__ void kloop(char* smem, int nkt, Loader& ld, f32x4 (&a
 constexpr int kRow2 = 128;
 constexpr int kStage2A = kBM * kRow2;                                 // 32768
 constexpr int kStage2 = (kBM + kBN + kSlot * kMaxSide) * kRow2;      // 71680
-static_assert(2 * kStage2 <= kGemmLds, "two 128-byte-row stages");
+static_assert(2 * kStage2 == kGemmLds, "two 128-byte-row stages");
 __device__ __forceinline__ int lds_off2(int row, int chunk) { return row * kRow2 + ((chunk ^ (row & 7)) << 4); }
 __device__ __forceinline__ Frag<bf16> lds_frag2(const char* buf, int row, int ks, int g) {
   Frag<bf16> f;
@@ -333,7 +291,6 @@ __device__ __forceinline__ int direct2_row(int it) { return 8 * direct_blk(it) +
 // NKLoader).  Requires K % 64 == 0, 16-byte aligned rows, 32-bit A offsets.
 template <int NSIDE>
 struct NKPairLoader {
-  static constexpr int kLoads = 8 + (NSIDE > 0 ? 1 : 0);
   const bf16* A;
   int aoff[4];
   const bf16* brow[4];
@@ -382,11 +339,10 @@ struct NKPairLoader {
 template <int NSIDE>
 __device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<NSIDE>& ld, f32x4 (&acc)[kMB][8],
                                        f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB]) {
-  constexpr int L = NKPairLoader<NSIDE>::kLoads;
   const WaveId q = wave_id();
   if (nkt <= 0) return;
   ld.issue(0, smem, smem + kStage2A);
-  sync_tiles<L>(0);
+  sync_stage();
   for (int kt = 0; kt < nkt; ++kt) {
     const char* As = smem + (kt & 1) * kStage2;
     const char* Bs = As + kStage2A;
@@ -444,7 +400,7 @@ __device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<N
         }
       }
     }
-    sync_tiles<L>(0);
+    sync_stage();
   }
 }
 
@@ -470,7 +426,6 @@ static_assert(2 * kStage2Tr <= kGemmLds, "two transpose-read stages");
 template <class KRow, class SRow, int NSIDE>
 struct KNPairLoader {
   static_assert(NSIDE <= 1, "one direct side block");
-  static constexpr int kLoads = 8 + (NSIDE > 0 ? 1 : 0);
   const bf16* A0;
   const bf16* A1;
   long K0;
@@ -516,12 +471,11 @@ struct KNPairLoader {
 template <int NSIDE, class Loader>
 __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, f32x4 (&acc)[kMB][8],
                                          f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
-  constexpr int L = Loader::kLoads;
   const WaveId q = wave_id();
   if (nkt <= kt0) return;
   auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage2Tr; };
   ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
-  sync_tiles<L>(0);
+  sync_stage();
   for (int kt = kt0; kt < nkt; ++kt) {
     const char* As = stage(kt);
     const char* Bs = As + kStage2A;
@@ -571,7 +525,7 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
         }
       }
     }
-    sync_tiles<L>(0);
+    sync_stage();
   }
 }
 
@@ -685,7 +639,6 @@ __device__ __forceinline__ int col_lds_row(int lg, int n) { return (n >> 7) * 12
 // stages chunk (t & 3) of rows (t >> 2) + 128 qq, qq = 0, 1.
 template <class T>
 struct RowsA {
-  static constexpr bool kDirect = false;
   const T* b0;
   const T* b1;
   long ld, K0, K1;
@@ -714,57 +667,17 @@ struct RowsA {
     }
     return pack(v);
   }
-  __device__ __forceinline__ void issue(int, char*) const {}
-};
-
-// Direct to LDS.  Requires K0 % BK == 0 (each K tile inside one segment),
-// 16-byte aligned rows, and every K tile full.  Rows past M are clamped to
-// row M-1 (finite values; those rows are never stored and every row
-// reduction masks them).
-template <class T>
-struct DirectA {
-  static constexpr bool kDirect = true;
-  const T* b0;
-  const T* b1;
-  long K0;
-  int off[2];
-  __device__ __forceinline__ void init(const T* A0, const T* A1, long Kd0, long, long lda, long M, long m0, bool) {
-    b0 = A0; b1 = A1 ? A1 : A0; K0 = A1 ? Kd0 : (1L << 40);
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      long row = m0 + direct_row(it);
-      if (row > M - 1) row = M - 1;
-      off[it] = (int)(row * lda);
-    }
-  }
-  __device__ __forceinline__ u32x4 get(int, long) const { return zero4(); }
-  __device__ __forceinline__ void issue(int kt, char* As) const {
-    const int L = threadIdx.x & 63;
-    long k = (long)kt * ET<T>::BK;
-    const T* b = b0;
-    if (k >= K0) { b = b1; k -= K0; }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) g2lds16(b + off[it] + k + direct_chunk(L) * ET<T>::VEC, As + direct_blk(it) * 1024);
-  }
 };
 
 // ---------------------------------------------------------------------------
-// NK loader: A rows + B rows (output columns, row-major [n][K]) + side rows
-// (adapter A_p rows [t][K]), all K-contiguous.  The kernel resolves the B row
-// pointers once for the rows row_of(qq), qq = 0, 1, of this thread, and the
-// side row pointer for side_row() (see side_ptr).
-//   Direct (AOp::kDirect): all three go straight into LDS.  A nullptr B row
-//   falls back to `bfallback` (a valid row whose output columns are never
-//   stored).  Side rows: lanes 0 .. 8 NSIDE - 1 of every wave load one chunk
-//   each; ranks past r read row r-1 (finite; their products meet zero fold
-//   rows and are never saved).
-//   Staged: A and B rows in registers, side rows zero-filled past the rank.
+// NK loader (staged): A rows + B rows (output columns, row-major [n][K]) +
+// side rows (adapter A_p rows [t][K]), all K-contiguous, in registers one K
+// tile ahead; zero-filled past K and past the rank.  The kernel resolves the
+// B row pointers once for the rows row_of(qq), qq = 0, 1, of this thread, and
+// the side row pointer for side_row() (see side_ptr).
 // ---------------------------------------------------------------------------
 template <class T, class AOp, int NSIDE>
 struct NKLoader {
-  static constexpr bool DIRECT = AOp::kDirect;
-  static constexpr int kDepth = DIRECT ? 3 : 1;
-  static constexpr int kLoads = 4 + (NSIDE > 0 ? 1 : 0);
   static constexpr bool kBTr = false;
   AOp a;
   const T* brow[2];
@@ -773,69 +686,37 @@ struct NKLoader {
   long K;
   bool vecB, vecS;
   unsigned smask;
-  u32x4 ra[DIRECT ? 1 : 2], rb[DIRECT ? 1 : 2], rs;
-  __device__ static __forceinline__ int row_of(int qq) {
-    return DIRECT ? direct_row(qq) : (int)(threadIdx.x >> 2) + 128 * qq;
-  }
+  u32x4 ra[2], rb[2], rs;
+  __device__ static __forceinline__ int row_of(int qq) { return (int)(threadIdx.x >> 2) + 128 * qq; }
   // Side row (16 sb + t) this thread loads, or -1.
   __device__ static __forceinline__ int side_row() {
-    if constexpr (DIRECT) {
-      const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
-      return (l < 8 * NSIDE) ? (w * 8 * NSIDE + l) >> 2 : -1;
-    } else {
-      const int r = threadIdx.x >> 2;
-      return (r < 16 * NSIDE) ? r : -1;
-    }
+    const int r = threadIdx.x >> 2;
+    return (r < 16 * NSIDE) ? r : -1;
   }
   // Pointer for side row t of an adapter whose rows start at `base` (nullptr:
-  // no adapter in this block); `fallback` is any valid row.
-  __device__ static __forceinline__ const T* side_ptr(const T* base, int t, int r, long Kd, const T* fallback) {
-    if constexpr (DIRECT) return base ? base + (long)min(t, r - 1) * Kd : fallback;
-    else return (base && t < r) ? base + (long)t * Kd : nullptr;
-  }
-  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
-    if constexpr (DIRECT) {
-      a.issue(kt, As);
-      const int L = threadIdx.x & 63;
-      const long k = (long)kt * ET<T>::BK;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const T* p = brow[it] ? brow[it] : bfallback;
-        g2lds16(p + k + direct_chunk(L) * ET<T>::VEC, Bs + direct_blk(it) * 1024);
-      }
-      if constexpr (NSIDE > 0) {
-        if (L < 8 * NSIDE) {
-          const int w = threadIdx.x >> 6;
-          const int ci = w * 8 * NSIDE + L, sr = ci >> 2;
-          const int chunk = (ci & 3) ^ ((sr >> 1) & 3);
-          g2lds16(srow + k + chunk * ET<T>::VEC, Bs + kSideOff + w * 128 * NSIDE);
-        }
-      }
-    }
+  // no adapter in this block); ranks past r load nothing.
+  __device__ static __forceinline__ const T* side_ptr(const T* base, int t, int r, long Kd, const T*) {
+    return (base && t < r) ? base + (long)t * Kd : nullptr;
   }
   __device__ __forceinline__ void load(int kt) {
-    if constexpr (!DIRECT) {
-      const long k = (long)kt * ET<T>::BK + (threadIdx.x & 3) * ET<T>::VEC;
+    const long k = (long)kt * ET<T>::BK + (threadIdx.x & 3) * ET<T>::VEC;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, k);
+    for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, k);
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<T>(brow[qq], k, K, vecB);
-      if constexpr (NSIDE > 0) {
-        rs = zero4();
-        if ((int)(threadIdx.x >> 2) < 16 * NSIDE) rs = gload<T>(srow, k, K, vecS);
-      }
+    for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<T>(brow[qq], k, K, vecB);
+    if constexpr (NSIDE > 0) {
+      rs = zero4();
+      if ((int)(threadIdx.x >> 2) < 16 * NSIDE) rs = gload<T>(srow, k, K, vecS);
     }
   }
   __device__ __forceinline__ void store(char* As, char* Bs) const {
-    if constexpr (!DIRECT) {
-      const int c = threadIdx.x & 3, r0 = threadIdx.x >> 2;
+    const int c = threadIdx.x & 3, r0 = threadIdx.x >> 2;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
+    for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + lds_off(r0 + 128 * qq, c)) = rb[qq];
-      if constexpr (NSIDE > 0)
-        if (r0 < NSIDE * 16) *reinterpret_cast<u32x4*>(Bs + lds_off(kBN + r0, c)) = rs;
-    }
+    for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + lds_off(r0 + 128 * qq, c)) = rb[qq];
+    if constexpr (NSIDE > 0)
+      if (r0 < NSIDE * 16) *reinterpret_cast<u32x4*>(Bs + lds_off(kBN + r0, c)) = rs;
   }
   __device__ __forceinline__ unsigned side_mask(int) const { return smask; }
 };
@@ -848,20 +729,13 @@ struct NKLoader {
 //   smask_of(kt)   -> active side blocks in tile kt
 // ---------------------------------------------------------------------------
 
-// bf16: the B tile keeps the [k][n] layout (kn_off) and is read with
-// transpose reads; output column (within the tile) = wn*128 + 16 nb + r16.
-// The side tile of block sb is [32 k][16 t] at kSideOff + 1024 sb.
-//   Direct (AOp::kDirect): requires every K tile full, N % 8 == 0, 16-byte
-//   aligned rows; columns past N are clamped to the last chunk (never
-//   stored).  A direct side operand needs r == 16 and NSIDE <= 1.
-//   Staged: 2 chunks of B and 2 of A per thread, zero-filled past K and N.
+// bf16 (staged): the B tile keeps the [k][n] layout (kn_off) and is read
+// with transpose reads; output column (within the tile) = wn*128 + 16 nb +
+// r16.  The side tile of block sb is [32 k][16 t] at kSideOff + 1024 sb.  Two
+// chunks of B and two of A per thread, zero-filled past K and N.
 template <class AOp, class KRow, class SRow, class SMask, int NSIDE>
 struct KNTrLoader {
-  static constexpr bool DIRECT = AOp::kDirect;
-  static constexpr int kDepth = DIRECT ? 3 : 1;
-  static constexpr int kLoads = 4 + (NSIDE > 0 ? 1 : 0);
   static constexpr bool kBTr = true;
-  static_assert(!DIRECT || NSIDE <= 1, "direct KN side operand: one block");
   AOp a;
   KRow krow;
   SRow srow;
@@ -869,58 +743,32 @@ struct KNTrLoader {
   long n0, N;
   int r;
   bool vecB, vecS;
-  u32x4 ra[DIRECT ? 1 : 2], rb[DIRECT ? 1 : 2], rs;
-  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
-    if constexpr (DIRECT) {
-      a.issue(kt, As);
-      const int L = threadIdx.x & 63;
-      const long k0 = (long)kt * 32;
-#pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int blk = direct_blk(it);
-        const int row = 2 * blk + (L >> 5);
-        const int lseg = (L & 31) ^ ftr(row);
-        const long col = min(n0 + lseg * 8, N - 8);
-        g2lds16(krow(k0 + row) + col, Bs + blk * 1024);
-      }
-      if constexpr (NSIDE > 0) {
-        if (L < 8) {
-          const int w = threadIdx.x >> 6, ci = 8 * w + L;
-          const bf16* p = srow(0, k0 + (ci >> 1));
-          g2lds16(p + 8 * (ci & 1), Bs + kSideOff + 128 * w);
-        }
-      }
-    }
-  }
+  u32x4 ra[2], rb[2], rs;
   __device__ __forceinline__ void load(int kt) {
-    if constexpr (!DIRECT) {
-      const int tid = threadIdx.x;
-      const long ka = (long)kt * 32 + (tid & 3) * 8;
+    const int tid = threadIdx.x;
+    const long ka = (long)kt * 32 + (tid & 3) * 8;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, ka);
-      const int seg = tid & 31, kr = tid >> 5;           // k rows kr, kr + 16
+    for (int qq = 0; qq < 2; ++qq) ra[qq] = a.get(qq, ka);
+    const int seg = tid & 31, kr = tid >> 5;           // k rows kr, kr + 16
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<bf16>(krow((long)kt * 32 + kr + 16 * qq), n0 + seg * 8, N, vecB);
-      if constexpr (NSIDE > 0) {
-        const int sb = tid >> 6, e = tid & 63;
-        rs = zero4();
-        if (sb < NSIDE) rs = gload<bf16>(srow(sb, (long)kt * 32 + (e >> 1)), (e & 1) * 8, r, vecS);
-      }
+    for (int qq = 0; qq < 2; ++qq) rb[qq] = gload<bf16>(krow((long)kt * 32 + kr + 16 * qq), n0 + seg * 8, N, vecB);
+    if constexpr (NSIDE > 0) {
+      const int sb = tid >> 6, e = tid & 63;
+      rs = zero4();
+      if (sb < NSIDE) rs = gload<bf16>(srow(sb, (long)kt * 32 + (e >> 1)), (e & 1) * 8, r, vecS);
     }
   }
   __device__ __forceinline__ void store(char* As, char* Bs) const {
-    if constexpr (!DIRECT) {
-      const int tid = threadIdx.x;
-      const int c = tid & 3, r0 = tid >> 2;
+    const int tid = threadIdx.x;
+    const int c = tid & 3, r0 = tid >> 2;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
-      const int seg = tid & 31, kr = tid >> 5;
+    for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(As + lds_off(r0 + 128 * qq, c)) = ra[qq];
+    const int seg = tid & 31, kr = tid >> 5;
 #pragma unroll
-      for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + kn_off(kr + 16 * qq, seg * 8)) = rb[qq];
-      if constexpr (NSIDE > 0) {
-        const int sb = tid >> 6, e = tid & 63;
-        if (sb < NSIDE) *reinterpret_cast<u32x4*>(Bs + kSideOff + sb * 1024 + 16 * e) = rs;
-      }
+    for (int qq = 0; qq < 2; ++qq) *reinterpret_cast<u32x4*>(Bs + kn_off(kr + 16 * qq, seg * 8)) = rb[qq];
+    if constexpr (NSIDE > 0) {
+      const int sb = tid >> 6, e = tid & 63;
+      if (sb < NSIDE) *reinterpret_cast<u32x4*>(Bs + kSideOff + sb * 1024 + 16 * e) = rs;
     }
   }
   __device__ __forceinline__ unsigned side_mask(int kt) const { return smask_of(kt); }
@@ -931,8 +779,6 @@ struct KNTrLoader {
 // 4 (k) x 2 (n) block of B.
 template <class KRow, class SRow, class SMask, int NSIDE>
 struct KNLoader32 {
-  static constexpr int kDepth = 1;
-  static constexpr int kLoads = 0;
   static constexpr bool kBTr = false;
   RowsA<float> a;
   KRow krow;
@@ -944,7 +790,6 @@ struct KNLoader32 {
   u32x4 ra[2];
   float rb[4][2];
   float rs;
-  __device__ __forceinline__ void issue(int, char*, char*) const {}
   __device__ __forceinline__ void load(int kt) {
     const int tid = threadIdx.x;
     const long ka = (long)kt * 16 + (tid & 3) * 4;
