@@ -133,7 +133,9 @@ typedef struct {
 /* ---- workspace queries (pass: 0 = forward, 1 = backward) ---------------- */
 size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass);
 size_t lora_qkv_workspace_bytes(const lora_qkv_desc_t* desc, int pass);
-/* 0 for the forward (which needs none; workspace may then be NULL). */
+/* The linear forward needs workspace only when few output tiles leave the
+ * GPU underfilled (small n_tokens: the K range is then split over several
+ * workgroups); when the query returns 0 the workspace may be NULL. */
 size_t lora_linear_workspace_bytes(const lora_linear_desc_t* desc, int pass);
 
 /*

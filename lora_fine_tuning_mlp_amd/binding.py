@@ -350,9 +350,11 @@ class Linear:
         self.dX = torch.empty(self.N, self.k, **e)
         self.grads = {"dA": torch.empty(self.r, self.k, **e), "dB": torch.empty(self.o, self.r, **e)}
         self.ws_bwd = torch.empty(max(1, lora_linear_workspace_bytes(self.desc, 1)), device=dev, dtype=torch.uint8)
+        nf = lora_linear_workspace_bytes(self.desc, 0)
+        self.ws_fwd = torch.empty(nf, device=dev, dtype=torch.uint8) if nf else None
 
     def forward(self, stream=None):
-        lora_linear_fwd(self.desc, self.t["X"], self.p, self.Y, self.T, None, stream)
+        lora_linear_fwd(self.desc, self.t["X"], self.p, self.Y, self.T, self.ws_fwd, stream)
         return self.Y
 
     def backward(self, dY, stream=None):

@@ -271,8 +271,7 @@ template <int ACT> __device__ __forceinline__ void act_both(float g, float& phi,
 // to the 8 XCDs; remap so each XCD gets a contiguous range of logical tiles,
 // then walk that range in groups of `gm` row blocks so CTAs resident on one
 // XCD share A row blocks and B column tiles in its L2.
-__device__ __forceinline__ void tile_coords(int ntiles, int R, int NC, int gm, int& rb, int& cb) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ void tile_coords_at(int b, int ntiles, int R, int NC, int gm, int& rb, int& cb) {
   const int per = ntiles >> 3, rem = ntiles & 7, x = b & 7, i = b >> 3;
   const int L = (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
   const int gsz = gm * NC;
@@ -282,6 +281,9 @@ __device__ __forceinline__ void tile_coords(int ntiles, int R, int NC, int gm, i
   const int w = L - grp * gsz;
   rb = first + w % g;
   cb = w / g;
+}
+__device__ __forceinline__ void tile_coords(int ntiles, int R, int NC, int gm, int& rb, int& cb) {
+  tile_coords_at(blockIdx.x, ntiles, R, NC, gm, rb, cb);
 }
 
 }  // namespace lora

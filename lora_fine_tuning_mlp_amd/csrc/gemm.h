@@ -338,16 +338,17 @@ struct NKPairLoader {
 
 template <int NSIDE>
 __device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<NSIDE>& ld, f32x4 (&acc)[kMB][8],
-                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB]) {
+                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
   const WaveId q = wave_id();
-  if (nkt <= 0) return;
-  ld.issue(0, smem, smem + kStage2A);
+  if (nkt <= kt0) return;
+  auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage2; };
+  ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
   sync_stage();
-  for (int kt = 0; kt < nkt; ++kt) {
-    const char* As = smem + (kt & 1) * kStage2;
+  for (int kt = kt0; kt < nkt; ++kt) {
+    const char* As = stage(kt);
     const char* Bs = As + kStage2A;
     if (kt + 1 < nkt) {
-      char* An = smem + ((kt + 1) & 1) * kStage2;
+      char* An = stage(kt + 1);
       ld.issue(kt + 1, An, An + kStage2A);
     }
 #pragma unroll
@@ -527,6 +528,89 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
     }
     sync_stage();
   }
+}
+
+// ---------------------------------------------------------------------------
+// Split K.  When a call has fewer output tiles than the chip has CUs, each
+// tile's K range is cut into S pieces run by S workgroups (blockIdx.x = tile
+// * S + split).  Each writes its fp32 accumulators, side accumulators and
+// (optionally) a parked side product from LDS to the workspace, then takes a
+// ticket from the tile's counter (zero before the launch).  The workgroup
+// holding the last ticket sums the S partials in split order, so the result
+// does not depend on which one finishes last, and runs the epilogue; the
+// others return.  No workgroup ever waits for another.
+// ---------------------------------------------------------------------------
+struct SplitK {
+  float* part;     // [tiles][S][kSplitFloats]
+  int* cnt;        // [tiles]
+  int S;           // 1: no split
+};
+constexpr int kSplitAcc = kMB * 8;                         // f32x4 accumulators per thread
+constexpr int kSplitSide = kMaxSide * kMB;                 // f32x4 side accumulators per thread
+constexpr int kSplitFlush = kBM * kSlot;                   // floats of one parked side product
+constexpr long kSplitFloats = (long)(kSplitAcc + kSplitSide) * 4 * kGemmThreads + kSplitFlush;
+
+// K tiles [kb, ke) of split `split` out of S over nkt tiles.
+__device__ __forceinline__ void split_range(int nkt, int S, int split, int& kb, int& ke) {
+  kb = (int)((long)split * nkt / S);
+  ke = (int)((long)(split + 1) * nkt / S);
+}
+
+template <int NS>
+__device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int split, f32x4 (&acc)[kMB][8],
+                                            f32x4 (&sacc)[NS > 0 ? NS : 1][kMB], float* flush) {
+  __shared__ int s_ticket;
+  // An opaque copy of the thread id: nothing derived from it (the partial's
+  // addresses) can be hoisted above the K-loop, where every register is taken.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  __syncthreads();                               // the flush area may have been written by other threads
+  f32x4* mine = reinterpret_cast<f32x4*>(sk.part + ((long)tile * sk.S + split) * kSplitFloats);
+#pragma unroll
+  for (int i = 0; i < kSplitAcc; ++i) mine[i * kGemmThreads + tid] = acc[i >> 3][i & 7];
+#pragma unroll
+  for (int sb = 0; sb < NS; ++sb)
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) mine[(kSplitAcc + sb * kMB + mb) * kGemmThreads + tid] = sacc[sb][mb];
+  float* myflush = reinterpret_cast<float*>(mine + (kSplitAcc + kSplitSide) * kGemmThreads);
+  if (flush)
+    for (int e = tid; e < kSplitFlush; e += kGemmThreads) myflush[e] = flush[e];
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_ticket = atomicAdd(sk.cnt + tile, 1);
+  __syncthreads();
+  if (s_ticket != sk.S - 1) return false;
+  __threadfence();
+#pragma unroll
+  for (int i = 0; i < kMB; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int sb = 0; sb < NS; ++sb)
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  if (flush)
+    for (int e = tid; e < kSplitFlush; e += kGemmThreads) flush[e] = 0.f;
+  for (int sp = 0; sp < sk.S; ++sp) {
+    const f32x4* pp = reinterpret_cast<const f32x4*>(sk.part + ((long)tile * sk.S + sp) * kSplitFloats);
+#pragma unroll
+    for (int i = 0; i < kSplitAcc; ++i) acc[i >> 3][i & 7] += pp[i * kGemmThreads + tid];
+#pragma unroll
+    for (int sb = 0; sb < NS; ++sb)
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] += pp[(kSplitAcc + sb * kMB + mb) * kGemmThreads + tid];
+    if (flush) {
+      const float* pf = reinterpret_cast<const float*>(pp + (kSplitAcc + kSplitSide) * kGemmThreads);
+      for (int e = tid; e < kSplitFlush; e += kGemmThreads) flush[e] += pf[e];
+    }
+  }
+  __syncthreads();
+  return true;
+}
+
+__global__ void k_split_zero(int* cnt, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) cnt[i] = 0;
 }
 
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[kMB][8]) {

@@ -676,14 +676,21 @@ struct MlpDxArgs {
   long N; int h, i, r;
   int vecA, vecW, vecS, vecO;
   int R, NC;
+  SplitK sk;                      // fast path only; sk.S == 1: no split
 };
 
-template <class T, bool FAST>
+// SPLIT (fast path only): the K range is split over a.sk.S workgroups per
+// tile; a separate instantiation, so the merge costs the unsplit kernel no
+// registers.
+template <class T, bool FAST, bool SPLIT = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   constexpr bool TR = sizeof(T) == 2;
+  static_assert(FAST || !SPLIT, "split K on the fast path only");
   __shared__ __align__(16) char smem[FAST ? kGemmLdsX : kGemmLds];
+  const int S = SPLIT ? a.sk.S : 1;
+  const int tile = blockIdx.x / S, split = blockIdx.x % S;
   int rb, cb;
-  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  tile_coords_at(tile, a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
   const long n0 = (long)cb * kBN;
   const long h = a.h, ni = a.i, r = a.r;
@@ -708,8 +715,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     ld.init(dG, dU, ni, ni, a.N, m0, h, n0, h, r);
     f32x4 sacc[1][kMB];
     zero_side(sacc);
-    const int nk0 = (int)(ni / 64), nk2 = 2 * nk0;
-    kloop2tr<1>(smem, nk0, ld, acc, sacc);
+    const int nk0 = (int)(ni / 64);
+    int kb, ke;                                      // this split's K tiles over both phases
+    split_range(2 * nk0, S, split, kb, ke);
+    kloop2tr<1>(smem, min(ke, nk0), ld, acc, sacc, kb);
     {
       const WaveId q = wave_id();
       float* fl = reinterpret_cast<float*>(smem + kFlushOff);
@@ -728,7 +737,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     zero_side(sacc);
     ld.srow.B = Bu;                                  // phase 2: B_u rows
     ld.srow.kb = ni;
-    kloop2tr<1>(smem, nk2, ld, acc, sacc, nk0);
+    kloop2tr<1>(smem, ke, ld, acc, sacc, max(kb, nk0));
+    if constexpr (SPLIT) {
+      if (!split_merge<1>(a.sk, tile, split, acc, sacc, reinterpret_cast<float*>(smem + kFlushOff))) return;
+    }
     side_reduce<T, 1>(smem, sacc, 1);                // dT_u -> slot 1
     {
       float* Ts = ts_ptr(smem);

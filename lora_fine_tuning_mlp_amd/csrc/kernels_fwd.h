@@ -150,14 +150,17 @@ struct LinearArgs {
   long N; int K, O, r;
   int vecA, vecW, vecS, vecO;
   int R, NC;
+  SplitK sk;           // fast path only; sk.S == 1: no split
 };
 
 template <class T, bool FAST>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   const WaveId q = wave_id();
+  const int S = FAST ? a.sk.S : 1;
+  const int tile = blockIdx.x / S, split = blockIdx.x % S;
   int rb, cb;
-  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  tile_coords_at(tile, a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
   const long n0 = (long)cb * kBN;
   const T* Z = static_cast<const T*>(a.Z);
@@ -183,7 +186,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
     ld.srow = A;
     const int sr = ld.side_row();
     if (sr >= 0) ld.srow = ld.side_ptr(A, sr, a.r, a.K, A);
-    kloop2<1>(smem, a.K / 64, ld, acc, sacc);
+    int kb, ke;
+    split_range(a.K / 64, S, split, kb, ke);
+    kloop2<1>(smem, ke, ld, acc, sacc, kb);
+    if (S > 1 && !split_merge<1>(a.sk, tile, split, acc, sacc, nullptr)) return;
   } else {
     NKLoader<T, RowsA<T>, 1> ld;
     ld.a.init(Z, nullptr, a.K, 0, a.K, a.N, m0, a.vecA);

@@ -38,7 +38,7 @@ int ok() {
 
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
-                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum", "k_qk_norm_bwd"};
+                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum", "k_qk_norm_bwd", "k_split_zero"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -132,10 +132,49 @@ struct Carver {
 };
 
 // MLP workspace.
+// Splits of a GEMM's K range when the call has fewer output tiles than the
+// chip has CUs (256 on MI355X): about one workgroup per CU, at least 8 K
+// tiles per split, at most 16 splits.  Shape-only, so the workspace queries
+// and the launches agree; used on the bf16 fast paths (K % 64 == 0).
+constexpr int kCUs = 256;
+int split_count(long tiles, long nkt) {
+  if (tiles <= 0 || tiles >= kCUs) return 1;
+  long S = kCUs / tiles;
+  if (S > nkt / 8) S = nkt / 8;
+  if (S > 16) S = 16;
+  return S < 1 ? 1 : (int)S;
+}
+struct SplitWs {
+  float* part = nullptr;
+  int* cnt = nullptr;
+  int S = 1;
+  long tiles = 0;
+};
+template <class C>
+SplitWs take_split(C& c, bool eligible, long tiles, long nkt) {
+  SplitWs sw;
+  sw.S = eligible ? split_count(tiles, nkt) : 1;
+  sw.tiles = tiles;
+  if (sw.S > 1) {
+    sw.part = c.template take<float>((size_t)tiles * sw.S * kSplitFloats * 4);
+    sw.cnt = c.template take<int>((size_t)tiles * 4);
+  }
+  return sw;
+}
+// Counter reset before a split launch; the kernels' SplitK argument.
+int split_prepare(const SplitWs& sw, hipStream_t st, SplitK& sk) {
+  sk.part = sw.part;
+  sk.cnt = sw.cnt;
+  sk.S = sw.S;
+  if (sw.S <= 1) return LORA_OK;
+  return launch(11, k_split_zero, dim3((unsigned)cdiv(sw.tiles, 256)), dim3(256), st, sw.cnt, (int)sw.tiles);
+}
+
 struct MlpWs {
   void* H;
   void *dG, *dU;
   float *dT_part, *dT, *pA_d, *pB_g, *pB_u, *pA_g, *pA_u, *pB_d;
+  SplitWs split;    // forward: down projection; backward: MLP dX
   int NCR, NCH, CPC;
   size_t bytes;
 };
@@ -149,9 +188,12 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
   w.NCH = (int)cdiv(h, BK);
   w.NCR = w.NCH < 8 ? w.NCH : 8;
   w.CPC = (int)cdiv(w.NCH, w.NCR);
+  const bool bf = d.dtype == LORA_BF16;
   if (pass == 0) {
     w.H = c.take<void>(N * i * es);
+    w.split = take_split(c, bf && i % 64 == 0, R * cdiv(h, kBN), i / 64);
   } else {
+    w.split = take_split(c, bf && i % 64 == 0 && d.rank == 16, R * cdiv(h, kBN), 2 * i / 64);
     w.dG = c.take<void>(N * i * es);
     w.dU = c.take<void>(N * i * es);
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
@@ -201,6 +243,7 @@ QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
 // LoRA linear workspace (backward only).
 struct LinWs {
   float *dT_part, *dT, *pA, *dB_part;
+  SplitWs split;    // forward
   int NCR, NCH, CPC;
   size_t bytes;
 };
@@ -213,6 +256,7 @@ LinWs lin_ws(const lora_linear_desc_t& d, int pass, void* base) {
   w.NCH = (int)cdiv(out, BK);
   w.NCR = w.NCH < 8 ? w.NCH : 8;
   w.CPC = (int)cdiv(w.NCH, w.NCR);
+  if (pass == 0) w.split = take_split(c, d.dtype == LORA_BF16 && in % 64 == 0, R * cdiv(out, kBN), in / 64);
   if (pass == 1) {
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
     w.dT = c.take<float>((size_t)3 * N * 16 * 4);
@@ -324,8 +368,13 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecO = (h % 8 == 0) && al16(Y);
     a.R = R; a.NC = (int)cdiv(h, kBN);
     const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W, dn.A}) && i % 64 == 0;
-    const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
-                                    dim3(kGemmThreads), st, a);
+    a.sk.S = 1;
+    if (sizeof(T) == 2 && fast) {
+      const int rc = split_prepare(w.split, st, a.sk);
+      if (rc) return rc;
+    }
+    const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>),
+                                    dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a);
     if (rc) return rc;
   }
   return ok();
@@ -391,8 +440,16 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       a.R = R; a.NC = (int)cdiv(h, kBN);
       const bool fast =
           fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 && i % 64 == 0;
-      const int rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
-                                      dim3(kGemmThreads), st, a);
+      a.sk.S = 1;
+      if (sizeof(T) == 2 && fast) {
+        const int rc = split_prepare(w.split, st, a.sk);
+        if (rc) return rc;
+      }
+      const int rc = a.sk.S > 1
+                         ? LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true, true>), (k_mlp_dx_bwd<T, false>),
+                                            dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a)
+                         : LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>),
+                                            dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
 }
@@ -602,7 +659,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
 // ---- LoRA linear ----------------------------------------------------------------
 template <class T>
 int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_t& p, void* Y, void* Tsv,
-                    hipStream_t st) {
+                    const LinWs& w, hipStream_t st) {
   const long N = d.n_tokens;
   if (N == 0) return ok();
   const int in = d.in_features, out = d.out_features, r = d.rank, V = vecw(DT<T>::code);
@@ -616,8 +673,13 @@ int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_
   a.vecO = (out % 8 == 0) && al16(Y);
   a.R = (int)cdiv(N, kBM); a.NC = (int)cdiv(out, kBN);
   const bool fast = fast_ok(DT<T>::code, in, N, {X, p.W, p.A}) && in % 64 == 0;
-  const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>), dim3(a.R * a.NC),
-                                  dim3(kGemmThreads), st, a);
+  a.sk.S = 1;
+  if (sizeof(T) == 2 && fast) {
+    const int rc = split_prepare(w.split, st, a.sk);
+    if (rc) return rc;
+  }
+  const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>),
+                                  dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a);
   if (rc) return rc;
   return ok();
 }
@@ -874,11 +936,13 @@ int lora_linear_fwd(const lora_linear_desc_t* desc, const void* X, const lora_pr
   if (rc) return rc;
   if ((rc = check_proj(proj, "proj"))) return rc;
   if (desc->n_tokens > 0 && (!X || !Y || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
-  (void)workspace;
-  (void)workspace_bytes;
+  const LinWs probe = lin_ws(*desc, 0, nullptr);
+  if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
+    return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
+  const LinWs w = lin_ws(*desc, 0, workspace);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
-  if (desc->dtype == LORA_BF16) return linear_fwd_impl<bf16>(*desc, X, *proj, Y, T, st);
-  return linear_fwd_impl<float>(*desc, X, *proj, Y, T, st);
+  if (desc->dtype == LORA_BF16) return linear_fwd_impl<bf16>(*desc, X, *proj, Y, T, w, st);
+  return linear_fwd_impl<float>(*desc, X, *proj, Y, T, w, st);
 }
 
 int lora_linear_bwd(const lora_linear_desc_t* desc, const void* dY, const void* X, const void* T,

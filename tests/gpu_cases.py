@@ -49,6 +49,9 @@ MLP_CASES = [
     S.MLPConfig("mlp_bf16_long_k", 256, 1024, 512, 16, 2.0, "geglu_tanh", "bf16"),
     S.MLPConfig("mlp_bf16_geglu_erf", 520, 256, 640, 16, 2.0, "geglu_erf", "bf16"),
     S.MLPConfig("mlp_f32_geglu_erf_ragged", 130, 96, 200, 7, 2.0, "geglu_erf", "f32"),
+    # few output tiles, long K: the down projection and dX split their K range
+    S.MLPConfig("mlp_bf16_splitk", 64, 512, 2048, 16, 2.0, "swiglu", "bf16"),
+    S.MLPConfig("mlp_bf16_splitk_cross", 100, 256, 1472, 16, 2.0, "geglu_tanh", "bf16"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
@@ -76,6 +79,7 @@ LINEAR_CASES = [
     S.LinearConfig("linear_bf16_tiny", 7, 8, 16, 1, 2.0, "bf16"),
     S.LinearConfig("linear_bf16_bias", 520, 512, 384, 16, 2.0, "bf16", bias=True),
     S.LinearConfig("linear_f32_bias_ragged", 90, 40, 70, 4, 2.0, "f32", bias=True),
+    S.LinearConfig("linear_bf16_splitk_uneven", 200, 1600, 256, 16, 2.0, "bf16", bias=True),
 ]
 
 

@@ -128,7 +128,11 @@ def _lin(**kw):
 
 
 def test_linear_workspace_queries():
-    assert B.lora_linear_workspace_bytes(_lin(), 0) == 0          # the forward needs none
+    assert B.lora_linear_workspace_bytes(_lin(), 0) == 0          # one tile, short K: no split
+    # one output tile with a long K range: the forward splits K and needs workspace
+    long_k = _lin(n_tokens=64, in_features=4096, out_features=256)
+    assert B.lora_linear_workspace_bytes(long_k, 0) > 4 * 256 * 256 * 4
+    assert B.lora_linear_workspace_bytes(_lin(n_tokens=64, in_features=4096, out_features=256, dtype="f32"), 0) == 0
     need = B.lora_linear_workspace_bytes(_lin(), 1)
     # at least the per-row-block dA partials [ceil(N/256)][in][16] and dB partials in float32
     assert need >= (128 + 96) * 16 * 4

@@ -201,7 +201,7 @@ def test_rope_position_zero_identity_on_device():
 
 
 def test_determinism():
-    for cfg in (gc.MLP_CASES[1], gc.QKV_CASES[0], gc.LINEAR_CASES[0]):
+    for cfg in (gc.MLP_CASES[1], gc.QKV_CASES[0], gc.LINEAR_CASES[0], gc.MLP_CASES[-1], gc.LINEAR_CASES[-1]):
         if isinstance(cfg, S.MLPConfig):
             t = S.mlp_inputs(cfg, 3)
             a, b = gc.run_mlp_gpu(cfg, t), gc.run_mlp_gpu(cfg, t)
