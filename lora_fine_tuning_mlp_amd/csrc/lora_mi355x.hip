@@ -452,7 +452,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
                                             dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
-}
+  }
   {
     RedArgs a{};
     a.r = r;
@@ -637,7 +637,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
                             dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
-}
+  }
   {
     RedArgs a{};
     a.r = r;
@@ -730,7 +730,7 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
                                       dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
-}
+  }
   {
     RedArgs a{};
     a.r = r;
