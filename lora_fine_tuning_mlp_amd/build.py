@@ -11,7 +11,7 @@ SRC = os.path.join(PKG, "csrc", "lora_mi355x.hip")
 HEADERS = [os.path.join(PKG, "csrc", f) for f in ("common.h", "gemm.h", "kernels_fwd.h", "kernels_bwd.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblora_mi355x.so")
-ARCH = os.environ.get("LORA_OFFLOAD_ARCH", "gfx950")
+ARCH = "gfx950"     # MI355X (CDNA4) only
 
 
 def hipcc_command(out: str) -> list:

@@ -37,8 +37,9 @@ int ok() {
 }
 
 // ---- timing ---------------------------------------------------------------
-const char* kNames[] = {"k_gateup_fwd", "k_linear_fwd", "k_rope_table", "k_qkv_fwd", "k_bwd_prologue",
-                        "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd", "k_reduce",   "k_dt_sum", "k_qk_norm_bwd", "k_split_zero"};
+const char* kNames[] = {"k_gateup_fwd",  "k_linear_fwd", "k_rope_table", "k_qkv_fwd",
+                        "k_bwd_prologue", "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd",
+                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd", "k_split_zero"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -78,6 +79,10 @@ int launch(int kid, Kern kern, dim3 grid, dim3 block, hipStream_t st, Args... ar
       e0 = take_event();
       e1 = take_event();
       timed = e0 && e1;
+      if (!timed) {                      // keep whichever event was made for later
+        if (e0) g_pool.push_back(e0);
+        if (e1) g_pool.push_back(e1);
+      }
     }
   }
   if (timed) (void)hipEventRecord(e0, st);
@@ -99,11 +104,6 @@ size_t esz(int dtype) { return dtype == LORA_BF16 ? 2 : 4; }
 size_t up256(size_t x) { return (x + 255) & ~size_t(255); }
 long cdiv(long a, long b) { return (a + b - 1) / b; }
 
-// Direct global->LDS loads need full bf16 K tiles, 16-byte aligned rows and
-// 32-bit row offsets (each call adds what its other operands need); other
-// calls take the register-staged (masked) loaders.
-bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> ptrs);
-
 // Launch Fast<true> when allowed (bf16 only), else Fast<false>.
 #define LORA_LAUNCH_FAST(kid, FAST_COND, KERN_TRUE, KERN_FALSE, grid, block, st, args)                   \
   ([&]() -> int {                                                                                        \
@@ -113,6 +113,9 @@ bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> pt
     return launch(kid, KERN_FALSE, grid, block, st, args);                                               \
   }())
 
+// Direct global->LDS loads need full bf16 K tiles, 16-byte aligned rows and
+// 32-bit row offsets (each call adds what its other operands need); other
+// calls take the register-staged (masked) loaders.
 bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> ptrs) {
   if (dtype != LORA_BF16 || K % ET<bf16>::BK != 0 || rows * K >= (1L << 31)) return false;
   for (const void* p : ptrs)
@@ -131,7 +134,6 @@ struct Carver {
   }
 };
 
-// MLP workspace.
 // Splits of a GEMM's K range when the call has fewer output tiles than the
 // chip has CUs (256 on MI355X): about one workgroup per CU, at least 8 K
 // tiles per split, at most 16 splits.  Shape-only, so the workspace queries
@@ -170,6 +172,7 @@ int split_prepare(const SplitWs& sw, hipStream_t st, SplitK& sk) {
   return launch(11, k_split_zero, dim3((unsigned)cdiv(sw.tiles, 256)), dim3(256), st, sw.cnt, (int)sw.tiles);
 }
 
+// MLP workspace.
 struct MlpWs {
   void* H;
   void *dG, *dU;
