@@ -8,8 +8,11 @@ no dW; elementwise work not counted) per second.
 
 Prints one JSON line.  Besides the headline value it carries
   legs:          separate legs, outside `value`: one LoRA linear fwd+bwd at
-                 the attention output projection's shape (8192 x 4096 -> 4096)
-                 and the headline QKV shape with per-head q/k RMSNorm;
+                 the attention output projection's shape (8192 x 4096 -> 4096),
+                 the headline QKV shape with per-head q/k RMSNorm, the GeGLU-tanh
+                 MLP at 8192 x 3072 -> 24576, and the small-shape regime
+                 (4 x 1024 tokens, h 896: MLP i 4864, QKV 14/2 heads of 64), each
+                 with its MFMA fraction and its HBM rate on planned bytes;
   roofline:      the dominant kernel's achieved TFLOP/s against the bf16
                  dense MFMA peak, timed live with HIP events around each launch
                  on the stream it runs on;
@@ -107,6 +110,75 @@ def bench_linear(cfg, steps: int, warmup: int):
             "kernels": kernels}
 
 
+def mlp_planned_bytes(cfg) -> int:
+    """HBM bytes one fused MLP fwd+bwd must move as planned: X twice, the
+    three base weights twice, Y, dY and dX, and the [N, i] intermediates
+    G, U (saved), H (forward workspace) and dG, dU (backward workspace), each
+    written once and read once."""
+    N, h, i = cfg.n_tokens, cfg.hidden, cfg.inter
+    e = 2 if cfg.dtype == "bf16" else 4
+    return e * (5 * N * h + 6 * h * i + 10 * N * i)
+
+
+def qkv_planned_bytes(cfg) -> int:
+    """HBM bytes of one fused QKV fwd+bwd as planned: X twice, dX, the base
+    weights twice, Q/K/V written, dQ/dK/dV read, and the token-major
+    gradient dP [N, O] (inverse RoPE applied) written and read back."""
+    N, h = cfg.n_tokens, cfg.hidden
+    O = sum(cfg.out_dims)
+    e = 2 if cfg.dtype == "bf16" else 4
+    return e * (3 * N * h + 2 * O * h + 4 * N * O)
+
+
+def with_rooflines(leg: dict, flops: int, planned_bytes: int) -> dict:
+    """Add the MFMA fraction and the achieved HBM rate on planned bytes."""
+    sec = leg["ms_per_step"] * 1e-3
+    leg["frac_peak"] = round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4)
+    leg["planned_bytes"] = planned_bytes
+    leg["hbm_gbs"] = round(planned_bytes / sec / 1e9, 1)
+    leg["hbm_frac"] = round(planned_bytes / sec / 1e9 / PEAK_HBM_GBS, 4)
+    return leg
+
+
+def qkv_kernel_flops(cfg):
+    N, h, r = cfg.n_tokens, cfg.hidden, cfg.rank
+    O = sum(cfg.out_dims)
+    return {"k_qkv_fwd": 2 * N * h * O + 6 * N * h * r + 2 * N * r * O,
+            "k_proj_dx_bwd": 2 * N * O * h + 12 * N * r * h}
+
+
+def mlp_kernel_flops(cfg):
+    N, h, i, r = cfg.n_tokens, cfg.hidden, cfg.inter, cfg.rank
+    return {"k_gateup_fwd": 4 * N * h * i + 4 * N * h * r + 4 * N * r * i,
+            "k_linear_fwd": 2 * N * i * h + 2 * N * i * r + 2 * N * r * h,
+            "k_down_bwd": 2 * N * h * i + 8 * N * r * i,
+            "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h}
+
+
+def bench_mlp(cfg, steps: int, warmup: int):
+    """LoRA MLP fwd+bwd at `cfg` on its own (GeGLU-tanh at h 3072, and the
+    small-shape regime).  Not part of `value`."""
+    import torch
+    from lora_fine_tuning_mlp_amd import binding as B
+    from lora_fine_tuning_mlp_amd import synthetic as S
+
+    dev = torch.device("cuda:0")
+    t = {k: v.to(dev) for k, v in S.mlp_inputs(cfg, 0).items()}
+    m = B.MLP({k: v for k, v in t.items() if k != "dY"}, cfg.n_tokens, cfg.hidden, cfg.inter, cfg.rank, cfg.dtype,
+              cfg.act, (cfg.scale,) * 3)
+    dY = t["dY"]
+
+    def step():
+        m.forward()
+        m.backward(dY)
+
+    ms, kernels = time_leg(step, steps, warmup, mlp_kernel_flops(cfg))
+    leg = {"workload": cfg.name, "tokens": cfg.n_tokens, "hidden": cfg.hidden, "inter": cfg.inter,
+           "rank": cfg.rank, "act": cfg.act, "ms_per_step": round(ms, 4),
+           "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
+    return with_rooflines(leg, cfg.flops(), mlp_planned_bytes(cfg))
+
+
 def bench_qkv(cfg, steps: int, warmup: int):
     """LoRA QKV fwd+bwd at `cfg` (used for the q/k-norm variant of the
     headline QKV shape).  Not part of `value`."""
@@ -124,9 +196,10 @@ def bench_qkv(cfg, steps: int, warmup: int):
         m.forward()
         m.backward(dQ, dK, dV)
 
-    ms, kernels = time_leg(step, steps, warmup)
-    return {"workload": cfg.name, "qk_norm": cfg.qk_norm, "bias": cfg.bias, "ms_per_step": round(ms, 4),
-            "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
+    ms, kernels = time_leg(step, steps, warmup, qkv_kernel_flops(cfg))
+    leg = {"workload": cfg.name, "tokens": cfg.n_tokens, "qk_norm": cfg.qk_norm, "bias": cfg.bias,
+           "ms_per_step": round(ms, 4), "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
+    return with_rooflines(leg, cfg.flops(), qkv_planned_bytes(cfg))
 
 
 def _unfused_mlp(t, act: str, s: float):
@@ -390,6 +463,10 @@ def main():
         legs = {"oproj": bench_linear(S.C_OPROJ, ls, lw),
                 "qkv_qknorm": bench_qkv(dataclasses.replace(qkv_cfg, name=qkv_cfg.name + "_qknorm", qk_norm=True),
                                         ls, lw)}
+        print("[bench] separate legs: GeGLU MLP at h 3072, small-shape MLP and QKV", file=sys.stderr, flush=True)
+        legs["mlp_geglu_h3072"] = bench_mlp(S.C3, ls, lw)
+        legs["small_mlp_h896"] = bench_mlp(S.C4_MLP, args.steps, lw)
+        legs["small_qkv_h896"] = bench_qkv(S.C4_QKV, args.steps, lw)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4

@@ -4,6 +4,8 @@ library (kernel durations, HBM traffic per launch).
     python -m lora_fine_tuning_mlp_amd.profiling stats  <kernel_stats.csv> <out.md> --cmd "<command>"
     python -m lora_fine_tuning_mlp_amd.profiling traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> <copy bytes> <out.json> <out.md> --cmd "<fetch cmd>" --cmd "<write cmd>"
+    python -m lora_fine_tuning_mlp_amd.profiling counters <counter_collection.csv> <out.md> --cmd "<command>" \
+        [--bench-flops]
 
 Traffic: FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Both are
 calibrated against the largest device copy kernel of the same run (a plain
@@ -115,6 +117,33 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: s
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
+def counters_summary(path: str, out: str, cmd: str, kflops=None) -> None:
+    """Per-kernel averages of rocprofv3 derived metrics (MfmaUtil, LdsUtil,
+    LDSBankConflict, MfmaFlopsBF16, ...) from one counter-collection run.
+    With `kflops` (kernel -> algorithmic FLOPs per launch) the table also
+    gives executed MFMA FLOPs over algorithmic FLOPs."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        k = base_name(r["Kernel_Name"])
+        if not k.startswith("k_"):
+            continue
+        vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    names = sorted({c for k in vals for c in vals[k]})
+    lines = ["# rocprofv3 derived counters per kernel (average over dispatches)", "", "Command:", "", "```", cmd, "```",
+             "", "| kernel | dispatches | " + " | ".join(names) + (" | MFMA FLOPs / algorithmic |" if kflops else " |"),
+             "|---|---:|" + "---:|" * len(names) + ("---:|" if kflops else "")]
+    for k in sorted(vals):
+        n = max(len(v) for v in vals[k].values())
+        row = [f"{sum(vals[k][c]) / len(vals[k][c]):.4g}" if vals[k].get(c) else "" for c in names]
+        extra = ""
+        if kflops:
+            mf = vals[k].get("MfmaFlopsBF16")
+            extra = f" {sum(mf) / len(mf) / kflops[k]:.3f} |" if (mf and k in kflops) else " |"
+        lines.append(f"| `{k}` | {n} | " + " | ".join(row) + " |" + extra)
+    lines += ["", f"HIP sources hash: `{source_hash()}`"]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -129,9 +158,24 @@ def main():
     t.add_argument("out_json")
     t.add_argument("out_md")
     t.add_argument("--cmd", action="append", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("out")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--bench-flops", action="store_true",
+                   help="divide MfmaFlopsBF16 by the headline step's algorithmic FLOPs per launch")
     a = ap.parse_args()
     if a.what == "stats":
         stats_summary(a.csv, a.out, a.cmd)
+    elif a.what == "counters":
+        kf = None
+        if a.bench_flops:
+            import sys
+            sys.path.insert(0, ROOT)
+            import bench
+            from lora_fine_tuning_mlp_amd import synthetic as S
+            kf = bench.kernel_flops(S.C1, S.C2)
+        counters_summary(a.csv, a.out, a.cmd, kf)
     else:
         traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.out_json, a.out_md, a.cmd)
 
