@@ -575,12 +575,17 @@ __device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int spli
   float* myflush = reinterpret_cast<float*>(mine + (kSplitAcc + kSplitSide) * kGemmThreads);
   if (flush)
     for (int e = tid; e < kSplitFlush; e += kGemmThreads) myflush[e] = flush[e];
-  __threadfence();
+  // Release only (write back, no invalidate): the workgroups that are not
+  // last never read anything the others wrote.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
   if (tid == 0) s_ticket = atomicAdd(sk.cnt + tile, 1);
   __syncthreads();
   if (s_ticket != sk.S - 1) return false;
-  __threadfence();
+  // The last workgroup acquires once; the barrier orders every wave's reads
+  // of the partials after it (one invalidation covers the CU and its L2).
+  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll

@@ -6,6 +6,7 @@
 // besides the optional timing recorder and the thread-local error message.
 #include "lora_mi355x.h"
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -135,14 +136,17 @@ struct Carver {
 };
 
 // Splits of a GEMM's K range when the call has fewer output tiles than the
-// chip has CUs (256 on MI355X): about one workgroup per CU, at least 8 K
-// tiles per split, at most 16 splits.  Shape-only, so the workspace queries
-// and the launches agree; used on the bf16 fast paths (K % 64 == 0).
+// chip has CUs (256 on MI355X).  S splits cost about nkt * c_k / S for the
+// K-loop and c_m * S for the merge (one workgroup reads the S partial tiles
+// one after another); measured on MI355X c_k ~ 1.7 us per K tile of 64 and
+// c_m ~ 10 us per 360 KB partial, so S ~ sqrt(0.17 nkt), at most one
+// workgroup per CU and 16 splits.  Shape-only, so the workspace queries and
+// the launches agree; used on the bf16 fast paths (K % 64 == 0).
 constexpr int kCUs = 256;
 int split_count(long tiles, long nkt) {
-  if (tiles <= 0 || tiles >= kCUs) return 1;
-  long S = kCUs / tiles;
-  if (S > nkt / 8) S = nkt / 8;
+  if (tiles <= 0 || tiles >= kCUs || nkt <= 0) return 1;
+  long S = (long)(std::sqrt(0.17 * (double)nkt) + 0.5);
+  if (S > kCUs / tiles) S = kCUs / tiles;
   if (S > 16) S = 16;
   return S < 1 ? 1 : (int)S;
 }
