@@ -336,8 +336,8 @@ struct NKPairLoader {
   }
 };
 
-template <int NSIDE>
-__device__ __forceinline__ void kloop2(char* smem, int nkt, const NKPairLoader<NSIDE>& ld, f32x4 (&acc)[kMB][8],
+template <int NSIDE, class Loader>
+__device__ __forceinline__ void kloop2(char* smem, int nkt, const Loader& ld, f32x4 (&acc)[kMB][8],
                                        f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
   const WaveId q = wave_id();
   if (nkt <= kt0) return;

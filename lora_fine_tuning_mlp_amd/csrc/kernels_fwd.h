@@ -284,6 +284,65 @@ struct QKVFwdArgs {
 
 // LG = log2(256 / head_dim): 1 for d = 128, 2 for d = 64 (RoPE pairs share a lane).
 // NS = the most projections any 256-column tile overlaps (side blocks held).
+// Fast-path loader of the head_dim-64 QKV forward (the interface of
+// NKPairLoader): every lane's X, W and adapter row pointers are derived afresh
+// in each issue() from an opaque thread id and the uniform arguments, so none
+// of them lives through the K-loop.  Kept there, they were spilled in these
+// variants, and each scratch reload's vmcnt wait serialised the tile's loads
+// (k_qkv_fwd took twice as long as at head_dim 128).  At head_dim 128 the
+// pointers fit and the stored-pointer loader is faster.
+template <int NSIDE, int LG>
+struct QKVRowLoader {
+  // Named fields, no arrays: a runtime index into a member array would put
+  // the whole loader in scratch memory.
+  const bf16* X;
+  const bf16 *W0, *W1, *W2;       // base weights of q, k, v
+  const bf16 *S0, *S1, *S2;       // adapter rows of side blocks 0..2 (nullptr past the tile's projections)
+  const bf16* afall;
+  long N, m0;
+  int h, n0, r;
+  int off1, off2, off3;           // projection column boundaries (off0 = 0)
+  unsigned smask;
+  __device__ __forceinline__ void issue(int kt, char* As, char* Bs) const {
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int L = tid & 63, w = tid >> 6;
+    const long k = (long)kt * 64 + ((L & 7) ^ (L >> 3)) * 8;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      long row = m0 + 8 * (w + 8 * it) + (L >> 3);
+      if (row > N - 1) row = N - 1;
+      g2lds16(X + row * h + k, As + (w + 8 * it) * 1024);
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int o = n0 + lds_row_col(LG, 8 * (w + 8 * it) + (L >> 3));
+      const bf16* p = W0;
+      if (o < off3) {
+        if (o < off1) p = W0 + (long)o * h;
+        else if (o < off2) p = W1 + (long)(o - off1) * h;
+        else p = W2 + (long)(o - off2) * h;
+      }
+      g2lds16(p + k, Bs + (w + 8 * it) * 1024);
+    }
+    if constexpr (NSIDE > 0) {
+      if (L < 16 * NSIDE) {
+        const int ci = w * 16 * NSIDE + L, sr = ci >> 3;
+        const int chunk = (ci & 7) ^ (sr & 7);
+        const int sl = sr >> 4;
+        // Opaque copies: a select among the members themselves is turned into
+        // a load from a selected member address, which keeps the loader in
+        // scratch memory.
+        unsigned long b0 = (unsigned long)S0, b1 = (unsigned long)S1, b2 = (unsigned long)S2;
+        asm volatile("" : "+v"(b0), "+v"(b1), "+v"(b2));
+        const bf16* base = reinterpret_cast<const bf16*>((sl == 0) ? b0 : ((sl == 1) ? b1 : b2));
+        const bf16* srow = base ? base + (long)min(sr & 15, r - 1) * h : afall;
+        g2lds16(srow + (long)kt * 64 + chunk * 8, Bs + kBN * kRow2 + w * 256 * NSIDE);
+      }
+    }
+  }
+};
+
 template <class T, int LG, bool FAST, int NS>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
@@ -295,14 +354,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   const int O = a.off[3];
   const T* X = static_cast<const T*>(a.X);
 
-  // Projections overlapping this tile, in q, k, v order -> fold / side slots.
-  int plist[3] = {0, 0, 0};
-  int nslot = 0;
-#pragma unroll
-  for (int p = 0; p < 3; ++p)
-    if (a.off[p] < min(n0 + kBN, O) && a.off[p + 1] > n0) plist[nslot++] = p;
+  // Projections overlapping this tile -> fold / side slots.  The projections
+  // are contiguous column ranges, so the tile overlaps a contiguous run of
+  // them: slot sl holds projection pfirst + sl, sl < nslot (plain arithmetic,
+  // no runtime-indexed array, which would live in scratch memory).
+  const int hi = min(n0 + kBN, O);
+  const int ov0 = (a.off[0] < hi && a.off[1] > n0) ? 1 : 0;
+  const int ov1 = (a.off[1] < hi && a.off[2] > n0) ? 1 : 0;
+  const int ov2 = (a.off[2] < hi && a.off[3] > n0) ? 1 : 0;
+  const int nslot = ov0 + ov1 + ov2;
+  const int pfirst = ov0 ? 0 : (ov1 ? 1 : 2);
   auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
-  auto slot_of = [&](int p) { return (plist[0] == p) ? 0 : ((plist[1] == p) ? 1 : 2); };
+  auto slot_of = [&](int p) { return p - pfirst; };
 
   auto brow_of = [&](int R) -> const T* {
     const int o = n0 + lds_row_col(LG, R);
@@ -310,18 +373,19 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     const int p = proj_of(o);
     return static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
   };
-  auto side_base = [&](int sl) -> const T* {        // side block sl: adapter of plist[sl]
+  auto side_base = [&](int sl) -> const T* {        // side block sl: adapter of projection pfirst + sl
     if (sl >= nslot) return nullptr;
-    const int pj = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
-    return static_cast<const T*>(a.A[pj]);
+    const int pj = pfirst + sl;
+    return static_cast<const T*>(pj == 0 ? a.A[0] : (pj == 1 ? a.A[1] : a.A[2]));
   };
-  const T* afall = static_cast<const T*>(a.A[plist[0]]);
+  const T* afall = static_cast<const T*>(pfirst == 0 ? a.A[0] : (pfirst == 1 ? a.A[1] : a.A[2]));
 
   f32x4 acc[kMB][8];
   f32x4 sacc[NS][kMB];
   zero_acc(acc);
   zero_side(sacc);
-  if constexpr (FAST) {
+  if constexpr (FAST && LG == 1) {
+    // head_dim 128: the per-lane row pointers fit in registers through the loop.
     NKPairLoader<NS> ld;
     ld.init_a(X, a.h, a.N, m0);
     ld.bfallback = static_cast<const T*>(a.W[0]);
@@ -331,6 +395,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     ld.srow = afall;
     const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
     if (sr >= 0) ld.srow = ld.side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
+    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
+  } else if constexpr (FAST) {
+    // head_dim 64: the row pointers are derived inside the loop.
+    QKVRowLoader<NS, LG> ld;
+    ld.X = X;
+    ld.W0 = static_cast<const T*>(a.W[0]);
+    ld.W1 = static_cast<const T*>(a.W[1]);
+    ld.W2 = static_cast<const T*>(a.W[2]);
+    ld.S0 = side_base(0);
+    ld.S1 = side_base(1);
+    ld.S2 = side_base(2);
+    ld.afall = afall;
+    ld.N = a.N; ld.m0 = m0; ld.h = a.h; ld.n0 = n0; ld.r = a.r;
+    ld.off1 = a.off[1]; ld.off2 = a.off[2]; ld.off3 = a.off[3];
+    ld.smask = (1u << nslot) - 1u;
     kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
   } else {
     NKLoader<T, RowsA<T>, NS> ld;
@@ -348,15 +427,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     kloop<T, NS>(smem, (a.h + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
   }
   side_reduce<T, NS>(smem, sacc);
+  // A fresh (opaque) wave id for everything after the K-loop: the one above
+  // dies with the loader set-up instead of staying live through the loop.
+  const WaveId qe = wave_id();
 
   // T_p is saved by the tile holding projection p's first column.
-  if (q.tid < kBM) {
+  if (qe.tid < kBM) {
     const float* Ts = ts_ptr(smem);
-    const long row = m0 + q.tid;
+    const long row = m0 + qe.tid;
     for (int sl = 0; sl < nslot; ++sl) {
-      const int p = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+      const int p = pfirst + sl;
       if (a.off[p] >= n0 && a.off[p] < n0 + kBN && row < a.N)
-        for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, q.tid, t)];
+        for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, qe.tid, t)];
     }
   }
 
@@ -372,7 +454,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   float fs[kMaxSide];
 #pragma unroll
   for (int sl = 0; sl < kMaxSide; ++sl) {
-    const int p = (sl == 0) ? plist[0] : ((sl == 1) ? plist[1] : plist[2]);
+    const int p = min(pfirst + sl, 2);
     fs[sl] = (p == 0) ? a.s[0] : ((p == 1) ? a.s[1] : a.s[2]);
   }
   fold<T>(smem, acc, nslot, fs, fb);
@@ -400,7 +482,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   float b1v[NG][cw], b2v[NG][cw];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+    const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
     const T* bp = nullptr;
     int oo = 0;
     if (o1 < O) {
@@ -418,7 +500,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
   float w1v[NG][cw], w2v[NG][cw];
 #pragma unroll
   for (int gi = 0; gi < NG; ++gi) {
-    const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+    const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
     const T* wp = nullptr;
     int jj = 0;
     if (a.norm && o1 < a.off[2]) {
@@ -439,11 +521,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     float cc[4][NG][cw], ss[4][NG][cw];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + acc_row(q, mb, j);
+      const long row = m0 + acc_row(qe, mb, j);
       const int s = (int)(row % a.S);
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
-        const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, 2 * cw * gi);
+        const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
         const int jj = (o1 - a.off[proj_of(o1)]) % a.d;
         if (row < a.N && o1 < O && proj_of(o1) < 2) {
           load_cw(cs + (long)s * half + jj, cc[j][gi]);
@@ -456,14 +538,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + acc_row(q, mb, j);
+      const long row = m0 + acc_row(qe, mb, j);
       if (row >= a.N) continue;
       const int s = (int)(row % a.S);
       const long bidx = row / a.S;
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         const int b1 = 2 * cw * gi;                  // first block of the pair group
-        const int o1 = n0 + q.wn * 128 + perm_col(LG, q.r16, b1);
+        const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, b1);
         if (o1 >= O) continue;
         const int p = proj_of(o1);
         const int oo = o1 - a.off[p];
@@ -487,7 +569,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
           T* pn = static_cast<T*>(a.Pn) + row * (long)a.off[2] + o1;
           gstore<T, cw>(pn, x1, cw, a.vecN);
           gstore<T, cw>(pn + half, x2, cw, a.vecN);
-          if (q.r16 == 0) a.rinv[row * nhqk + (p == 0 ? 0 : a.nh[0]) + hd] = ri;
+          if (qe.r16 == 0) a.rinv[row * nhqk + (p == 0 ? 0 : a.nh[0]) + hd] = ri;
 #pragma unroll
           for (int e = 0; e < cw; ++e) {
             x1[e] *= ri * w1v[gi][e];
