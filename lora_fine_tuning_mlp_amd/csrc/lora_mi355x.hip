@@ -138,14 +138,17 @@ struct Carver {
 // Splits of a GEMM's K range when the call has fewer output tiles than the
 // chip has CUs (256 on MI355X).  S splits cost about nkt * c_k / S for the
 // K-loop and c_m * S for the merge (one workgroup reads the S partial tiles
-// one after another); measured on MI355X c_k ~ 1.7 us per K tile of 64 and
-// c_m ~ 10 us per 360 KB partial, so S ~ sqrt(0.17 nkt), at most one
-// workgroup per CU and 16 splits.  Shape-only, so the workspace queries and
-// the launches agree; used on the bf16 fast paths (K % 64 == 0).
+// one after another).  Measured on MI355X: c_k ~ 1.7 us per K tile of 64;
+// c_m ~ 10 us per 360 KB partial with a few tiles merging, ~30 us with 64
+// (they share the fabric), i.e. c_m ~ 10 + 0.3 tiles.  So
+// S ~ sqrt(c_k nkt / c_m), at most one workgroup per CU and 16 splits.
+// Shape-only, so the workspace queries and the launches agree; used on the
+// bf16 fast paths (K % 64 == 0).
 constexpr int kCUs = 256;
 int split_count(long tiles, long nkt) {
   if (tiles <= 0 || tiles >= kCUs || nkt <= 0) return 1;
-  long S = (long)(std::sqrt(0.17 * (double)nkt) + 0.5);
+  const double c_m = 10.0 + 0.3 * (double)tiles;
+  long S = (long)(std::sqrt(1.7 * (double)nkt / c_m) + 0.5);
   if (S > kCUs / tiles) S = kCUs / tiles;
   if (S > 16) S = 16;
   return S < 1 ? 1 : (int)S;
