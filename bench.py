@@ -105,9 +105,10 @@ def bench_linear(cfg, steps: int, warmup: int):
         lin.backward(dY)
 
     ms, kernels = time_leg(step, steps, warmup, linear_kernel_flops(cfg))
-    return {"workload": cfg.name, "tokens": cfg.n_tokens, "in": cfg.in_features, "out": cfg.out_features,
-            "rank": cfg.rank, "ms_per_step": round(ms, 4), "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
-            "kernels": kernels}
+    leg = {"workload": cfg.name, "tokens": cfg.n_tokens, "in": cfg.in_features, "out": cfg.out_features,
+           "rank": cfg.rank, "ms_per_step": round(ms, 4), "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2),
+           "kernels": kernels}
+    return with_rooflines(leg, cfg.flops(), linear_planned_bytes(cfg))
 
 
 def mlp_planned_bytes(cfg) -> int:
@@ -128,6 +129,13 @@ def qkv_planned_bytes(cfg) -> int:
     O = sum(cfg.out_dims)
     e = 2 if cfg.dtype == "bf16" else 4
     return e * (3 * N * h + 2 * O * h + 4 * N * O)
+
+
+def linear_planned_bytes(cfg) -> int:
+    """HBM bytes of one LoRA linear fwd+bwd: Z twice, dZ, W twice, Y, dY."""
+    N, k, o = cfg.n_tokens, cfg.in_features, cfg.out_features
+    e = 2 if cfg.dtype == "bf16" else 4
+    return e * (3 * N * k + 2 * k * o + 2 * N * o)
 
 
 def with_rooflines(leg: dict, flops: int, planned_bytes: int) -> dict:

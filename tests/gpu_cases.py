@@ -67,6 +67,10 @@ QKV_CASES = [
                 qk_norm=True),
     S.QKVConfig("qkv_f32_norm_d64", 2, 70, 128, 4, 2, 64, 4, 1.5, 1.0e4, "f32", qk_norm=True, norm_eps=1e-5),
     S.QKVConfig("qkv_f32_norm_d128", 1, 40, 64, 2, 2, 128, 16, 2.0, 1.0e4, "f32", qk_norm=True, norm_eps=0.5),
+    # head_dim 64 on the fast path with one projection per tile (q 512, k 256,
+    # v 256 columns) and with q, k and v all in one 256-column tile
+    S.QKVConfig("qkv_bf16_d64_one_proj_per_tile", 2, 130, 128, 8, 4, 64, 16, 2.0, 1.0e4, "bf16"),
+    S.QKVConfig("qkv_bf16_d64_three_proj_tile", 1, 300, 256, 2, 1, 64, 8, 2.0, 1.0e6, "bf16", bias=True),
 ]
 
 
