@@ -373,8 +373,20 @@ __global__ __launch_bounds__(256) void k_dt_sum(const float* part, float* dT, in
   const int p = blockIdx.y;
   const long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;   // float4 index within [N][16]
   if (e4 >= N * 4) return;
+  // Partials are added in column-range order; they are loaded eight at a
+  // time so the loads overlap (the sums, and so the result, are unchanged).
+  const f32x4* src = reinterpret_cast<const f32x4*>(part + (long)p * N * 16) + e4;
+  const long stride = 3 * N * 4;                                  // float4s between column ranges
   f32x4 v = {0.f, 0.f, 0.f, 0.f};
-  for (int c = 0; c < NCR; ++c) v += reinterpret_cast<const f32x4*>(part + ((long)c * 3 + p) * N * 16)[e4];
+  int c = 0;
+  for (; c + 8 <= NCR; c += 8) {
+    f32x4 b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = src[(long)(c + u) * stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += b[u];
+  }
+  for (; c < NCR; ++c) v += src[(long)c * stride];
   reinterpret_cast<f32x4*>(dT + (long)p * N * 16)[e4] = v;
 }
 

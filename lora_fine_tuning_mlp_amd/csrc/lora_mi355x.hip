@@ -179,6 +179,22 @@ int split_prepare(const SplitWs& sw, hipStream_t st, SplitK& sk) {
   return launch(11, k_split_zero, dim3((unsigned)cdiv(sw.tiles, 256)), dim3(256), st, sw.cnt, (int)sw.tiles);
 }
 
+// Column ranges of the backward prologue (grid R x NCR, CPC chunks of BK
+// columns each): at least 8, more when there are few row blocks, so that the
+// grid still covers the CUs (a small call has R = 16 row blocks or fewer);
+// ranges that would get no chunk are dropped.
+void prologue_ranges(long NCH, long R, int& NCR, int& CPC) {
+  if (NCH <= 0) {
+    NCR = 0;
+    CPC = 0;
+    return;
+  }
+  long want = std::max(8L, cdiv(kCUs, std::max(1L, R)));
+  if (want > NCH) want = NCH;
+  CPC = (int)cdiv(NCH, want);
+  NCR = (int)cdiv(NCH, CPC);
+}
+
 // MLP workspace.
 struct MlpWs {
   void* H;
@@ -196,8 +212,7 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
   const size_t es = esz(d.dtype);
   const int BK = d.dtype == LORA_BF16 ? PT<bf16>::BK : PT<float>::BK;   // prologue column chunk
   w.NCH = (int)cdiv(h, BK);
-  w.NCR = w.NCH < 8 ? w.NCH : 8;
-  w.CPC = (int)cdiv(w.NCH, w.NCR);
+  prologue_ranges(w.NCH, R, w.NCR, w.CPC);
   const bool bf = d.dtype == LORA_BF16;
   if (pass == 0) {
     w.H = c.take<void>(N * i * es);
@@ -237,8 +252,7 @@ QkvWs qkv_ws(const lora_qkv_desc_t& d, int pass, void* base) {
   w.cs = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
   w.sn = c.take<float>((size_t)d.seq * (d.head_dim / 2) * 4);
   w.NCH = (int)(O / BK);
-  w.NCR = w.NCH < 8 ? w.NCH : 8;
-  w.CPC = w.NCR > 0 ? (int)cdiv(w.NCH, w.NCR) : 0;
+  prologue_ranges(w.NCH, R, w.NCR, w.CPC);
   if (pass == 1) {
     w.dP = c.take<void>(N * O * es);
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
@@ -264,8 +278,7 @@ LinWs lin_ws(const lora_linear_desc_t& d, int pass, void* base) {
   const long R = cdiv(N, kBM);
   const int BK = d.dtype == LORA_BF16 ? PT<bf16>::BK : PT<float>::BK;   // prologue column chunk
   w.NCH = (int)cdiv(out, BK);
-  w.NCR = w.NCH < 8 ? w.NCH : 8;
-  w.CPC = (int)cdiv(w.NCH, w.NCR);
+  prologue_ranges(w.NCH, R, w.NCR, w.CPC);
   if (pass == 0) w.split = take_split(c, d.dtype == LORA_BF16 && in % 64 == 0, R * cdiv(out, kBN), in / 64);
   if (pass == 1) {
     w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
