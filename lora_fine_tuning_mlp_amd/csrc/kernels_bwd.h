@@ -913,8 +913,19 @@ __global__ __launch_bounds__(256) void k_reduce(RedArgs a) {
   const int t = (int)(e & 15);
   const long col = e >> 4;
   if (t >= a.r) return;
+  // Row-block partials are added in row-block order, loaded eight at a time
+  // so the loads overlap (the sum is unchanged).
+  const float* src = jb.part + e;
   float v = 0.f;
-  for (int x = 0; x < jb.nslice; ++x) v += jb.part[(long)x * jb.stride + e];
+  int x = 0;
+  for (; x + 8 <= jb.nslice; x += 8) {
+    float b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = src[(long)(x + u) * jb.stride];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v += b[u];
+  }
+  for (; x < jb.nslice; ++x) v += src[(long)x * jb.stride];
   T* out = static_cast<T*>(jb.out);
   if (jb.transpose) out[(long)t * jb.cols + col] = from_f<T>(v);
   else out[col * a.r + t] = from_f<T>(v);
