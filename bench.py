@@ -310,6 +310,36 @@ def crossover(steps: int, warmup: int):
     return rows
 
 
+def step_distribution(qkv, mlp, dqkv, dY, steps: int, stream):
+    """Per-step timings from events recorded between the four calls of each
+    step (QKV fwd, QKV bwd, MLP fwd, MLP bwd): median, min and p90 of the
+    whole step, and the median of each call."""
+    import numpy as np
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        qkv.forward()
+        e[1].record(stream)
+        qkv.backward(*dqkv)
+        e[2].record(stream)
+        mlp.forward()
+        e[3].record(stream)
+        mlp.backward(dY)
+        e[4].record(stream)
+    torch.cuda.synchronize()
+    t = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])   # [steps][4] ms
+    whole = t.sum(axis=1)
+    r4 = lambda x: round(float(x), 4)
+    return {"median": r4(np.median(whole)), "min": r4(whole.min()), "p90": r4(np.percentile(whole, 90)),
+            "qkv_fwd_median": r4(np.median(t[:, 0])), "qkv_bwd_median": r4(np.median(t[:, 1])),
+            "mlp_fwd_median": r4(np.median(t[:, 2])), "mlp_bwd_median": r4(np.median(t[:, 3])),
+            "fwd_median": r4(np.median(t[:, 0] + t[:, 2])), "bwd_median": r4(np.median(t[:, 1] + t[:, 3])),
+            "steps": steps}
+
+
 def stored_traffic(kernel: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current sources (else None)."""
@@ -360,6 +390,25 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int, reps: int = 1):
     dt = time.perf_counter() - t0
     flops = reps * (qkv_s.flops() + mlp_s.flops())
     threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    # The tiny fp32 MLP (2 x 16 tokens, h 64) on one thread, as a fixed reference point.
+    from threadpoolctl import threadpool_limits
+    t0c = S.mlp_inputs(S.C0, 0)
+    pc = S.to_f64({k: v for k, v in t0c.items() if k != "dY"})
+    dYc = t0c["dY"].double().numpy()
+    with threadpool_limits(limits=1):
+        c0t = time.perf_counter()
+        for _ in range(20):
+            orc.mlp_fwd(pc, S.C0.act, S.C0.scale, S.C0.scale, S.C0.scale)
+            orc.mlp_bwd(pc, dYc, S.C0.act, S.C0.scale, S.C0.scale, S.C0.scale)
+        c0_s = (time.perf_counter() - c0t) / 20
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {
         "value": flops / dt / 1e12,
         "unit": "TFLOP/s",
@@ -368,6 +417,8 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int, reps: int = 1):
         "sample": f"{tokens} tokens of each workload (QKV as {qkv_s.batch} x {qkv_s.seq}; MLP {tokens} rows): "
                   f"fwd+bwd of both in float64 numpy, {reps} time(s), {dt:.2f} s wall",
         "seconds": dt,
+        "cpu_model": model,
+        "tiny_mlp_1thread_ms": round(1e3 * c0_s, 3),
     }
 
 
@@ -464,6 +515,11 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic, "kernel": dominant,
                 "flops_per_launch": kf[dominant], "avg_launch_us": round(per_kernel[dominant]["avg_us"], 2)}
 
+    # Distribution pass (after the timed region, same work): events between
+    # the four calls of every step give per-step median / min / p90 and the
+    # forward and backward medians of each op.
+    dist = step_distribution(qkv, mlp, (dQ, dK, dV), dY, args.steps, stream)
+
     legs = None
     if not args.no_legs:
         print("[bench] separate legs: o_proj linear, q/k-norm QKV", file=sys.stderr, flush=True)
@@ -493,6 +549,7 @@ def main():
                    "qkv_heads": f"{qkv_cfg.n_q}/{qkv_cfg.n_kv}x{qkv_cfg.head_dim}", "qkv_rank": qkv_cfg.rank,
                    "rope_theta": qkv_cfg.theta, "flops_per_step": flops_step},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "step_ms": dist,
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in per_kernel.items()},
