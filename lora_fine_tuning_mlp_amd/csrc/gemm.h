@@ -576,10 +576,16 @@ __device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int spli
   if (flush)
     for (int e = tid; e < kSplitFlush; e += kGemmThreads) myflush[e] = flush[e];
   // Release only (write back, no invalidate): the workgroups that are not
-  // last never read anything the others wrote.
+  // last never read anything the others wrote.  Every wave releases its own
+  // stores; thread 0 releases again after the barrier, right before the
+  // ticket, so the release that heads the ticket covers the whole workgroup's
+  // partial (the barrier orders the other waves' stores before it).
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  if (tid == 0) s_ticket = atomicAdd(sk.cnt + tile, 1);
+  if (tid == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    s_ticket = atomicAdd(sk.cnt + tile, 1);
+  }
   __syncthreads();
   if (s_ticket != sk.S - 1) return false;
   // The last workgroup acquires once; the barrier orders every wave's reads
