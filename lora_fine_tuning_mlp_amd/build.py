@@ -1,40 +1,75 @@
-"""Build the HIP library (liblora_mi355x.so) in-tree for gfx950 with hipcc."""
+"""Build the HIP library (liblora_mi355x.so) in-tree for gfx950 with hipcc.
+
+Two translation units: the library (host code and most kernels), compiled
+with the ILP-oriented instruction scheduling, and the gate/up GEMM and the
+split-K MLP dX kernel with their launchers, compiled with the default
+scheduling (measured per kernel; see the comment in that source); the
+objects are linked into one shared library.
+"""
 from __future__ import annotations
 
 import os
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SRC = os.path.join(PKG, "csrc", "lora_mi355x.hip")
+SRC_DEFAULT_SCHED = os.path.join(PKG, "csrc", "kernels_default_sched.hip")
 HEADERS = [os.path.join(PKG, "csrc", f) for f in ("common.h", "gemm.h", "kernels_fwd.h", "kernels_bwd.h")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "liblora_mi355x.so")
 ARCH = "gfx950"     # MI355X (CDNA4) only
 
 
-def hipcc_command(out: str) -> list:
-    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-    return [
-        hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+def _hipcc() -> str:
+    return os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def compile_commands(obj_main: str, obj_split: str) -> list:
+    common = [
+        _hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # Packed fp32 VALU forms stay off (the compiler still vectorises the rest).
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"),
-        SRC, "-o", out,
     ]
+    return [
+        # Instruction scheduling for ILP: measured on MI355X, the MLP dX GEMM
+        # 1878 -> 1791 us and the down-projection backward 1191 -> 1172 us
+        # against the default strategy.
+        common + ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-c", SRC, "-o", obj_main],
+        common + ["-c", SRC_DEFAULT_SCHED, "-o", obj_split],
+    ]
+
+
+def link_command(objs: list, out: str) -> list:
+    return [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+
+
+def _run(cmds: list, verbose: bool) -> None:
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
+    failed = None
+    for cmd, p in procs:
+        out, err = p.communicate()
+        if p.returncode != 0 and failed is None:
+            sys.stderr.write(out + err)
+            failed = p.returncode
+    if failed is not None:
+        raise RuntimeError(f"hipcc failed with exit code {failed}")
 
 
 def build(verbose: bool = False) -> str:
     """Compile the library every time it is called; returns the .so path."""
     tmp = LIB + ".tmp"
-    cmd = hipcc_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
+    with tempfile.TemporaryDirectory() as d:
+        objs = [os.path.join(d, "lora_mi355x.o"), os.path.join(d, "kernels_default_sched.o")]
+        _run(compile_commands(*objs), verbose)          # the two units compile in parallel
+        _run([link_command(objs, tmp)], verbose)
     os.replace(tmp, LIB)
     return LIB
 

@@ -619,7 +619,7 @@ __device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int spli
   return true;
 }
 
-__global__ void k_split_zero(int* cnt, int n) {
+static __global__ void k_split_zero(int* cnt, int n) {   // static: the header is in two translation units
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) cnt[i] = 0;
 }

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_qk_norm_bwd(NormBwdArgs a) {
 
 // dT[p][n][t] = sum over the prologue's column ranges c (fixed order) of its
 // partials [NCR][3][N][16], for the adapters p < nadp.  One float4 per thread.
-__global__ __launch_bounds__(256) void k_dt_sum(const float* part, float* dT, int NCR, long N) {
+static __global__ __launch_bounds__(256) void k_dt_sum(const float* part, float* dT, int NCR, long N) {
   const int p = blockIdx.y;
   const long e4 = (long)blockIdx.x * blockDim.x + threadIdx.x;   // float4 index within [N][16]
   if (e4 >= N * 4) return;

@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
 // ===========================================================================
 // RoPE angle table: cos/sin of s * theta^(-2j/d), evaluated in double.
 // ===========================================================================
-__global__ void k_rope_table(float* cs, float* sn, int S, int half, double theta) {
+static __global__ void k_rope_table(float* cs, float* sn, int S, int half, double theta) {
   const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (long)S * half) return;
   const int s = (int)(idx / half), j = (int)(idx % half);

@@ -21,6 +21,14 @@
 
 using namespace lora;
 
+namespace lora {
+// Defined in kernels_default_sched.hip (a translation unit of its own,
+// compiled with the default instruction scheduling).
+hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, dim3 grid, hipStream_t st);
+template <class T, int ACT>
+hipError_t launch_gateup(bool fast, const GateUpArgs& a, dim3 grid, hipStream_t st);
+}  // namespace lora
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -89,6 +97,35 @@ int launch(int kid, Kern kern, dim3 grid, dim3 block, hipStream_t st, Args... ar
   if (timed) (void)hipEventRecord(e0, st);
   hipLaunchKernelGGL(kern, grid, block, 0, st, args...);
   const hipError_t err = hipGetLastError();
+  if (timed) {
+    (void)hipEventRecord(e1, st);
+    std::lock_guard<std::mutex> lk(g_tm);
+    g_recs.push_back(Rec{kid, e0, e1});
+  }
+  if (err != hipSuccess) return fail(LORA_ERR_HIP, "%s launch failed: %s", kNames[kid], hipGetErrorString(err));
+  return LORA_OK;
+}
+
+// Timed launch through a callable that enqueues one kernel and returns the
+// launch status (for kernels compiled in another translation unit).
+template <class F>
+int launch_call(int kid, hipStream_t st, F enqueue) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  bool timed = false;
+  {
+    std::lock_guard<std::mutex> lk(g_tm);
+    if (g_timing) {
+      e0 = take_event();
+      e1 = take_event();
+      timed = e0 && e1;
+      if (!timed) {
+        if (e0) g_pool.push_back(e0);
+        if (e1) g_pool.push_back(e1);
+      }
+    }
+  }
+  if (timed) (void)hipEventRecord(e0, st);
+  const hipError_t err = enqueue();
   if (timed) {
     (void)hipEventRecord(e1, st);
     std::lock_guard<std::mutex> lk(g_tm);
@@ -376,8 +413,9 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
     a.R = R; a.NC = (int)cdiv(i, 128);
     const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W, g.A, u.A}) && h % 64 == 0;
-    const int rc = LORA_LAUNCH_FAST(0, fast, (k_gateup_fwd<T, ACT, true>), (k_gateup_fwd<T, ACT, false>),
-                                    dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+    const dim3 grid(a.R * a.NC);
+    const int rc = grid.x == 0 ? LORA_OK
+                               : launch_call(0, st, [&]() { return launch_gateup<T, ACT>(fast, a, grid, st); });
     if (rc) return rc;
   }
   {
@@ -468,11 +506,18 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
         const int rc = split_prepare(w.split, st, a.sk);
         if (rc) return rc;
       }
-      const int rc = a.sk.S > 1
-                         ? LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true, true>), (k_mlp_dx_bwd<T, false>),
-                                            dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a)
-                         : LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>),
-                                            dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+      int rc = LORA_OK;
+      bool split = false;
+      if constexpr (sizeof(T) == 2) {
+        if (a.sk.S > 1) {                          // set only on the bf16 fast path
+          const dim3 grid(a.R * a.NC * a.sk.S);
+          rc = launch_call(6, st, [&]() { return launch_mlp_dx_split_bf16(a, grid, st); });
+          split = true;
+        }
+      }
+      if (!split)
+        rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
+                              dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
   }
