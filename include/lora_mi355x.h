@@ -139,7 +139,10 @@ size_t lora_qkv_workspace_bytes(const lora_qkv_desc_t* desc, int pass);
 size_t lora_linear_workspace_bytes(const lora_linear_desc_t* desc, int pass);
 
 /*
- * MLP forward.
+ * MLP forward.  Defined by Opake, "Model Patches and Kernels", section "Fused
+ * LoRA operations" (opake_lora_mlp: gate, up and down LoRA projections with
+ * the activation between them) and section "Activation functions" (SwiGLU
+ * silu(gate) * up, GeGLU gelu_tanh(gate) * up or gelu(gate) * up).
  *   X [N, h]; gate, up: W [i, h], A [r, h], B [i, r]; down: W [h, i], A [r, i], B [h, r].
  *   Writes Y [N, h] = L_d(H) with H = phi(G) * U, and the saved tensors
  *   G = L_g(X), U = L_u(X) [N, i] (pre-activation, call dtype) and
@@ -151,7 +154,12 @@ int lora_mlp_fwd(const lora_mlp_desc_t* desc, const void* X,
                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * MLP backward for the loss <dY, Y>, base weights frozen.
+ * MLP backward for the loss <dY, Y>, base weights frozen.  Defined by the
+ * same passages as the forward (Opake, "Model Patches and Kernels", "Fused
+ * LoRA operations": the autograd pair of opake_lora_mlp; "Activation
+ * functions": the activation backward reads the upstream gradient, gate and
+ * up and writes both input gradients; "Fused linear cross-entropy", key design
+ * decisions: frozen weights get no weight gradient).
  *   dY [N, h]; X, G, U, T as written by lora_mlp_fwd; same projections.
  *   Writes dX [N, h] and the adapter gradients dA_* [r, in], dB_* [out, r]
  *   (call dtype, float32 accumulation).
@@ -164,7 +172,12 @@ int lora_mlp_bwd(const lora_mlp_desc_t* desc, const void* dY, const void* X,
                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
- * QKV forward.
+ * QKV forward.  Defined by Opake, "Model Patches and Kernels", section "Fused
+ * LoRA operations" (opake_lora_qkv: the Q, K and V LoRA projections of one
+ * input in one call) and section "Rotary position embeddings (RoPE)" (RoPE
+ * on Q and K together, grouped-query head counts), and by Axolotl,
+ * "monkeypatch.lora_kernels", "original_apply_qkv" (hidden states in, query,
+ * key and value out).
  *   X [batch*seq, h]; q: W [n_q*d, h], A [r, h], B [n_q*d, r]; k, v: W [n_kv*d, h], ...
  *   Writes Q [batch, n_q, seq, d], K, V [batch, n_kv, seq, d] (RoPE on Q and K)
  *   and T [3, N, r] float32 = (X A_q^T, X A_k^T, X A_v^T).
@@ -176,6 +189,9 @@ int lora_qkv_fwd(const lora_qkv_desc_t* desc, const void* X,
 
 /*
  * QKV backward for the loss <dQ,Q> + <dK,K> + <dV,V>, base weights frozen.
+ * Defined by the same passages as the forward (the autograd pair of
+ * opake_lora_qkv; the RoPE backward is the transposed rotation) and by "Fused
+ * linear cross-entropy", key design decisions (no gradient for frozen W).
  *   dQ, dK, dV in the layouts of Q, K, V; X and T as for the forward.
  *   Writes dX [N, h] and dA_* [r, h], dB_* [out, r].
  */

@@ -1,7 +1,11 @@
 """GPU parity at the benchmark's full sizes, in the launch configuration
 bench.py times (same binding classes, same kernels).
 
-Every output row (Y, G, U, T, dX; Q, K, V) depends only on its own token,
+The two headline workloads (the 4 x 2048-token QKV and the 8192-token MLP at
+h 4096) are compared unmasked, every element of every output against the
+oracle's full run, for seeds 0, 1 and 2.
+
+For the other full sizes every output row (Y, G, U, T, dX; Q, K, V) depends only on its own token,
 and zeroing the upstream gradient outside a set of rows removes every other
 row's contribution to dA and dB.  So the GPU runs the whole problem, the
 upstream gradient is masked to a row sample, and the CPU oracle runs on the
@@ -61,6 +65,34 @@ def test_mlp_full_size(cfg):
     # Rows outside the sample had zero upstream gradient: their dX is exactly 0.
     others = np.setdiff1d(np.arange(cfg.n_tokens), rows)
     assert not np.any(out["dX"][others]), "dX non-zero where dY is zero"
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_mlp_c2_unmasked(seed):
+    """Every row of Y, G, U, T and dX and the complete adapter gradients of the
+    8192-token MLP, against the oracle on the same inputs."""
+    cfg = S.C2
+    gc.say(f"unmasked mlp {cfg.name} seed={seed}: generating inputs")
+    t = S.mlp_inputs(cfg, seed)
+    gc.say(f"unmasked mlp {cfg.name} seed={seed}: GPU")
+    out = gc.run_mlp_gpu(cfg, t)
+    gc.say(f"unmasked mlp {cfg.name} seed={seed}: oracle")
+    ref = gc.run_mlp_oracle(cfg, t)
+    gc.compare(f"{cfg.name}/unmasked/s{seed}", out, ref, gc.TOL[cfg.dtype])
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_qkv_c1_unmasked(seed):
+    """All four sequences of the 4 x 2048-token QKV (Q, K, V, T, dX and the
+    adapter gradients), against the oracle on the same inputs."""
+    cfg = S.C1
+    gc.say(f"unmasked qkv {cfg.name} seed={seed}: generating inputs")
+    t = S.qkv_inputs(cfg, seed)
+    gc.say(f"unmasked qkv {cfg.name} seed={seed}: GPU")
+    out = gc.run_qkv_gpu(cfg, t)
+    gc.say(f"unmasked qkv {cfg.name} seed={seed}: oracle")
+    ref = gc.run_qkv_oracle(cfg, t)
+    gc.compare(f"{cfg.name}/unmasked/s{seed}", out, ref, gc.TOL[cfg.dtype])
 
 
 def test_mlp_full_size_deterministic():

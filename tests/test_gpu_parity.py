@@ -24,7 +24,7 @@ def _need_gpu():
 
 
 @pytest.mark.parametrize("cfg", gc.MLP_CASES, ids=lambda c: c.name)
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_mlp_parity(cfg, seed):
     gc.say(f"mlp parity {cfg.name} seed={seed}")
     t = S.mlp_inputs(cfg, seed)
@@ -32,7 +32,7 @@ def test_mlp_parity(cfg, seed):
 
 
 @pytest.mark.parametrize("cfg", gc.QKV_CASES, ids=lambda c: c.name)
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_qkv_parity(cfg, seed):
     gc.say(f"qkv parity {cfg.name} seed={seed}")
     t = S.qkv_inputs(cfg, seed)
@@ -91,7 +91,7 @@ def test_qkv_special_cases(cfg):
 
 
 @pytest.mark.parametrize("cfg", gc.LINEAR_CASES, ids=lambda c: c.name)
-@pytest.mark.parametrize("seed", [0, 1])
+@pytest.mark.parametrize("seed", [0, 1, 2])
 def test_linear_parity(cfg, seed):
     gc.say(f"linear parity {cfg.name} seed={seed}")
     t = S.linear_inputs(cfg, seed)
