@@ -201,6 +201,25 @@ int lora_qkv_bwd(const lora_qkv_desc_t* desc, const void* dQ, const void* dK, co
                  void* dX, void* dA_q, void* dB_q, void* dA_k, void* dB_k, void* dA_v, void* dB_v,
                  void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * QKV forward that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid it).  Same arguments, results and errors as
+ * lora_qkv_fwd without the workspace pair: its scratch (the RoPE cos / sin
+ * table, lora_qkv_workspace_bytes(desc, 0) bytes) lives in a static device
+ * array of lora_qkv_fwd_noalloc_max_scratch_bytes() bytes (4 MiB: seq *
+ * head_dim up to 524288) that each GPU holds until the process ends.  Larger
+ * shapes return LORA_ERR_WORKSPACE before any device call.  Every call on one
+ * GPU shares that GPU's array (nothing in it needs to start at zero; each call
+ * rewrites the table before use), so calls that overlap on one GPU, on
+ * different streams or from different threads, race.  The stream must belong
+ * to the current device.
+ */
+int lora_qkv_fwd_noalloc(const lora_qkv_desc_t* desc, const void* X,
+                         const lora_proj_t* q, const lora_proj_t* k, const lora_proj_t* v,
+                         void* Q, void* K, void* V, void* T, void* hip_stream);
+size_t lora_qkv_fwd_noalloc_max_scratch_bytes(void);
+
 /* Per-head RMSNorm of Q and K (q_norm / k_norm) between the projection and
  * RoPE: each head x [head_dim] becomes x / sqrt(mean(x^2) + eps) * w, with
  * one weight vector w [head_dim] (call dtype) for all Q heads and one for all

@@ -66,6 +66,9 @@ _SIGS = {
                                     ctypes.c_size_t, _P]),
     "lora_qkv_fwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, ctypes.POINTER(Proj), ctypes.POINTER(Proj),
                                     ctypes.POINTER(Proj), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "lora_qkv_fwd_noalloc": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, ctypes.POINTER(Proj), ctypes.POINTER(Proj),
+                                            ctypes.POINTER(Proj), _P, _P, _P, _P, _P]),
+    "lora_qkv_fwd_noalloc_max_scratch_bytes": (ctypes.c_size_t, []),
     "lora_qkv_bwd": (ctypes.c_int, [ctypes.POINTER(QkvDesc), _P, _P, _P, _P, _P, ctypes.POINTER(Proj),
                                     ctypes.POINTER(Proj), ctypes.POINTER(Proj), _P, _P, _P, _P, _P, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
@@ -277,6 +280,18 @@ def lora_qkv_fwd(desc, X, q: Proj, k: Proj, v: Proj, Q, K, V, T, workspace, stre
     _check(lib().lora_qkv_fwd(ctypes.byref(desc), _ptr(X), ctypes.byref(q), ctypes.byref(k), ctypes.byref(v),
                               _ptr(Q), _ptr(K), _ptr(V), _ptr(T), _ptr(workspace), workspace.numel(),
                               _stream(stream)))
+
+
+def lora_qkv_fwd_noalloc(desc, X, q: Proj, k: Proj, v: Proj, Q, K, V, T, stream=None):
+    N, h, Oq, Ok, r, dt = _need_qkv_common(desc, X, q, k, v, T)
+    for t, n, m in ((Q, "Q", N * Oq), (K, "K", N * Ok), (V, "V", N * Ok)):
+        _need(t, n, dt, m)
+    _check(lib().lora_qkv_fwd_noalloc(ctypes.byref(desc), _ptr(X), ctypes.byref(q), ctypes.byref(k),
+                                      ctypes.byref(v), _ptr(Q), _ptr(K), _ptr(V), _ptr(T), _stream(stream)))
+
+
+def lora_qkv_fwd_noalloc_max_scratch_bytes() -> int:
+    return int(lib().lora_qkv_fwd_noalloc_max_scratch_bytes())
 
 
 def _need_qkv_grads(desc, dQ, dK, dV, dX, dA_q, dB_q, dA_k, dB_k, dA_v, dB_v):

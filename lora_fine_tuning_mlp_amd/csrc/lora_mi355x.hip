@@ -833,6 +833,40 @@ int check_norm(const lora_qkv_desc_t* desc, const lora_qk_norm_t* norm, const vo
 }
 }  // namespace
 
+// ---- allocation-free variant: a file-scope device scratch array -------------
+// Callers that cannot allocate (code under graph capture, tight serving loops)
+// use lora_qkv_fwd_noalloc, which keeps its scratch (the RoPE cos / sin table)
+// in this array instead of a workspace argument.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: only the address hipGetSymbolAddress
+// returns for the current device is ever handed to a kernel.
+constexpr size_t kNoAllocScratchBytes = size_t(4) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_dev[kMaxDevices] = {};
+
+// The current device's copy of `scratch`, looked up once per device.
+int scratch_for_current_device(char** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LORA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LORA_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(LORA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_dev[dev] = static_cast<char*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return LORA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 size_t lora_mlp_workspace_bytes(const lora_mlp_desc_t* desc, int pass) {
@@ -918,6 +952,31 @@ int lora_qkv_fwd(const lora_qkv_desc_t* desc, const void* X, const lora_proj_t* 
   if (probe.bytes > 0 && (!workspace || workspace_bytes < probe.bytes))
     return fail(LORA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, probe.bytes);
   const QkvWs w = qkv_ws(*desc, 0, workspace);
+  hipStream_t st = static_cast<hipStream_t>(hip_stream);
+  const lora_proj_t* const pr[3] = {q, k, v};
+  void* const out[3] = {Q, K, V};
+  if (desc->dtype == LORA_BF16) return qkv_fwd_impl<bf16>(*desc, X, pr, out, T, w, st);
+  return qkv_fwd_impl<float>(*desc, X, pr, out, T, w, st);
+}
+
+size_t lora_qkv_fwd_noalloc_max_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+int lora_qkv_fwd_noalloc(const lora_qkv_desc_t* desc, const void* X, const lora_proj_t* q, const lora_proj_t* k,
+                         const lora_proj_t* v, void* Q, void* K, void* V, void* T, void* hip_stream) {
+  int rc = check_qkv(desc);
+  if (rc) return rc;
+  if ((rc = check_proj(q, "q")) || (rc = check_proj(k, "k")) || (rc = check_proj(v, "v"))) return rc;
+  if (desc->batch > 0 && (!X || !Q || !K || !V || !T)) return fail(LORA_ERR_NULL, "a tensor pointer is NULL");
+  const QkvWs probe = qkv_ws(*desc, 0, nullptr);
+  if (probe.bytes > kNoAllocScratchBytes)
+    return fail(LORA_ERR_WORKSPACE,
+                "the allocation-free QKV forward needs %zu bytes of scratch (RoPE table of seq %d x head_dim %d), "
+                "its static buffer holds %zu: use lora_qkv_fwd with a workspace",
+                probe.bytes, desc->seq, desc->head_dim, kNoAllocScratchBytes);
+  if (desc->batch == 0) return ok();                 // nothing to compute, no device call
+  char* base = nullptr;
+  if ((rc = scratch_for_current_device(&base))) return rc;
+  const QkvWs w = qkv_ws(*desc, 0, base);
   hipStream_t st = static_cast<hipStream_t>(hip_stream);
   const lora_proj_t* const pr[3] = {q, k, v};
   void* const out[3] = {Q, K, V};

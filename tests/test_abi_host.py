@@ -205,3 +205,20 @@ def test_kernel_names_listed():
     for k in ("k_gateup_fwd", "k_linear_fwd", "k_qkv_fwd", "k_down_bwd", "k_mlp_dx_bwd", "k_proj_dx_bwd",
               "k_qk_norm_bwd"):
         assert k in names
+
+
+def test_noalloc_qkv_forward_is_exported_and_bounded():
+    """The allocation-free QKV forward reports its fixed scratch size and
+    refuses, before any device call, a shape whose RoPE table exceeds it."""
+    lib = B.lib()
+    cap = B.lora_qkv_fwd_noalloc_max_scratch_bytes()
+    assert cap == 4 << 20
+    pr = B.Proj(FAKE.value, FAKE.value, FAKE.value, 2.0)
+    f = FAKE
+    too_long = _qkv(batch=1, seq=cap // (64 * 4) + 8, head_dim=128)
+    assert B.lora_qkv_workspace_bytes(too_long, 0) > cap
+    assert lib.lora_qkv_fwd_noalloc(ctypes.byref(too_long), f, ctypes.byref(pr), ctypes.byref(pr), ctypes.byref(pr),
+                                    f, f, f, f, None) == 4
+    assert b"static buffer" in lib.lora_last_error_message()
+    assert lib.lora_qkv_fwd_noalloc(ctypes.byref(_qkv(batch=0)), f, ctypes.byref(pr), ctypes.byref(pr),
+                                    ctypes.byref(pr), f, f, f, f, None) == 0
