@@ -77,6 +77,22 @@ __device__ __forceinline__ WaveId wave_id() {
   q.r16 = q.lane & 15;
   return q;
 }
+// The same from an opaque copy of the thread id: nothing derived from it can
+// be hoisted above a K-loop (where every register is taken) by a compiler
+// that sees the same values are needed after it.
+__device__ __forceinline__ WaveId wave_id_opaque() {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  WaveId q;
+  q.tid = tid;
+  q.lane = tid & 63;
+  q.w = tid >> 6;
+  q.wm = q.w >> 1;
+  q.wn = q.w & 1;
+  q.g = q.lane >> 4;
+  q.r16 = q.lane & 15;
+  return q;
+}
 // Output row (within the tile) of C-layout element j of block mb.
 __device__ __forceinline__ int acc_row(const WaveId& q, int mb, int j) { return q.wm * 64 + mb * 16 + 4 * q.g + j; }
 
@@ -326,7 +342,7 @@ struct NKPairLoader {
       g2lds16(p + k, Bs + direct_blk(it) * 1024);
     }
     if constexpr (NSIDE > 0) {
-      if (L < 16 * NSIDE) {
+      if (L < 16 * NSIDE && smask != 0u) {
         const int w = threadIdx.x >> 6;
         const int ci = w * 16 * NSIDE + L, sr = ci >> 3;
         const int chunk = (ci & 7) ^ (sr & 7);
@@ -336,13 +352,17 @@ struct NKPairLoader {
   }
 };
 
+// prefetched: the caller already issued tile kt0 into stage 0 (a workgroup
+// walking several output tiles issues the next tile's first K tile before its
+// fold and epilogue); the loop then only waits for it.
 template <int NSIDE, class Loader>
 __device__ __forceinline__ void kloop2(char* smem, int nkt, const Loader& ld, f32x4 (&acc)[kMB][8],
-                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0) {
+                                       f32x4 (&sacc)[NSIDE > 0 ? NSIDE : 1][kMB], int kt0 = 0,
+                                       bool prefetched = false) {
   const WaveId q = wave_id();
   if (nkt <= kt0) return;
   auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage2; };
-  ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
+  if (!prefetched) ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
   sync_stage();
   for (int kt = kt0; kt < nkt; ++kt) {
     const char* As = stage(kt);
@@ -529,6 +549,8 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
     sync_stage();
   }
 }
+
+
 
 // ---------------------------------------------------------------------------
 // Split K.  When a call has fewer output tiles than the chip has CUs, each
@@ -1111,6 +1133,75 @@ __device__ __forceinline__ void reduce_store_partials(char* smem, f32x4 (&pacc)[
         const long col = n0 + q.wn * 128 + perm_col(0, q.r16, nb);
         if (col < ncols) *reinterpret_cast<f32x4*>(part[o] + col * 16 + 4 * q.g) = v;
       }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// Runs.  A workgroup walks a run of L consecutive column tiles of one row
+// block (the last run of a row block may be shorter).  The rank-r side
+// product of the row block is computed in the run's first tile only and its
+// fold operand stays in LDS for the rest of the run; the next tile's first K
+// tile is issued before the current tile's fold and epilogue.  Runs are
+// numbered row block by row block and handed to the 8 XCDs in contiguous
+// ranges (consecutive blockIdx go round-robin to the XCDs), so the workgroups
+// of one XCD share a few row blocks, and at any moment every XCD reads the
+// same few weight column blocks.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void run_coords(int nruns, int RPB, int L, int NC, int& rb, int& cb0, int& cb1) {
+  const int b = blockIdx.x;
+  const int per = nruns >> 3, rem = nruns & 7, x = b & 7, i = b >> 3;
+  const int u = (x < rem) ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+  rb = u / RPB;
+  cb0 = (u % RPB) * L;
+  cb1 = min(NC, cb0 + L);
+}
+
+// LDS of a run workgroup: the two K-loop stages, then the run's fold A operand
+// (scale * T in bf16, [256 rows][32 K], 64-byte rows).  It starts inside stage
+// 1's side-row area, which only the run's first tile loads (before the
+// operand is built).  After a K-loop, stage 1 holds the side products (fp32)
+// and the fold B tile while stage 0 takes the next tile's first K tile.
+constexpr int kRunFAOff = kStage2 + kStage2A + kBN * kRow2;      // stage 1's side rows
+constexpr int kRunLds = kRunFAOff + kBM * kRowBytes;
+static_assert(kRunLds <= 163840, "run workgroup LDS");
+constexpr int kRunTsOff = kStage2;                                // side products, fp32 [3][256][16]
+constexpr int kRunFBOff = kStage2 + kTsBytes;                     // fold B tile [256][32 K]
+static_assert(kRunFBOff + kBN * kRowBytes <= kRunFAOff, "fold B tile overlaps the fold A operand");
+
+// Build the fold A operand FA[m][16 s + t] = fscale[s] * Ts[s][m][t] (bf16)
+// for nslot <= 2 adapters from the side products at `ts`.
+__device__ __forceinline__ void build_fold_a(char* FA, const float* ts, int nslot, const float (&fscale)[kMaxSide]) {
+  for (int e = threadIdx.x; e < kBM * 4; e += kGemmThreads) {
+    const int m = e >> 2, c = e & 3;
+    const int slot = (c * 8) / kSlot, t0 = (c * 8) % kSlot;
+    float v[8];
+    const float sc = slot == 0 ? fscale[0] : fscale[1];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = (slot < nslot) ? sc * ts[ts_idx(slot, m, t0 + u)] : 0.f;
+    *reinterpret_cast<u32x4*>(FA + lds_off(m, c)) = pack(v);
+  }
+}
+
+// acc += FA . FB^T over one fold tile (K = 32) with FB rows built by fb.
+template <class FB>
+__device__ __forceinline__ void fold_run(const char* FA, char* FBt, f32x4 (&acc)[kMB][8], FB& fb) {
+  const WaveId q = wave_id_opaque();
+  for (int e = threadIdx.x; e < kBN * 4; e += kGemmThreads) {
+    const int R = e >> 2, c = e & 3;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    fb(R, (c * 8) / kSlot, (c * 8) % kSlot, v);
+    *reinterpret_cast<u32x4*>(FBt + lds_off(R, c)) = pack(v);
+  }
+  __syncthreads();
+  Frag<bf16> af[kMB];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb) af[mb] = lds_frag<bf16>(FA, q.wm * 64 + mb * 16 + q.r16, q.g);
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+    const Frag<bf16> bfr = lds_frag<bf16>(FBt, q.wn * 128 + nb * 16 + q.r16, q.g);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb) acc[mb][nb] = mma(acc[mb][nb], af[mb], bfr);
   }
 }
 

@@ -20,7 +20,7 @@ template <class T, int ACT>
 hipError_t launch_gateup(bool fast, const GateUpArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     if (fast) {
-      hipLaunchKernelGGL((k_gateup_fwd<T, ACT, true>), grid, dim3(kGemmThreads), 0, st, a);
+      hipLaunchKernelGGL((k_gateup_run<ACT>), grid, dim3(kGemmThreads), 0, st, a);
       return hipGetLastError();
     }
   }

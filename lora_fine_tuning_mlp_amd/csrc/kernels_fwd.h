@@ -26,6 +26,7 @@ struct GateUpArgs {
   long N; int h, i, r;
   int vecA, vecW, vecS, vecO;
   int R, NC;
+  int L, RPB, nruns;   // run kernel: run length, runs per row block, runs
 };
 
 // LDS row R of the B tile -> (is_up, intermediate column index j).
@@ -137,6 +138,112 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
       gstore<T, 4>(Uo + off, uv, nvalid, a.vecO);
       gstore<T, 4>(Ho + off, hv, nvalid, a.vecO);
     }
+}
+
+
+// Fast path (bf16, h % 64 == 0) as runs of column tiles: the side products
+// T_g, T_u of the row block are computed in the run's first tile only (the
+// later tiles skip the side loads and MFMAs) and folded into every tile from
+// the run's fold operand in LDS.
+template <int ACT>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
+  __shared__ __align__(16) char smem[kRunLds];
+  int rb, cb0, cb1;
+  run_coords(a.nruns, a.RPB, a.L, a.NC, rb, cb0, cb1);
+  const long m0 = (long)rb * kBM;
+  const bf16* X = static_cast<const bf16*>(a.X);
+  const bf16* Wg = static_cast<const bf16*>(a.Wg);
+  const bf16* Wu = static_cast<const bf16*>(a.Wu);
+  const bf16* Ag = static_cast<const bf16*>(a.Ag);
+  const bf16* Au = static_cast<const bf16*>(a.Au);
+  const bf16* Bg = static_cast<const bf16*>(a.Bg);
+  const bf16* Bu = static_cast<const bf16*>(a.Bu);
+
+  NKPairLoader<2> ld;
+  ld.init_a(X, a.h, a.N, m0);
+  ld.bfallback = Wg;
+  auto set_cols = [&](int cb) {
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      int up, j;
+      gateup_row(ld.row_of(it), cb * 128, up, j);
+      ld.brow[it] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
+    }
+  };
+  set_cols(cb0);
+  ld.smask = 3u;
+  ld.srow = Ag;
+  {
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = ld.side_ptr((sr >> 4) == 0 ? Ag : Au, sr & 15, a.r, a.h, Ag);
+  }
+  const float fs[kMaxSide] = {a.sg, a.su, 0.f};
+  char* FA = smem + kRunFAOff;
+  bf16* Go = static_cast<bf16*>(a.G);
+  bf16* Uo = static_cast<bf16*>(a.U);
+  bf16* Ho = static_cast<bf16*>(a.H);
+  const int nkt = a.h / 64;
+
+  for (int cb = cb0; cb < cb1; ++cb) {
+    const bool first = cb == cb0;
+    const int j0 = cb * 128;
+    f32x4 acc[kMB][8];
+    f32x4 sacc[2][kMB];
+    zero_acc(acc);
+    zero_side(sacc);
+    kloop2<2>(smem, nkt, ld, acc, sacc, 0, !first);
+    if (cb + 1 < cb1) {                 // the next tile's first K tile, into stage 0
+      set_cols(cb + 1);
+      ld.smask = 0u;
+      ld.issue(0, smem, smem + kStage2A);
+    }
+    const WaveId q = wave_id_opaque();   // everything after the K-loop derives from this
+    if (first) {
+      side_reduce<bf16, 2>(smem + kRunTsOff, sacc);
+      const float* Ts = ts_ptr(smem + kRunTsOff);
+      if (cb0 == 0 && q.tid < kBM) {    // T_g, T_u are saved once per row block
+        const long row = m0 + q.tid;
+        if (row < a.N)
+          for (int t = 0; t < a.r; ++t) {
+            a.Tg[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
+            a.Tu[row * a.r + t] = Ts[ts_idx(1, q.tid, t)];
+          }
+      }
+      build_fold_a(FA, Ts, 2, fs);
+    }
+    auto fb = [&](int R, int slot, int t0, float* v) {
+      int up, j;
+      gateup_row(R, j0, up, j);
+      if (slot != up || j >= a.i) return;
+      const bf16* src = (up ? Bu : Bg) + (long)j * a.r;
+      for (int e = 0; e < 8; ++e)
+        if (t0 + e < a.r) v[e] = (float)src[t0 + e];
+    };
+    fold_run(FA, smem + kRunFBOff, acc, fb);
+
+    // GLU epilogue (registers only): the lane holds gate (blocks 0..3) and
+    // up (blocks 4..7) of the same 4 consecutive intermediate columns.
+    const int jj = j0 + q.wn * 64 + 4 * q.r16;
+    const int nvalid = min(4, a.i - jj);
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long row = m0 + acc_row(q, mb, j);
+        if (row >= a.N || nvalid <= 0) continue;
+        float gv[4], uv[4], hv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          gv[e] = acc[mb][e][j];
+          uv[e] = acc[mb][4 + e][j];
+          hv[e] = act_fwd<ACT>(gv[e]) * uv[e];
+        }
+        const long off = row * a.i + jj;
+        gstore<bf16, 4>(Go + off, gv, nvalid, a.vecO);
+        gstore<bf16, 4>(Uo + off, uv, nvalid, a.vecO);
+        gstore<bf16, 4>(Ho + off, hv, nvalid, a.vecO);
+      }
+  }
 }
 
 // ===========================================================================

@@ -190,6 +190,14 @@ int split_count(long tiles, long nkt) {
   if (S > 16) S = 16;
   return S < 1 ? 1 : (int)S;
 }
+// Runs of column tiles (kernels that walk several tiles of one row block):
+// run length L = ceil(tiles / CUs), so the runs fill the chip about once.
+void run_layout(long R, long NC, int& L, int& RPB, int& nruns) {
+  const long tiles = R * NC;
+  L = (int)std::max(1L, cdiv(tiles, kCUs));
+  RPB = (int)cdiv(NC, L);
+  nruns = (int)(R * RPB);
+}
 struct SplitWs {
   float* part = nullptr;
   int* cnt = nullptr;
@@ -413,7 +421,8 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.vecO = (i % 4 == 0) && al16(G) && al16(U) && al16(w.H);
     a.R = R; a.NC = (int)cdiv(i, 128);
     const bool fast = fast_ok(DT<T>::code, h, N, {X, g.W, u.W, g.A, u.A}) && h % 64 == 0;
-    const dim3 grid(a.R * a.NC);
+    run_layout(a.R, a.NC, a.L, a.RPB, a.nruns);
+    const dim3 grid(fast && sizeof(T) == 2 ? a.nruns : a.R * a.NC);
     const int rc = grid.x == 0 ? LORA_OK
                                : launch_call(0, st, [&]() { return launch_gateup<T, ACT>(fast, a, grid, st); });
     if (rc) return rc;
