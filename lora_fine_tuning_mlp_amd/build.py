@@ -1,10 +1,11 @@
 """Build the HIP library (liblora_mi355x.so) in-tree for gfx950 with hipcc.
 
 Two translation units: the library (host code and most kernels), compiled
-with the ILP-oriented instruction scheduling, and the gate/up GEMM and the
-split-K MLP dX kernel with their launchers, compiled with the default
-scheduling (measured per kernel; see the comment in that source); the
-objects are linked into one shared library.
+with the ILP-oriented instruction scheduling, and the LoRA linear forward,
+the QKV forward and the split-K MLP dX kernel with their launchers, compiled
+with the default scheduling (chosen per kernel from alternating builds on one
+device; see the comment in that source); the objects are linked into one
+shared library.
 """
 from __future__ import annotations
 
@@ -35,9 +36,9 @@ def compile_commands(obj_main: str, obj_split: str) -> list:
         "-I", INCLUDE, "-I", os.path.join(PKG, "csrc"),
     ]
     return [
-        # Instruction scheduling for ILP: measured on MI355X, the MLP dX GEMM
-        # 1878 -> 1791 us and the down-projection backward 1191 -> 1172 us
-        # against the default strategy.
+        # Instruction scheduling for ILP: measured on MI355X with the two
+        # builds alternating on one device, the MLP dX GEMM 1844 -> 1780 us and
+        # the down-projection backward 1174 -> 1163 us against the default.
         common + ["-mllvm", "-amdgpu-sched-strategy=max-ilp", "-c", SRC, "-o", obj_main],
         common + ["-c", SRC_DEFAULT_SCHED, "-o", obj_split],
     ]

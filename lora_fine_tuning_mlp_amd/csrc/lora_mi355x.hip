@@ -25,8 +25,23 @@ namespace lora {
 // Defined in kernels_default_sched.hip (a translation unit of its own,
 // compiled with the default instruction scheduling).
 hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, dim3 grid, hipStream_t st);
+template <class T>
+hipError_t launch_linear_fwd(bool fast, const LinearArgs& a, dim3 grid, hipStream_t st);
+template <class T>
+hipError_t launch_qkv_fwd(bool fast, int head_dim, int ns, const QKVFwdArgs& a, dim3 grid, hipStream_t st);
+
+// gate/up: the fast path runs as column-tile runs (k_gateup_run).
 template <class T, int ACT>
-hipError_t launch_gateup(bool fast, const GateUpArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_gateup(bool fast, const GateUpArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (fast) {
+      hipLaunchKernelGGL((k_gateup_run<ACT>), grid, dim3(kGemmThreads), 0, st, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((k_gateup_fwd<T, ACT, false>), grid, dim3(kGemmThreads), 0, st, a);
+  return hipGetLastError();
+}
 }  // namespace lora
 
 namespace {
@@ -443,8 +458,8 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
       const int rc = split_prepare(w.split, st, a.sk);
       if (rc) return rc;
     }
-    const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>),
-                                    dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a);
+    const dim3 grid(a.R * a.NC * a.sk.S);
+    const int rc = launch_call(1, st, [&]() { return launch_linear_fwd<T>(fast, a, grid, st); });
     if (rc) return rc;
   }
   return ok();
@@ -616,15 +631,8 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
       if (a.off[p] < std::min((cb + 1) * kBN, a.off[3]) && a.off[p + 1] > cb * kBN) ++c;
     ns = std::max(ns, c);
   }
-  const dim3 grid(a.R * a.NC), blk(kGemmThreads);
-#define LORA_QKV_NS(LG, NS) \
-  LORA_LAUNCH_FAST(3, fast, (k_qkv_fwd<T, LG, true, NS>), (k_qkv_fwd<T, LG, false, NS>), grid, blk, st, a)
-  if (d.head_dim == 128) {
-    rc = ns == 1 ? LORA_QKV_NS(1, 1) : (ns == 2 ? LORA_QKV_NS(1, 2) : LORA_QKV_NS(1, 3));
-  } else {
-    rc = ns == 1 ? LORA_QKV_NS(2, 1) : (ns == 2 ? LORA_QKV_NS(2, 2) : LORA_QKV_NS(2, 3));
-  }
-#undef LORA_QKV_NS
+  const dim3 grid(a.R * a.NC);
+  rc = launch_call(3, st, [&]() { return launch_qkv_fwd<T>(fast, d.head_dim, ns, a, grid, st); });
   if (rc) return rc;
   return ok();
 }
@@ -755,8 +763,8 @@ int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_
     const int rc = split_prepare(w.split, st, a.sk);
     if (rc) return rc;
   }
-  const int rc = LORA_LAUNCH_FAST(1, fast, (k_linear_fwd<T, true>), (k_linear_fwd<T, false>),
-                                  dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), st, a);
+  const dim3 grid(a.R * a.NC * a.sk.S);
+  const int rc = launch_call(1, st, [&]() { return launch_linear_fwd<T>(fast, a, grid, st); });
   if (rc) return rc;
   return ok();
 }
