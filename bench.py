@@ -58,10 +58,14 @@ def linear_kernel_flops(cfg):
             "k_proj_dx_bwd": 2 * N * o * k + 4 * N * r * k}
 
 
-def time_leg(step, steps: int, warmup: int, kflops=None):
+def time_leg(step, steps: int, warmup: int, kflops=None, flush=None):
     """Warm up, then time `steps` calls of `step` with HIP events on the
     current stream (the library's per-launch recorder off); a second pass of
-    the same calls with the recorder on gives the per-kernel averages."""
+    the same calls with the recorder on gives the per-kernel averages.
+
+    With `flush` (a device tensor larger than the 256 MB MALL and the L2s),
+    the tensor is overwritten before every call and each call is timed on
+    its own, so every call starts with its inputs in HBM only."""
     import torch
     from lora_fine_tuning_mlp_amd import binding as B
 
@@ -70,15 +74,27 @@ def time_leg(step, steps: int, warmup: int, kflops=None):
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    if flush is None:
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+    else:
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            flush.fill_(1.0)
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ms = sum(a.elapsed_time(b) for a, b in ev) / steps
     B.timing_reset()
     B.timing_enable(True)
     for _ in range(steps):
+        if flush is not None:
+            flush.fill_(1.0)
         step()
     torch.cuda.synchronize()
     B.timing_enable(False)
@@ -90,6 +106,22 @@ def time_leg(step, steps: int, warmup: int, kflops=None):
             if kflops and name in kflops:
                 kernels[name]["tflops"] = round(kflops[name] / (1e-3 * tot / n) / 1e12, 1)
     return ms, kernels
+
+
+def copy_probe(mib: int) -> None:
+    """A plain device copy of `mib` MiB: calibrates rocprofv3's byte counters."""
+    if mib:
+        import torch
+        a = torch.empty(mib * (1 << 20) // 4, device="cuda:0", dtype=torch.float32).fill_(1.0)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+
+def mall_flush_buffer():
+    """A 1 GiB device buffer; overwriting it evicts the MALL (256 MB) and the L2s."""
+    import torch
+    return torch.empty(1 << 28, device="cuda:0", dtype=torch.float32)
 
 
 def bench_linear(cfg, steps: int, warmup: int):
@@ -168,9 +200,9 @@ def mlp_kernel_flops(cfg):
             "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h}
 
 
-def bench_mlp(cfg, steps: int, warmup: int):
+def bench_mlp(cfg, steps: int, warmup: int, flush=None):
     """LoRA MLP fwd+bwd at `cfg` on its own (GeGLU-tanh at h 3072, and the
-    small-shape regime).  Not part of `value`."""
+    small-shape regime).  Not part of `value`.  `flush`: see time_leg."""
     import torch
     from lora_fine_tuning_mlp_amd import binding as B
     from lora_fine_tuning_mlp_amd import synthetic as S
@@ -185,16 +217,17 @@ def bench_mlp(cfg, steps: int, warmup: int):
         m.forward()
         m.backward(dY)
 
-    ms, kernels = time_leg(step, steps, warmup, mlp_kernel_flops(cfg))
+    ms, kernels = time_leg(step, steps, warmup, mlp_kernel_flops(cfg), flush)
     leg = {"workload": cfg.name, "tokens": cfg.n_tokens, "hidden": cfg.hidden, "inter": cfg.inter,
            "rank": cfg.rank, "act": cfg.act, "ms_per_step": round(ms, 4),
            "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
     return with_rooflines(leg, cfg.flops(), mlp_planned_bytes(cfg))
 
 
-def bench_qkv(cfg, steps: int, warmup: int):
+def bench_qkv(cfg, steps: int, warmup: int, flush=None):
     """LoRA QKV fwd+bwd at `cfg` (used for the q/k-norm variant of the
-    headline QKV shape).  Not part of `value`."""
+    headline QKV shape, and the small-shape regime).  Not part of `value`.
+    `flush`: see time_leg."""
     import torch
     from lora_fine_tuning_mlp_amd import binding as B
     from lora_fine_tuning_mlp_amd import synthetic as S
@@ -209,7 +242,7 @@ def bench_qkv(cfg, steps: int, warmup: int):
         m.forward()
         m.backward(dQ, dK, dV)
 
-    ms, kernels = time_leg(step, steps, warmup, qkv_kernel_flops(cfg))
+    ms, kernels = time_leg(step, steps, warmup, qkv_kernel_flops(cfg), flush)
     leg = {"workload": cfg.name, "tokens": cfg.n_tokens, "qk_norm": cfg.qk_norm, "bias": cfg.bias,
            "ms_per_step": round(ms, 4), "tflops": round(cfg.flops() / (ms * 1e-3) / 1e12, 2), "kernels": kernels}
     return with_rooflines(leg, cfg.flops(), qkv_planned_bytes(cfg))
@@ -427,6 +460,39 @@ def cpu_baseline(qkv_cfg, mlp_cfg, tokens: int, reps: int = 1):
     }
 
 
+LEG_NAMES = ("oproj", "qkv_qknorm", "mlp_geglu_h3072", "small_mlp_h896", "small_qkv_h896",
+             "small_mlp_h896_cold", "small_qkv_h896_cold")
+
+
+def run_legs(names, steps: int, warmup: int):
+    """The separate legs (outside `value`).  The large ones run steps / 2
+    calls; the small-shape ones run `steps` calls twice: as a loop of calls
+    whose inputs stay in the MALL between calls, and ("_cold") with the MALL
+    and L2s flushed before every call."""
+    from lora_fine_tuning_mlp_amd import synthetic as S
+
+    ls, lw = max(1, steps // 2), max(1, warmup)
+    flush = mall_flush_buffer() if any(n.endswith("_cold") for n in names) else None
+    make = {
+        "oproj": lambda: bench_linear(S.C_OPROJ, ls, lw),
+        "qkv_qknorm": lambda: bench_qkv(dataclasses.replace(S.C1, name=S.C1.name + "_qknorm", qk_norm=True), ls, lw),
+        "mlp_geglu_h3072": lambda: bench_mlp(S.C3, ls, lw),
+        "small_mlp_h896": lambda: bench_mlp(S.C4_MLP, steps, lw),
+        "small_qkv_h896": lambda: bench_qkv(S.C4_QKV, steps, lw),
+        "small_mlp_h896_cold": lambda: bench_mlp(S.C4_MLP, steps, lw, flush),
+        "small_qkv_h896_cold": lambda: bench_qkv(S.C4_QKV, steps, lw, flush),
+    }
+    out = {}
+    for n in names:
+        print(f"[bench] leg {n}", file=sys.stderr, flush=True)
+        out[n] = make[n]()
+        if n.endswith("_cold"):
+            out[n]["mall"] = "flushed before every call (1 GiB overwrite), each call timed on its own"
+        elif n.startswith("small_"):
+            out[n]["mall"] = "not flushed: a loop of calls on the same inputs (working set < 256 MB MALL)"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -441,6 +507,8 @@ def main():
                     help="also run a plain device copy of this size (calibrates rocprofv3 byte counters)")
     ap.add_argument("--crossover", action="store_true",
                     help="instead of the headline step: fused vs unfused (torch) timings over token counts")
+    ap.add_argument("--leg", choices=LEG_NAMES, action="append",
+                    help="instead of the headline step: run only this separate leg (repeatable) and print its JSON")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -457,6 +525,11 @@ def main():
     qkv_cfg, mlp_cfg = S.C1, S.C2
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.leg:
+        legs = run_legs(args.leg, args.steps, args.warmup)
+        copy_probe(args.copy_probe_mib)
+        print(json.dumps({"legs": legs, "dtype": "bf16", "data": "synthetic"}), flush=True)
+        return
     if args.crossover:
         rows = crossover(max(3, args.steps), max(2, args.warmup))
         print(json.dumps({"crossover": rows, "unit": "ms per fwd+bwd", "dtype": "bf16", "data": "synthetic"}),
@@ -533,22 +606,11 @@ def main():
 
     legs = None
     if not args.no_legs:
-        print("[bench] separate legs: o_proj linear, q/k-norm QKV", file=sys.stderr, flush=True)
-        ls, lw = max(1, args.steps // 2), max(1, args.warmup)
-        legs = {"oproj": bench_linear(S.C_OPROJ, ls, lw),
-                "qkv_qknorm": bench_qkv(dataclasses.replace(qkv_cfg, name=qkv_cfg.name + "_qknorm", qk_norm=True),
-                                        ls, lw)}
-        print("[bench] separate legs: GeGLU MLP at h 3072, small-shape MLP and QKV", file=sys.stderr, flush=True)
-        legs["mlp_geglu_h3072"] = bench_mlp(S.C3, ls, lw)
-        legs["small_mlp_h896"] = bench_mlp(S.C4_MLP, args.steps, lw)
-        legs["small_qkv_h896"] = bench_qkv(S.C4_QKV, args.steps, lw)
+        print("[bench] separate legs: o_proj, q/k-norm QKV, GeGLU MLP at h 3072, small shapes", file=sys.stderr,
+              flush=True)
+        legs = run_legs(LEG_NAMES, args.steps, args.warmup)
 
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * (1 << 20) // 4
-        a = torch.empty(n, device=dev, dtype=torch.float32).fill_(1.0)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+    copy_probe(args.copy_probe_mib)
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,

@@ -1,11 +1,12 @@
 """Turn rocprofv3 CSV output into the short text summaries kept with the
-library (kernel durations, HBM traffic per launch).
+library (kernel durations, HBM traffic per launch, wave states).
 
     python -m lora_fine_tuning_mlp_amd.profiling stats  <kernel_stats.csv> <out.md> --cmd "<command>"
     python -m lora_fine_tuning_mlp_amd.profiling traffic <fetch counter_collection.csv> \
         <write counter_collection.csv> <copy bytes> <out.json> <out.md> --cmd "<fetch cmd>" --cmd "<write cmd>"
     python -m lora_fine_tuning_mlp_amd.profiling counters <counter_collection.csv> <out.md> --cmd "<command>" \
         [--bench-flops]
+    python -m lora_fine_tuning_mlp_amd.profiling stalls <out.md> <SQ counter_collection.csv>... --cmd "<command>"...
 
 Traffic: FETCH_SIZE and WRITE_SIZE are read in KiB per dispatch.  Both are
 calibrated against the largest device copy kernel of the same run (a plain
@@ -58,8 +59,15 @@ def short_name(name: str) -> str:
     return n
 
 
+# The library's per-launch recorder names a launch by the step it performs;
+# where a step has more than one kernel variant, the variant's own name (as
+# rocprofv3 reports it) maps to that step's name.
+RECORDER_NAME = {"k_gateup_run": "k_gateup_fwd"}
+
+
 def base_name(name: str) -> str:
-    return short_name(name).split("<")[0]
+    b = short_name(name).split("<")[0]
+    return RECORDER_NAME.get(b, b)
 
 
 def stats_summary(path: str, out: str, cmd: str) -> None:
@@ -144,6 +152,81 @@ def counters_summary(path: str, out: str, cmd: str, kflops=None) -> None:
     open(out, "w").write("\n".join(lines) + "\n")
 
 
+# Wave-state counters (SQ block), read as fractions of the wave-resident
+# time SQ_WAVE_CYCLES (all in quad-cycles, summed over the chip).
+STALL_RATIOS = [
+    ("issue", "SQ_ACTIVE_INST_ANY"),       # issuing an instruction
+    ("wait_issue", "SQ_WAIT_INST_ANY"),    # next instruction ready, waiting for its issue slot
+    ("wait_any", "SQ_WAIT_ANY"),           # waiting on anything else: s_waitcnt, barrier
+    ("wait_lds", "SQ_WAIT_INST_LDS"),      # waiting to issue an LDS instruction
+    ("valu", "SQ_ACTIVE_INST_VALU"),       # issue split by instruction type (VALU includes MFMA)
+    ("vmem", "SQ_ACTIVE_INST_VMEM"),       # buffer instructions (global_* loads are FLAT-encoded)
+    ("flat", "SQ_ACTIVE_INST_FLAT"),
+    ("lds", "SQ_ACTIVE_INST_LDS"),
+    ("salu", "SQ_ACTIVE_INST_SCA"),
+    ("misc", "SQ_ACTIVE_INST_MISC"),
+]
+
+
+def stalls_summary(paths, out: str, cmds) -> None:
+    """Per-kernel wave-state breakdown from raw SQ counters collected over one
+    or more rocprofv3 --pmc runs of the same program (each run's counters
+    averaged over its dispatches)."""
+    vals = collections.defaultdict(lambda: collections.defaultdict(list))
+    clk = collections.defaultdict(list)
+    for p in paths:
+        for r in csv.DictReader(open(p)):
+            k = base_name(r["Kernel_Name"])
+            if k.startswith("k_"):
+                vals[k][r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    if ns > 0:
+                        clk[k].append(float(r["Counter_Value"]) / 8 / ns)
+
+    def avg(k, c):
+        v = vals[k].get(c)
+        return sum(v) / len(v) if v else None
+
+    cols = [n for n, _ in STALL_RATIOS]
+    lines = ["# Wave-state breakdown per kernel (rocprofv3 SQ counters)", "", "Commands:", ""]
+    for c in cmds:
+        lines += ["```", c, "```", ""]
+    lines += ["Each state column is a counter divided by SQ_WAVE_CYCLES (the time waves are resident), "
+              "so it reads as the share of a wave's lifetime in that state: `issue` (SQ_ACTIVE_INST_ANY), "
+              "`wait_issue` (SQ_WAIT_INST_ANY: next instruction ready, waiting for an issue slot, e.g. the "
+              "MFMA pipe the SIMD's other wave holds), `wait_any` (SQ_WAIT_ANY: s_waitcnt, barrier); the three "
+              "add up to about 1. `wait_lds` is SQ_WAIT_INST_LDS; `valu` ... `misc` split `issue` by "
+              "instruction type. GRBM_GUI_ACTIVE is summed over the 8 XCDs (it reads 8 x the kernel's "
+              "cycles), so `mfma_busy` = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8), "
+              "the MFMA pipes' busy share at the clock the kernel ran (`clock`, from the duration of the "
+              "same dispatches), and `waves/CU` = 4 SQ_WAVE_CYCLES / (256 CUs x GRBM_GUI_ACTIVE / 8). "
+              "`lds_conflict` = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. The clock is only meaningful "
+              "for kernels that run for hundreds of microseconds (GRBM_GUI_ACTIVE also counts the dispatch "
+              "around a short kernel). Empty cells: counter not collected.", "",
+              "| kernel | dispatches | clock GHz | waves/CU | " + " | ".join(cols) + " | mfma_busy | lds_conflict |",
+              "|---|---:|---:|---:|" + "---:|" * len(cols) + "---:|---:|"]
+    for k in sorted(vals):
+        wc = avg(k, "SQ_WAVE_CYCLES")
+        if not wc:
+            continue
+        n = min(len(v) for v in vals[k].values())
+        row = []
+        for _, c in STALL_RATIOS:
+            v = avg(k, c)
+            row.append(f"{v / wc:.3f}" if v is not None else "")
+        gui = avg(k, "GRBM_GUI_ACTIVE")
+        mb = avg(k, "SQ_VALU_MFMA_BUSY_CYCLES")
+        busy = f"{mb / (1024 * gui / 8):.3f}" if (gui and mb is not None) else ""
+        occ = f"{4 * wc / (256 * gui / 8):.2f}" if gui else ""
+        la, lc = avg(k, "SQ_LDS_IDX_ACTIVE"), avg(k, "SQ_LDS_BANK_CONFLICT")
+        conf = f"{lc / la:.3f}" if (la and lc is not None) else ""
+        ghz = f"{sum(clk[k]) / len(clk[k]):.2f}" if clk[k] else ""
+        lines.append(f"| `{k}` | {n} | {ghz} | {occ} | " + " | ".join(row) + f" | {busy} | {conf} |")
+    lines += ["", f"HIP sources hash: `{source_hash()}`"]
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -164,6 +247,10 @@ def main():
     c.add_argument("--cmd", required=True)
     c.add_argument("--bench-flops", action="store_true",
                    help="divide MfmaFlopsBF16 by the headline step's algorithmic FLOPs per launch")
+    w = sub.add_parser("stalls")
+    w.add_argument("out")
+    w.add_argument("csv", nargs="+")
+    w.add_argument("--cmd", action="append", default=[])
     a = ap.parse_args()
     if a.what == "stats":
         stats_summary(a.csv, a.out, a.cmd)
@@ -176,6 +263,8 @@ def main():
             from lora_fine_tuning_mlp_amd import synthetic as S
             kf = bench.kernel_flops(S.C1, S.C2)
         counters_summary(a.csv, a.out, a.cmd, kf)
+    elif a.what == "stalls":
+        stalls_summary(a.csv, a.out, a.cmd)
     else:
         traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.out_json, a.out_md, a.cmd)
 
