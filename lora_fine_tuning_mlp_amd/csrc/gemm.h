@@ -35,6 +35,9 @@
 
 #include "common.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace lora {
 
 constexpr int kGemmThreads = 512;                          // 8 waves
@@ -142,6 +145,59 @@ __device__ __forceinline__ u32x2 tr16(unsigned addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(addr));
   return r;
 }
+// LDS writes as inline asm, for code that must not let the compiler see an
+// LDS access while direct loads are in flight (it would wait for all of them).
+__device__ __forceinline__ void ds_w16_lo(unsigned addr, unsigned v) {
+  asm volatile("ds_write_b16 %0, %1" : : "v"(addr), "v"(v));
+}
+__device__ __forceinline__ void ds_w16_hi(unsigned addr, unsigned v) {
+  asm volatile("ds_write_b16_d16_hi %0, %1" : : "v"(addr), "v"(v));
+}
+__device__ __forceinline__ void ds_w128(unsigned addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v));
+}
+// The same with an immediate byte offset (the DS offset field), so unrolled
+// code addresses many locations from one base register.
+template <int OFF>
+__device__ __forceinline__ void ds_w16_lo_at(unsigned base, unsigned v) {
+  asm volatile("ds_write_b16 %0, %1 offset:%2" : : "v"(base), "v"(v), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_w16_hi_at(unsigned base, unsigned v) {
+  asm volatile("ds_write_b16_d16_hi %0, %1 offset:%2" : : "v"(base), "v"(v), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ u32x2 tr16_at(unsigned base) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4 rd128_at(unsigned base) {
+  u32x4 r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(base), "n"(OFF));
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ void ds_w128_at(unsigned base, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1 offset:%2" : : "v"(base), "v"(v), "n"(OFF));
+}
+// Compile-time loop: f(std::integral_constant<int, 0>{}) ... f(<N - 1>), so
+// the body can form immediate offsets from the index.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+// At most N of this wave's vector memory operations outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void lgkm_tie(u32x2& a, u32x2& b, u32x2& c, u32x2& d, u32x2& e, u32x2& f, u32x2& g,
                                          u32x2& h) {
@@ -149,8 +205,13 @@ __device__ __forceinline__ void lgkm_tie(u32x2& a, u32x2& b, u32x2& c, u32x2& d,
                : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
                : "n"(N));
 }
+// (a and b must be distinct: the same variable named twice would be copied
+// into a second register before the wait.)
 __device__ __forceinline__ void lgkm_tie0(u32x2& a, u32x2& b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lgkm_tie0(u32x2& a) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a));
 }
 // The two reads of B fragment nb (K slots 0..3 and 4..7 of the lane).
 __device__ __forceinline__ void tr_issue(const char* Bs, int nb, const WaveId& q, u32x2& lo, u32x2& hi) {
@@ -950,6 +1011,19 @@ struct KNLoader32 {
   __device__ __forceinline__ unsigned side_mask(int kt) const { return smask_of(kt); }
 };
 
+// Rank entries t0 .. t0+NV-1 of one adapter row or column (element t at
+// src[t * stride]), zero past r.  Every load is issued, with its index
+// clamped to r - 1 (r >= 1), so they go out back to back rather than one
+// branch and one wait each.
+template <class T, int NV>
+__device__ __forceinline__ void load_rank(const T* src, long stride, int t0, int r, float* v) {
+  T x[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) x[e] = src[(long)min(t0 + e, r - 1) * stride];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) v[e] = (t0 + e < r) ? to_f<T>(x[e]) : 0.f;
+}
+
 // Store 8 consecutive values of one row (16-byte bf16 store, or 2 x 16 bytes fp32).
 template <class T>
 __device__ __forceinline__ void store_row8(T* p, const float (&v)[8], int n, bool vec) {
@@ -1095,16 +1169,17 @@ __device__ __forceinline__ void park_row(const char* base, int j, const WaveId& 
 
 // Sum of NOUT partial tiles [16 t][128 cols] over the four wave-rows (fixed
 // order wm = 3, 2, 1, 0) and store of the row-block partial to
-// part[o] + col * 16 + t (cols bounded by ncols).  Lane column layout: G = 1
-// (tile column wn*128 + 8*r16 + nb).
-template <int NOUT>
+// part[o] + col * 16 + t (cols bounded by ncols).  Lane column layout
+// perm_col(LG, r16, nb): LG = 0 gives tile column wn*128 + 8*r16 + nb, LG = 3
+// the natural order wn*128 + 16*nb + r16.
+template <int NOUT, int LG = 0>
 __device__ __forceinline__ void reduce_store_partials(char* smem, f32x4 (&pacc)[NOUT][8], float* const (&part)[NOUT],
                                                       long n0, long ncols) {
   const WaveId q = wave_id();
   float* red = reinterpret_cast<float*>(smem + kRedOff);
   static_assert(NOUT * 2 * 128 * 16 * 4 <= kRedBytes, "reduction scratch too small");
   auto slot = [&](int o, int nb) -> f32x4* {
-    return reinterpret_cast<f32x4*>(red + ((o * 2 + q.wn) * 128 + perm_col(0, q.r16, nb)) * 16 + 4 * q.g);
+    return reinterpret_cast<f32x4*>(red + ((o * 2 + q.wn) * 128 + perm_col(LG, q.r16, nb)) * 16 + 4 * q.g);
   };
   __syncthreads();
   if (q.wm == 3) {
@@ -1130,7 +1205,7 @@ __device__ __forceinline__ void reduce_store_partials(char* smem, f32x4 (&pacc)[
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const f32x4 v = *slot(o, nb) + pacc[o][nb];
-        const long col = n0 + q.wn * 128 + perm_col(0, q.r16, nb);
+        const long col = n0 + q.wn * 128 + perm_col(LG, q.r16, nb);
         if (col < ncols) *reinterpret_cast<f32x4*>(part[o] + col * 16 + 4 * q.g) = v;
       }
   }

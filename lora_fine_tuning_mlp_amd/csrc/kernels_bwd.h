@@ -425,10 +425,224 @@ struct DownBwdArgs {
 // (its 64 rows x 128 columns) after Ts slot 0, the only side slot this kernel
 // uses.  That frees the accumulators for the GLU backward and the partials.
 constexpr int kDownParkOff = kBM * kSlot * 4;
-constexpr int kDownBwdLds = kDownParkOff + 8 * 16384;            // 147456
+
+// ---------------------------------------------------------------------------
+// GLU backward of a whole tile (bf16; N and i multiples of 256).
+//
+// G and U are staged through LDS by direct loads, one m-block at a time (a
+// wave's 16 rows x 128 columns of each, 8 KB) in a wave-private ring of two
+// buffers: the next m-block's loads are in flight while one is processed,
+// nothing in flight occupies registers, and no workgroup barrier is needed.
+// A lane reads its four rows of a column with ds_read_b64_tr_b16, i.e. in the
+// accumulator layout, so dH stays where the K-loop left it (rounded to bf16,
+// packed in registers), and H, dG, dU are formed per column and go straight
+// into the partials' MFMAs as B operands (K = rows).  dG and dU are written
+// back over the consumed G and U rows and leave as 16-byte row stores.
+//
+// Buffer rows are 256 bytes (128 columns); their 32-byte segments are
+// XOR-swizzled by row (segment nb ^ (row & 7)), so the transpose reads of 16
+// rows and the column writes spread over the banks.  The A operands (dT_d,
+// s_g T_g, s_u T_u of the block's rows) sit in LDS as bf16 [row][16], read
+// the same way.
+//
+// Vector memory operations of a wave complete in issue order; the waits
+// below count the operations issued after the m-block being waited for.
+// ---------------------------------------------------------------------------
+constexpr int kGluRing = 0;                         // wave w at + w * 16 KB: two buffers of 8 KB
+constexpr int kGluT = 128 * 1024;                   // bf16 [3][256][16]: dT_d, s_g T_g, s_u T_u
+constexpr int kGluLds = kGluT + 3 * kBM * 32;       // 155648
+static_assert(kGluT >= kGluRing + 8 * 16384, "GLU ring layout");
+
+constexpr int kDownBwdLds = kGluLds > kDownParkOff + 8 * 16384 ? kGluLds : kDownParkOff + 8 * 16384;
 static_assert(kDownBwdLds >= kGemmLds && kDownBwdLds <= 163840, "k_down_bwd LDS");
 
-template <class T, int ACT, bool FAST>
+// Ring buffer b of a wave: G rows at b * 8 KB, U rows 4 KB after.  Row r
+// (0..15) of 256 bytes holds columns c (0..127) at
+// 256 r + 32 ((c / 16) ^ (r & 7)) + 2 (c % 16).
+template <int ACT>
+__device__ __forceinline__ void glu_bwd_full(char* smem, f32x4 (&acc)[kMB][8], const DownBwdArgs& a, long m0, long n0,
+                                             int rb) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wm = w >> 1, wn = w & 1;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));             // keep lane-derived values after the K-loop
+  const int s = lane & 15, g = lane >> 4;
+  const long ni = a.i;
+
+  // dH rounded to bf16, packed (rows j0 j1 | j2 j3 of each column): frees the
+  // accumulators.
+  u32x2 dh[kMB][8];
+#pragma unroll
+  for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+      dh[mb][nb] = (u32x2){pack_bf2(acc[mb][nb][0], acc[mb][nb][1]), pack_bf2(acc[mb][nb][2], acc[mb][nb][3])};
+
+  // Direct loads of m-block mb's G and U rows into buffer mb & 1: lane l
+  // fills the 16 bytes of row 4 it + l / 16 at chunk l % 16.
+  const long wrow = (m0 + wm * 64) * ni + n0 + wn * 128;
+  const bf16* Gw = static_cast<const bf16*>(a.G) + wrow;
+  const bf16* Uw = static_cast<const bf16*>(a.U) + wrow;
+  bf16* dGw = static_cast<bf16*>(a.dG) + wrow;
+  bf16* dUw = static_cast<bf16*>(a.dU) + wrow;
+  int eoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int R = 4 * it + g, c = s;
+    eoff[it] = R * (int)ni + 16 * ((c >> 1) ^ (R & 7)) + 8 * (c & 1);
+  }
+  char* const ringw = smem + kGluRing + w * 16384;
+  auto issue = [&](int mb) {
+    char* buf = ringw + (mb & 1) * 8192;
+    const int mo = mb * 16 * (int)ni;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(Gw + mo + eoff[it], buf + it * 1024);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(Uw + mo + eoff[it], buf + 4096 + it * 1024);
+  };
+
+  // The A operands of the wave's 64 rows (lane l stages row wm*64 + l), one
+  // array at a time; asm writes (see above).
+  const long trow = m0 + wm * 64 + lane;
+  char* const Tl = smem + kGluT;
+  const unsigned tw = lds_addr(Tl + (wm * 64 + lane) * 32);
+  auto stage_t = [&](auto Oc, const float (&v)[16]) {
+    constexpr int o = decltype(Oc)::value;
+    u32x4 lo, hi;
+    lo.x = pack_bf2(v[0], v[1]); lo.y = pack_bf2(v[2], v[3]);
+    lo.z = pack_bf2(v[4], v[5]); lo.w = pack_bf2(v[6], v[7]);
+    hi.x = pack_bf2(v[8], v[9]); hi.y = pack_bf2(v[10], v[11]);
+    hi.z = pack_bf2(v[12], v[13]); hi.w = pack_bf2(v[14], v[15]);
+    ds_w128_at<o * kBM * 32>(tw, lo);
+    ds_w128_at<o * kBM * 32 + 16>(tw, hi);
+  };
+  {
+    float v[16];
+    const f32x4* d4 = reinterpret_cast<const f32x4*>(a.dT + trow * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 x = d4[c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * c + e] = x[e];
+    }
+    stage_t(std::integral_constant<int, 0>{}, v);
+    load_rank<float, 16>(a.Tg + trow * a.r, 1, 0, a.r, v);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] *= a.sg;
+    stage_t(std::integral_constant<int, 1>{}, v);
+    load_rank<float, 16>(a.Tu + trow * a.r, 1, 0, a.r, v);
+#pragma unroll
+    for (int t = 0; t < 16; ++t) v[t] *= a.su;
+    stage_t(std::integral_constant<int, 2>{}, v);
+  }
+  issue(0);
+  issue(1);
+
+  f32x4 pacc[3][8];
+#pragma unroll
+  for (int o = 0; o < 3; ++o)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) pacc[o][nb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  // Per-lane bases.  Transpose reads: this lane addresses row Rr, columns
+  // 16 nb + 4 (s % 4) .. +3 (one base per nb).  Column writes of row 4g + j:
+  // the swizzle 32 ((nb ^ j) ^ 4 x), x = g & 1, is 32 (nb ^ j) + 128 x or
+  // - 128 x by bit 7 of 32 (nb ^ j).  Row reads: 16 bytes at 16 lane.
+  const int Rr = 4 * g + (s >> 2);
+  const unsigned rbase = lds_addr(ringw);
+  unsigned trb[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) trb[nb] = rbase + Rr * 256 + 32 * (nb ^ (Rr & 7)) + 8 * (s & 3);
+  const int x = g & 1;
+  const unsigned wlane = rbase + 4 * g * 256 + 2 * s;
+  const unsigned wplus = wlane + 128 * x, wminus = wlane - 128 * x;
+  const unsigned rowb = rbase + 16 * lane;
+  const unsigned tab = lds_addr(Tl + (wm * 64 + Rr) * 32 + 8 * (s & 3));
+
+  static_for<kMB>([&](auto MBc) {
+    constexpr int mb = decltype(MBc)::value;
+    constexpr int B = (mb & 1) * 8192;
+    // Operations issued after m-block mb's loads: mb 0: L1; 1: L2, S0;
+    // 2: S0, L3, S1; 3: S1, S2 (8 each).
+    vm_wait<mb == 0 ? 8 : (mb == 2 ? 24 : 16)>();
+    Frag4<bf16> aD, aG, aU;
+    aD.v = tr16_at<0 * kBM * 32 + mb * 512>(tab);
+    aG.v = tr16_at<1 * kBM * 32 + mb * 512>(tab);
+    aU.v = tr16_at<2 * kBM * 32 + mb * 512>(tab);
+    lgkm_tie0(aD.v, aG.v);
+    lgkm_tie0(aU.v);
+    static_for<2>([&](auto Hc) {           // two halves of 4 column blocks
+      constexpr int h0 = decltype(Hc)::value * 4;
+      u32x2 gv[4], uv[4];
+      static_for<4>([&](auto Kc) {
+        constexpr int k = decltype(Kc)::value;
+        gv[k] = tr16_at<B>(trb[h0 + k]);
+        uv[k] = tr16_at<B + 4096>(trb[h0 + k]);
+      });
+#pragma unroll
+      for (int k = 0; k < 4; ++k) lgkm_tie0(gv[k], uv[k]);
+      static_for<4>([&](auto Kc) {
+        constexpr int k = decltype(Kc)::value, nb = h0 + k;
+        const float dH4[4] = {bf_lo(dh[mb][nb].x), bf_hi(dh[mb][nb].x), bf_lo(dh[mb][nb].y), bf_hi(dh[mb][nb].y)};
+        const float G4[4] = {bf_lo(gv[k].x), bf_hi(gv[k].x), bf_lo(gv[k].y), bf_hi(gv[k].y)};
+        const float U4[4] = {bf_lo(uv[k].x), bf_hi(uv[k].x), bf_lo(uv[k].y), bf_hi(uv[k].y)};
+        float h4[4], g4[4], u4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float ph, dph;
+          act_both<ACT>(G4[j], ph, dph);
+          g4[j] = dH4[j] * U4[j] * dph;
+          u4[j] = dH4[j] * ph;
+          h4[j] = ph * U4[j];
+        }
+        const Frag4<bf16> fh = make_frag4<bf16>(h4), fg = make_frag4<bf16>(g4), fu = make_frag4<bf16>(u4);
+        pacc[0][nb] = mma4(pacc[0][nb], aD, fh);
+        pacc[1][nb] = mma4(pacc[1][nb], aG, fg);
+        pacc[2][nb] = mma4(pacc[2][nb], aU, fu);
+        // dG, dU over G, U: rows 4g + j, column 16 nb + s.
+        static_for<4>([&](auto Jc) {
+          constexpr int j = decltype(Jc)::value;
+          constexpr int A = 32 * (nb ^ j);
+          constexpr int off = B + j * 256 + A;
+          const unsigned base = (A & 128) ? wminus : wplus;
+          const unsigned vg = (j < 2) ? fg.v.x : fg.v.y, vu = (j < 2) ? fu.v.x : fu.v.y;
+          if constexpr (j & 1) {
+            ds_w16_hi_at<off>(base, vg);
+            ds_w16_hi_at<off + 4096>(base, vu);
+          } else {
+            ds_w16_lo_at<off>(base, vg);
+            ds_w16_lo_at<off + 4096>(base, vu);
+          }
+        });
+      });
+    });
+    // Rows back out: the 16-byte chunks the loads brought in.
+    u32x4 og[4], ou[4];
+    static_for<4>([&](auto Ic) {
+      constexpr int it = decltype(Ic)::value;
+      og[it] = rd128_at<B + it * 1024>(rowb);
+      ou[it] = rd128_at<B + 4096 + it * 1024>(rowb);
+    });
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      tie<0>(og[it]);
+      tie<0>(ou[it]);
+    }
+    // The buffer is free: next-but-one m-block's loads, then this one's stores.
+    if constexpr (mb + 2 < kMB) issue(mb + 2);
+    asm volatile("" ::: "memory");
+    const int mo = mb * 16 * (int)ni;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) *reinterpret_cast<u32x4*>(dGw + mo + eoff[it]) = og[it];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) *reinterpret_cast<u32x4*>(dUw + mo + eoff[it]) = ou[it];
+    asm volatile("" ::: "memory");
+  });
+  float* const parts[3] = {a.pA_d + (long)rb * ni * 16, a.pB_g + (long)rb * ni * 16, a.pB_u + (long)rb * ni * 16};
+  reduce_store_partials<3, 3>(smem, pacc, parts, n0, ni);
+}
+
+template <class T, int ACT, bool FAST, bool FULL = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   constexpr bool TR = sizeof(T) == 2;   // bf16: transpose-read K-loop, natural column order
   __shared__ __align__(16) char smem[kDownBwdLds];
@@ -470,11 +684,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   auto fb = [&](int R, int slot, int t0, float* v) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (slot != 0 || n >= ni) return;
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(Ad[(long)(t0 + e) * ni + n]);
+    load_rank<T, ET<T>::VEC>(Ad + n, ni, t0, a.r, v);
   };
   const float fs[kMaxSide] = {1.f, 0.f, 0.f};
   fold<T>(smem, acc, 1, fs, fb);
+  if constexpr (FULL) {
+    static_assert(FAST, "whole-tile GLU backward is part of the bf16 fast path");
+    glu_bwd_full<ACT>(smem, acc, a, m0, n0, rb);
+    return;
+  }
 
   // Epilogue: the lane's view of a row is the 8 consecutive columns c0 .. c0+7.
   char* wpark = smem + kDownParkOff + q.w * 16384;
@@ -794,8 +1012,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;
     const T* src = (slot == 0) ? Ag : Au;
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(src[(long)(t0 + e) * h + n]);
+    load_rank<T, ET<T>::VEC>(src + n, h, t0, a.r, v);
   };
   const float fs[kMaxSide] = {a.sg, a.su, 0.f};
   fold<T>(smem, acc, 2, fs, fb);
@@ -867,8 +1084,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_proj_dx_bwd(ProjDxArgs a) {
     const long n = n0 + (TR ? R : lds_row_col(0, R));
     if (n >= h) return;
     const T* src = static_cast<const T*>(a.A[slot < NP ? slot : 0]);
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(src[(long)(t0 + e) * h + n]);
+    load_rank<T, ET<T>::VEC>(src + n, h, t0, a.r, v);
   };
   const float fs[kMaxSide] = {1.f, 1.f, 1.f};
   fold<T>(smem, acc, NP, fs, fb);

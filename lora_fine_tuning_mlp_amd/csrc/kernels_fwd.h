@@ -107,8 +107,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
     gateup_row(R, j0, up, j);
     if (slot != up || j >= a.i) return;
     const T* src = (up ? Bu : Bg) + (long)j * a.r;
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(src[t0 + e]);
+    load_rank<T, ET<T>::VEC>(src, 1, t0, a.r, v);
   };
   const float fs[kMaxSide] = {a.sg, a.su, 0.f};
   fold<T>(smem, acc, 2, fs, fb);
@@ -216,8 +215,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
       gateup_row(R, j0, up, j);
       if (slot != up || j >= a.i) return;
       const bf16* src = (up ? Bu : Bg) + (long)j * a.r;
-      for (int e = 0; e < 8; ++e)
-        if (t0 + e < a.r) v[e] = (float)src[t0 + e];
+      load_rank<bf16, 8>(src, 1, t0, a.r, v);
     };
     fold_run(FA, smem + kRunFBOff, acc, fb);
 
@@ -325,8 +323,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   auto fb = [&](int R, int slot, int t0, float* v) {
     const long n = n0 + lds_row_col(0, R);
     if (slot != 0 || n >= a.O) return;
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(B[n * a.r + t0 + e]);
+    load_rank<T, ET<T>::VEC>(B + n * a.r, 1, t0, a.r, v);
   };
   const float fs[kMaxSide] = {a.s, 0.f, 0.f};
   fold<T>(smem, acc, 1, fs, fb);
@@ -555,8 +552,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     const int p = proj_of(o);
     if (slot_of(p) != slot) return;
     const T* src = static_cast<const T*>(a.B[p]) + (long)(o - a.off[p]) * a.r;
-    for (int e = 0; e < ET<T>::VEC; ++e)
-      if (t0 + e < a.r) v[e] = to_f<T>(src[t0 + e]);
+    load_rank<T, ET<T>::VEC>(src, 1, t0, a.r, v);
   };
   float fs[kMaxSide];
 #pragma unroll

@@ -508,8 +508,18 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       a.vecO = (i % 8 == 0) && al16(G) && al16(U) && al16(w.dG) && al16(w.dU);
       a.R = R; a.NC = (int)cdiv(i, kBN);
       const bool fast = fast_ok(DT<T>::code, h, N, {dY, dn.W}) && i % 8 == 0 && h % 64 == 0;
-      const int rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
-                                      dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+      // Whole tiles only: the GLU backward stages G, U through LDS (no masks).
+      const bool full = fast && a.vecO && N % kBM == 0 && i % kBN == 0 && N * (long)i < (1L << 31);
+      int rc;
+      if constexpr (sizeof(T) == 2) {
+        if (full) {
+          rc = launch(5, k_down_bwd<T, ACT, true, true>, dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
+          if (rc) return rc;
+        }
+      }
+      if (!full)
+        rc = LORA_LAUNCH_FAST(5, fast, (k_down_bwd<T, ACT, true>), (k_down_bwd<T, ACT, false>),
+                              dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
       if (rc) return rc;
     }
     {
