@@ -176,6 +176,10 @@ bool fast_ok(int dtype, long K, long rows, std::initializer_list<const void*> pt
   return true;
 }
 
+// dX epilogues of the fast paths read X rows by raw buffer loads: aligned
+// rows and X at most 2 GB.
+bool x_buf_ok(int vecO, long N, long h) { return vecO && N * h * 2 <= (1L << 31); }
+
 struct Carver {
   char* base;
   size_t off = 0;
@@ -242,7 +246,9 @@ int split_prepare(const SplitWs& sw, hipStream_t st, SplitK& sk) {
 // Column ranges of the backward prologue (grid R x NCR, CPC chunks of BK
 // columns each): at least 8, more when there are few row blocks, so that the
 // grid still covers the CUs (a small call has R = 16 row blocks or fewer);
-// ranges that would get no chunk are dropped.
+// ranges that would get no chunk are dropped.  (Twice as many ranges, two
+// workgroups per CU, measured slower on MI355X: every range adds a dT
+// partial of N x 16 floats per adapter.)
 void prologue_ranges(long NCH, long R, int& NCR, int& CPC) {
   if (NCH <= 0) {
     NCR = 0;
@@ -465,6 +471,24 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
   return ok();
 }
 
+// The backward prologue with raw buffer loads (bf16, aligned rows, whole
+// 16-byte chunks of B rows (r % 8 == 0), every source it reads at most 2 GB,
+// so one 32-bit offset past the end reads zero).
+template <class T>
+int launch_prologue(const ProArgs& a, dim3 grid, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    const long lim = 1L << 31;
+    bool buf = a.vecP != 0 && a.vecB != 0;
+    if (a.qkv) {
+      for (int p = 0; p < 3; ++p) buf = buf && a.N * a.nh[p] * (long)a.d * 2 <= lim;
+    } else {
+      buf = buf && a.N * (long)a.O * 2 <= lim;
+    }
+    if (buf) return launch(4, k_bwd_prologue<T, true>, grid, dim3(kThreads), st, a);
+  }
+  return launch(4, k_bwd_prologue<T>, grid, dim3(kThreads), st, a);
+}
+
 template <class T, int ACT>
 int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const void* G, const void* U,
                  const void* Tsv, const lora_proj_t& g, const lora_proj_t& u, const lora_proj_t& dn, void* dX,
@@ -488,7 +512,7 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
       a.vecP = (h % V == 0) && al16(dY);
       a.vecB = (r % V == 0) && al16(dn.B);
-      int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      int rc = launch_prologue<T>(a, dim3(R, w.NCR), st);
       if (rc) return rc;
       rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
                   w.NCR, N);
@@ -533,8 +557,8 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       a.vecS = (r % V == 0) && al16(g.B) && al16(u.B);
       a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
       a.R = R; a.NC = (int)cdiv(h, kBN);
-      const bool fast =
-          fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 && i % 64 == 0;
+      const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 &&
+                        i % 64 == 0 && x_buf_ok(a.vecO, N, h);
       a.sk.S = 1;
       if (sizeof(T) == 2 && fast) {
         const int rc = split_prepare(w.split, st, a.sk);
@@ -705,7 +729,7 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
       a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
       a.vecP = nio ? true : sal;
       a.vecB = (r % V == 0) && bal;
-      rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      rc = launch_prologue<T>(a, dim3(R, w.NCR), st);
       if (rc) return rc;
       rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 3), dim3(256), st, (const float*)w.dT_part, w.dT,
                   w.NCR, N);
@@ -727,7 +751,8 @@ int qkv_bwd_impl(const lora_qkv_desc_t& d, const void* const (&dO)[3], const voi
       a.vecW = (h % V == 0) && wal;
       a.vecO = (h % 8 == 0) && al16(dX) && al16(X);
       a.R = R; a.NC = (int)cdiv(h, kBN);
-      const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0 && O % 64 == 0;
+      const bool fast = fast_ok(DT<T>::code, O, N, {w.dP, pr[0]->W, pr[1]->W, pr[2]->W}) && h % 8 == 0 &&
+                        O % 64 == 0 && x_buf_ok(a.vecO, N, h);
       rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 3>), (k_proj_dx_bwd<T, false, 3>), dim3(a.R * a.NC),
                             dim3(kGemmThreads), st, a);
       if (rc) return rc;
@@ -800,7 +825,7 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
       a.NCH = w.NCH; a.CPC = w.CPC; a.NCR = w.NCR;
       a.vecP = (out % V == 0) && al16(dY);
       a.vecB = (r % V == 0) && al16(p.B);
-      int rc = launch(4, k_bwd_prologue<T>, dim3(R, w.NCR), dim3(kThreads), st, a);
+      int rc = launch_prologue<T>(a, dim3(R, w.NCR), st);
       if (rc) return rc;
       rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 1), dim3(256), st, (const float*)w.dT_part, w.dT,
                   w.NCR, N);
@@ -820,7 +845,8 @@ int linear_bwd_impl(const lora_linear_desc_t& d, const void* dY, const void* X, 
       a.vecW = (in % V == 0) && al16(p.W);
       a.vecO = (in % 8 == 0) && al16(dX) && al16(X);
       a.R = R; a.NC = (int)cdiv(in, kBN);
-      const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0 && out % 64 == 0;
+      const bool fast = fast_ok(DT<T>::code, out, N, {dY, p.W}) && in % 8 == 0 && out % 64 == 0 &&
+                        x_buf_ok(a.vecO, N, in);
       const int rc = LORA_LAUNCH_FAST(7, fast, (k_proj_dx_bwd<T, true, 1>), (k_proj_dx_bwd<T, false, 1>),
                                       dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
       if (rc) return rc;
