@@ -511,7 +511,7 @@ struct KNPairLoader {
   const bf16* A0;
   const bf16* A1;
   long K0;
-  int aoff[4], boff[4], soff, woff;
+  int aoff[4], boff[4], soff;
   KRow krow;
   SRow srow;
   __device__ __forceinline__ void init(const bf16* a0, const bf16* a1, long k0, long lda, long M, long m0, long ldb,
@@ -520,18 +520,6 @@ struct KNPairLoader {
     A0 = a0;
     A1 = a1 ? a1 : a0;
     K0 = a1 ? k0 : (1L << 40);
-    {
-      // L2 warm-up line of this thread: threads 0..255 the 128-byte A row
-      // segment of row t, threads 256..511 one of the four 128-byte pieces
-      // of B row (t - 256) / 4.
-      const int t = threadIdx.x;
-      if (t < 256) {
-        woff = (int)(min(m0 + t, M - 1) * lda);
-      } else {
-        const int u = t - 256;
-        woff = (int)((u >> 2) * ldb + min(n0 + (u & 3) * 64, N - 8));
-      }
-    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       long row = m0 + direct2_row(it);
@@ -559,21 +547,7 @@ struct KNPairLoader {
       if ((threadIdx.x & 63) < 16) g2lds16(srow(0, k) + soff, Bs + kStage2TrB + 256 * (threadIdx.x >> 6));
     }
   }
-  // One 4-byte load that brings this thread's line of K tile kt into L2.
-  __device__ __forceinline__ unsigned warm(int kt) const {
-    const long k = (long)kt * 64;
-    const bf16* p = (threadIdx.x < 256) ? ((k >= K0) ? A1 + (k - K0) : A0 + k) : krow(k);
-    return *reinterpret_cast<const unsigned*>(p + woff);
-  }
 };
-
-// L2 warm-up in the transpose-read K-loop: each iteration also touches K tile
-// kt + 2 (one load per thread), so its direct loads one iteration later hit
-// L2; the end-of-iteration wait leaves that one load outstanding.
-constexpr bool kWarmL2 = false;
-__device__ __forceinline__ void sync_stage_keep1() {
-  asm volatile("s_waitcnt vmcnt(1) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Tile kt + 1 is issued at the top of iteration kt and has landed by its end.
 template <int NSIDE, class Loader>
@@ -583,27 +557,13 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
   if (nkt <= kt0) return;
   auto stage = [&](int kt) { return smem + ((kt - kt0) & 1) * kStage2Tr; };
   ld.issue(kt0, stage(kt0), stage(kt0) + kStage2A);
-  // wprev: the previous warm-up value, consumed once the wait after it has
-  // passed (consuming the current one would wait for its load).
-  unsigned wsum = 0u, wprev = 0u;
-  if constexpr (kWarmL2) {
-    asm volatile("" ::: "memory");
-    wprev = ld.warm(min(kt0 + 1, nkt - 1));
-    sync_stage_keep1();
-  } else {
-    sync_stage();
-  }
+  sync_stage();
   for (int kt = kt0; kt < nkt; ++kt) {
     const char* As = stage(kt);
     const char* Bs = As + kStage2A;
     if (kt + 1 < nkt) {
       char* An = stage(kt + 1);
       ld.issue(kt + 1, An, An + kStage2A);
-    }
-    unsigned wv = 0u;
-    if constexpr (kWarmL2) {
-      asm volatile("" ::: "memory");
-      wv = ld.warm(min(kt + 2, nkt - 1));
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -647,15 +607,8 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
         }
       }
     }
-    if constexpr (kWarmL2) {
-      sync_stage_keep1();
-      wsum ^= wprev;
-      wprev = wv;
-    } else {
-      sync_stage();
-    }
+    sync_stage();
   }
-  if constexpr (kWarmL2) asm volatile("" : : "v"(wsum));
 }
 
 

@@ -581,62 +581,123 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
       v[0] = t.x; v[1] = t.y;
     }
   };
-  // Bias of the lane's columns (the same for every row): pair halves x1, x2.
+  // Bias (x1, x2 halves) and q/k norm weights of the lane's columns (the same
+  // for every row).  Two forms of the same loads: per-lane branches at head
+  // dim 128, unconditional loads under uniform guards at head dim 64 (each
+  // form makes the other variant's register allocation spill about 200 bytes
+  // per lane).
   float b1v[NG][cw], b2v[NG][cw];
-#pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
-    const T* bp = nullptr;
-    int oo = 0;
-    if (o1 < O) {
-      const int p = proj_of(o1);
-      bp = static_cast<const T*>(p == 0 ? a.bias[0] : (p == 1 ? a.bias[1] : a.bias[2]));
-      oo = o1 - a.off[p];
-    }
-#pragma unroll
-    for (int e = 0; e < cw; ++e) {
-      b1v[gi][e] = bp ? to_f<T>(bp[oo + e]) : 0.f;
-      b2v[gi][e] = bp ? to_f<T>(bp[oo + half + e]) : 0.f;
-    }
-  }
-  // q/k norm weights of the lane's columns (index within the head).
   float w1v[NG][cw], w2v[NG][cw];
+  if constexpr (LG == 1) {
+    // Bias of the lane's columns (the same for every row): pair halves x1, x2.
 #pragma unroll
-  for (int gi = 0; gi < NG; ++gi) {
-    const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
-    const T* wp = nullptr;
-    int jj = 0;
-    if (a.norm && o1 < a.off[2]) {
-      const int p = proj_of(o1);
-      wp = static_cast<const T*>(p == 0 ? a.nw[0] : a.nw[1]);
-      jj = (o1 - a.off[p]) % a.d;
+    for (int gi = 0; gi < NG; ++gi) {
+      const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
+      const T* bp = nullptr;
+      int oo = 0;
+      if (o1 < O) {
+        const int p = proj_of(o1);
+        bp = static_cast<const T*>(p == 0 ? a.bias[0] : (p == 1 ? a.bias[1] : a.bias[2]));
+        oo = o1 - a.off[p];
+      }
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        b1v[gi][e] = bp ? to_f<T>(bp[oo + e]) : 0.f;
+        b2v[gi][e] = bp ? to_f<T>(bp[oo + half + e]) : 0.f;
+      }
     }
+    // q/k norm weights of the lane's columns (index within the head).
 #pragma unroll
-    for (int e = 0; e < cw; ++e) {
-      w1v[gi][e] = wp ? to_f<T>(wp[jj + e]) : 1.f;
-      w2v[gi][e] = wp ? to_f<T>(wp[jj + half + e]) : 1.f;
+    for (int gi = 0; gi < NG; ++gi) {
+      const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
+      const T* wp = nullptr;
+      int jj = 0;
+      if (a.norm && o1 < a.off[2]) {
+        const int p = proj_of(o1);
+        wp = static_cast<const T*>(p == 0 ? a.nw[0] : a.nw[1]);
+        jj = (o1 - a.off[p]) % a.d;
+      }
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        w1v[gi][e] = wp ? to_f<T>(wp[jj + e]) : 1.f;
+        w2v[gi][e] = wp ? to_f<T>(wp[jj + half + e]) : 1.f;
+      }
+    }
+  } else {
+    // Loads below are issued unconditionally from a valid address (a lane with
+    // nothing to read points at W_q and discards the value), so they go out
+    // together instead of one branch and one wait each.
+    const T* const dummy = static_cast<const T*>(a.W[0]);
+    // Bias of the lane's columns (the same for every row): pair halves x1, x2.
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int e = 0; e < cw; ++e) b1v[gi][e] = b2v[gi][e] = 0.f;
+    const bool anyb = a.bias[0] != nullptr || a.bias[1] != nullptr || a.bias[2] != nullptr;
+#pragma unroll
+    for (int gi = 0; gi < NG && anyb; ++gi) {
+      const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
+      const int o1c = min(o1, O - 1);
+      const int p = proj_of(o1c);
+      const T* bp = static_cast<const T*>(p == 0 ? a.bias[0] : (p == 1 ? a.bias[1] : a.bias[2]));
+      const bool use = bp != nullptr && o1 < O;
+      const T* src = use ? bp + (o1c - a.off[p]) : dummy;
+      T v1[cw], v2[cw];
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        v1[e] = src[e];
+        v2[e] = src[half + e];
+      }
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        b1v[gi][e] = use ? to_f<T>(v1[e]) : 0.f;
+        b2v[gi][e] = use ? to_f<T>(v2[e]) : 0.f;
+      }
+    }
+    // q/k norm weights of the lane's columns (index within the head).
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+      for (int e = 0; e < cw; ++e) w1v[gi][e] = w2v[gi][e] = 1.f;
+#pragma unroll
+    for (int gi = 0; gi < NG && a.norm; ++gi) {
+      const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
+      const int o1c = min(o1, O - 1);
+      const int p = proj_of(o1c);
+      const bool use = a.norm && o1 < a.off[2];
+      const T* src = use ? static_cast<const T*>(p == 0 ? a.nw[0] : a.nw[1]) + (o1c - a.off[p]) % a.d : dummy;
+      T v1[cw], v2[cw];
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        v1[e] = src[e];
+        v2[e] = src[half + e];
+      }
+#pragma unroll
+      for (int e = 0; e < cw; ++e) {
+        w1v[gi][e] = use ? to_f<T>(v1[e]) : 1.f;
+        w2v[gi][e] = use ? to_f<T>(v2[e]) : 1.f;
+      }
     }
   }
   const float inv_d = 1.0f / (float)a.d;
   const int nhqk = a.nh[0] + a.nh[1];
 #pragma unroll
   for (int mb = 0; mb < kMB; ++mb) {
+    asm volatile("" ::: "memory");   // keep later blocks' table loads from being hoisted (registers)
     float cc[4][NG][cw], ss[4][NG][cw];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const long row = m0 + acc_row(qe, mb, j);
-      const int s = (int)(row % a.S);
+      const int s = (int)(min(row, a.N - 1) % a.S);
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
-        const int jj = (o1 - a.off[proj_of(o1)]) % a.d;
-        if (row < a.N && o1 < O && proj_of(o1) < 2) {
-          load_cw(cs + (long)s * half + jj, cc[j][gi]);
-          load_cw(sn + (long)s * half + jj, ss[j][gi]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < cw; ++e) { cc[j][gi][e] = 1.f; ss[j][gi][e] = 0.f; }
-        }
+        // Every lane loads (clamped to a valid entry); the values are used
+        // only for rows < N, columns < O of q and k, as below.
+        const int o1c = min(o1, O - 1);
+        const int jj = min((o1c - a.off[proj_of(o1c)]) % a.d, half - cw);
+        load_cw(cs + (long)s * half + jj, cc[j][gi]);
+        load_cw(sn + (long)s * half + jj, ss[j][gi]);
       }
     }
 #pragma unroll
