@@ -615,18 +615,20 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
 
 // ---------------------------------------------------------------------------
 // Split K.  When a call has fewer output tiles than the chip has CUs, each
-// tile's K range is cut into S pieces run by S workgroups (blockIdx.x = tile
-// * S + split).  Each writes its fp32 accumulators, side accumulators and
-// (optionally) a parked side product from LDS to the workspace, then takes a
-// ticket from the tile's counter (zero before the launch).  The workgroup
-// holding the last ticket sums the S partials in split order, so the result
-// does not depend on which one finishes last, and runs the epilogue; the
-// others return.  No workgroup ever waits for another.
+// tile's K range is cut into S pieces, in two launches of the same kernel.
+// The partial pass (grid tiles x S, blockIdx.x = tile * S + split) runs each
+// piece's K-loop and writes its fp32 accumulators, side accumulators and
+// (optionally) a parked side product to the workspace.  The merge pass (grid
+// tiles) sums the S partials in split order, so the result does not depend
+// on timing, and runs the epilogue.  The launch boundary orders the two
+// passes: no workgroup waits for another, and no cache maintenance is needed
+// inside a kernel (a device-scope release per workgroup, with the L2 write-
+// back it implies, cost more than the K-loop at these sizes).
 // ---------------------------------------------------------------------------
 struct SplitK {
   float* part;     // [tiles][S][kSplitFloats]
-  int* cnt;        // [tiles]
   int S;           // 1: no split
+  int pass;        // with S > 1: 0 = partial pass, 1 = merge pass
 };
 constexpr int kSplitAcc = kMB * 8;                         // f32x4 accumulators per thread
 constexpr int kSplitSide = kMaxSide * kMB;                 // f32x4 side accumulators per thread
@@ -639,15 +641,15 @@ __device__ __forceinline__ void split_range(int nkt, int S, int split, int& kb, 
   ke = (int)((long)(split + 1) * nkt / S);
 }
 
+// Partial pass: this piece's accumulators (and the parked side product in
+// LDS at `flush`, if any) to the workspace.
 template <int NS>
-__device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int split, f32x4 (&acc)[kMB][8],
-                                            f32x4 (&sacc)[NS > 0 ? NS : 1][kMB], float* flush) {
-  __shared__ int s_ticket;
+__device__ __forceinline__ void split_store(const SplitK& sk, int tile, int split, f32x4 (&acc)[kMB][8],
+                                            f32x4 (&sacc)[NS > 0 ? NS : 1][kMB], const float* flush) {
   // An opaque copy of the thread id: nothing derived from it (the partial's
   // addresses) can be hoisted above the K-loop, where every register is taken.
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
-  __syncthreads();                               // the flush area may have been written by other threads
   f32x4* mine = reinterpret_cast<f32x4*>(sk.part + ((long)tile * sk.S + split) * kSplitFloats);
 #pragma unroll
   for (int i = 0; i < kSplitAcc; ++i) mine[i * kGemmThreads + tid] = acc[i >> 3][i & 7];
@@ -655,26 +657,19 @@ __device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int spli
   for (int sb = 0; sb < NS; ++sb)
 #pragma unroll
     for (int mb = 0; mb < kMB; ++mb) mine[(kSplitAcc + sb * kMB + mb) * kGemmThreads + tid] = sacc[sb][mb];
-  float* myflush = reinterpret_cast<float*>(mine + (kSplitAcc + kSplitSide) * kGemmThreads);
-  if (flush)
+  if (flush) {
+    __syncthreads();                             // the flush area was written by other threads
+    float* myflush = reinterpret_cast<float*>(mine + (kSplitAcc + kSplitSide) * kGemmThreads);
     for (int e = tid; e < kSplitFlush; e += kGemmThreads) myflush[e] = flush[e];
-  // Release only (write back, no invalidate): the workgroups that are not
-  // last never read anything the others wrote.  Every wave releases its own
-  // stores; thread 0 releases again after the barrier, right before the
-  // ticket, so the release that heads the ticket covers the whole workgroup's
-  // partial (the barrier orders the other waves' stores before it).
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  if (tid == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    s_ticket = atomicAdd(sk.cnt + tile, 1);
   }
-  __syncthreads();
-  if (s_ticket != sk.S - 1) return false;
-  // The last workgroup acquires once; the barrier orders every wave's reads
-  // of the partials after it (one invalidation covers the CU and its L2).
-  if (tid == 0) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  __syncthreads();
+}
+
+// Merge pass: acc, sacc (and the parked side product into LDS at `flush`)
+// as the sum of the tile's S partials, in split order.
+template <int NS>
+__device__ __forceinline__ void split_load(const SplitK& sk, int tile, f32x4 (&acc)[kMB][8],
+                                           f32x4 (&sacc)[NS > 0 ? NS : 1][kMB], float* flush) {
+  const int tid = threadIdx.x;
 #pragma unroll
   for (int i = 0; i < kMB; ++i)
 #pragma unroll
@@ -709,12 +704,6 @@ __device__ __forceinline__ bool split_merge(const SplitK& sk, int tile, int spli
     }
   }
   __syncthreads();
-  return true;
-}
-
-static __global__ void k_split_zero(int* cnt, int n) {   // static: the header is in two translation units
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) cnt[i] = 0;
 }
 
 __device__ __forceinline__ void zero_acc(f32x4 (&acc)[kMB][8]) {

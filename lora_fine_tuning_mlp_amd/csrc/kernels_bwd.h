@@ -1128,7 +1128,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   static_assert(FAST || !SPLIT, "split K on the fast path only");
   __shared__ __align__(16) char smem[FAST ? kGemmLdsX : kGemmLds];
   const int S = SPLIT ? a.sk.S : 1;
-  const int tile = blockIdx.x / S, split = blockIdx.x % S;
+  const bool merge = SPLIT && a.sk.pass == 1;      // split K: merge pass (grid = tiles)
+  const int tile = merge ? (int)blockIdx.x : (int)blockIdx.x / S, split = merge ? 0 : (int)blockIdx.x % S;
   int rb, cb;
   tile_coords_at(tile, a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
@@ -1149,37 +1150,42 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
     // bf16, i % 64 == 0, r == 16: the dG tiles carry only dT_g, the dU tiles
     // only dT_u.  Two K-loop phases with one side accumulator; dT_g parks in
     // the flush slot.
-    KNPairLoader<KRow2<bf16>, SRowLin<bf16>, 1> ld;
-    ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
-    ld.srow.B = Bg; ld.srow.kb = 0; ld.srow.ld = r;          // phase 1: B_g rows
-    ld.init(dG, dU, ni, ni, a.N, m0, h, n0, h, r);
     f32x4 sacc[1][kMB];
-    zero_side(sacc);
-    const int nk0 = (int)(ni / 64);
-    int kb, ke;                                      // this split's K tiles over both phases
-    split_range(2 * nk0, S, split, kb, ke);
-    kloop2tr<1>(smem, min(ke, nk0), ld, acc, sacc, kb);
-    {
-      const WaveId q = wave_id();
-      float* fl = reinterpret_cast<float*>(smem + kFlushOff);
-      if (q.wn == 0)
+    if (merge) {
+      split_load<1>(a.sk, tile, acc, sacc, reinterpret_cast<float*>(smem + kFlushOff));
+    } else {
+      KNPairLoader<KRow2<bf16>, SRowLin<bf16>, 1> ld;
+      ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
+      ld.srow.B = Bg; ld.srow.kb = 0; ld.srow.ld = r;          // phase 1: B_g rows
+      ld.init(dG, dU, ni, ni, a.N, m0, h, n0, h, r);
+      zero_side(sacc);
+      const int nk0 = (int)(ni / 64);
+      int kb, ke;                                      // this split's K tiles over both phases
+      split_range(2 * nk0, S, split, kb, ke);
+      kloop2tr<1>(smem, min(ke, nk0), ld, acc, sacc, kb);
+      {
+        const WaveId q = wave_id();
+        float* fl = reinterpret_cast<float*>(smem + kFlushOff);
+        if (q.wn == 0)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
+          for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] = sacc[0][mb][j];
-      __syncthreads();
-      if (q.wn == 1)
+            for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] = sacc[0][mb][j];
+        __syncthreads();
+        if (q.wn == 1)
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
+          for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] += sacc[0][mb][j];
-    }
-    zero_side(sacc);
-    ld.srow.B = Bu;                                  // phase 2: B_u rows
-    ld.srow.kb = ni;
-    kloop2tr<1>(smem, ke, ld, acc, sacc, max(kb, nk0));
-    if constexpr (SPLIT) {
-      if (!split_merge<1>(a.sk, tile, split, acc, sacc, reinterpret_cast<float*>(smem + kFlushOff))) return;
+            for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] += sacc[0][mb][j];
+      }
+      zero_side(sacc);
+      ld.srow.B = Bu;                                  // phase 2: B_u rows
+      ld.srow.kb = ni;
+      kloop2tr<1>(smem, ke, ld, acc, sacc, max(kb, nk0));
+      if constexpr (SPLIT) {
+        split_store<1>(a.sk, tile, split, acc, sacc, reinterpret_cast<const float*>(smem + kFlushOff));
+        return;
+      }
     }
     side_reduce<T, 1>(smem, sacc, 1);                // dT_u -> slot 1
     {

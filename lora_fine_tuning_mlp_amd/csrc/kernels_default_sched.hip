@@ -15,8 +15,15 @@
 
 namespace lora {
 
-hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, dim3 grid, hipStream_t st) {
-  hipLaunchKernelGGL((k_mlp_dx_bwd<bf16, true, true>), grid, dim3(kGemmThreads), 0, st, a);
+// Split-K MLP dX: the partial pass (tiles x S workgroups), then the merge
+// pass (one workgroup per tile).
+hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_mlp_dx_bwd<bf16, true, true>), dim3(a.R * a.NC * a.sk.S), dim3(kGemmThreads), 0, st, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  MlpDxArgs m = a;
+  m.sk.pass = 1;
+  hipLaunchKernelGGL((k_mlp_dx_bwd<bf16, true, true>), dim3(a.R * a.NC), dim3(kGemmThreads), 0, st, m);
   return hipGetLastError();
 }
 

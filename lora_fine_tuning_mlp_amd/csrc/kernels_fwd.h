@@ -263,7 +263,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   __shared__ __align__(16) char smem[kGemmLds];
   const WaveId q = wave_id();
   const int S = FAST ? a.sk.S : 1;
-  const int tile = blockIdx.x / S, split = blockIdx.x % S;
+  const bool merge = S > 1 && a.sk.pass == 1;      // split K: merge pass (grid = tiles)
+  const int tile = merge ? (int)blockIdx.x : (int)blockIdx.x / S, split = merge ? 0 : (int)blockIdx.x % S;
   int rb, cb;
   tile_coords_at(tile, a.R * a.NC, a.R, a.NC, 8, rb, cb);
   const long m0 = (long)rb * kBM;
@@ -282,19 +283,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
   zero_acc(acc);
   zero_side(sacc);
   if constexpr (FAST) {
-    NKPairLoader<1> ld;
-    ld.init_a(Z, a.K, a.N, m0);
-    ld.bfallback = W;
-    ld.smask = 1u;
+    if (merge) {
+      split_load<1>(a.sk, tile, acc, sacc, nullptr);
+    } else {
+      NKPairLoader<1> ld;
+      ld.init_a(Z, a.K, a.N, m0);
+      ld.bfallback = W;
+      ld.smask = 1u;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
-    ld.srow = A;
-    const int sr = ld.side_row();
-    if (sr >= 0) ld.srow = ld.side_ptr(A, sr, a.r, a.K, A);
-    int kb, ke;
-    split_range(a.K / 64, S, split, kb, ke);
-    kloop2<1>(smem, ke, ld, acc, sacc, kb);
-    if (S > 1 && !split_merge<1>(a.sk, tile, split, acc, sacc, nullptr)) return;
+      for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
+      ld.srow = A;
+      const int sr = ld.side_row();
+      if (sr >= 0) ld.srow = ld.side_ptr(A, sr, a.r, a.K, A);
+      int kb, ke;
+      split_range(a.K / 64, S, split, kb, ke);
+      kloop2<1>(smem, ke, ld, acc, sacc, kb);
+      if (S > 1) {
+        split_store<1>(a.sk, tile, split, acc, sacc, nullptr);
+        return;
+      }
+    }
   } else {
     NKLoader<T, RowsA<T>, 1> ld;
     ld.a.init(Z, nullptr, a.K, 0, a.K, a.N, m0, a.vecA);

@@ -24,7 +24,7 @@ using namespace lora;
 namespace lora {
 // Defined in kernels_default_sched.hip (a translation unit of its own,
 // compiled with the default instruction scheduling).
-hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, dim3 grid, hipStream_t st);
+hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, hipStream_t st);
 template <class T>
 hipError_t launch_linear_fwd(bool fast, const LinearArgs& a, dim3 grid, hipStream_t st);
 template <class T>
@@ -63,7 +63,7 @@ int ok() {
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd",  "k_linear_fwd", "k_rope_table", "k_qkv_fwd",
                         "k_bwd_prologue", "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd",
-                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd", "k_split_zero"};
+                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -193,18 +193,16 @@ struct Carver {
 
 // Splits of a GEMM's K range when the call has fewer output tiles than the
 // chip has CUs (256 on MI355X).  S splits cost about nkt * c_k / S for the
-// K-loop and c_m * S for the merge (one workgroup reads the S partial tiles
-// one after another).  Measured on MI355X: c_k ~ 1.7 us per K tile of 64;
-// c_m ~ 10 us per 360 KB partial with a few tiles merging, ~30 us with 64
-// (they share the fabric), i.e. c_m ~ 10 + 0.3 tiles.  So
-// S ~ sqrt(c_k nkt / c_m), at most one workgroup per CU and 16 splits.
-// Shape-only, so the workspace queries and the launches agree; used on the
-// bf16 fast paths (K % 64 == 0).
+// partial pass and c_m * S for the merge pass (one workgroup per tile reads
+// the S partial tiles).  Measured on MI355X: c_k ~ 2.1 us per K tile of 64
+// at these sizes; c_m ~ 5 us per 376 KB partial.  So S ~ sqrt(c_k nkt /
+// c_m), at most one workgroup per CU and 16 splits.  Shape-only, so the
+// workspace queries and the launches agree; used on the bf16 fast paths
+// (K % 64 == 0).
 constexpr int kCUs = 256;
 int split_count(long tiles, long nkt) {
   if (tiles <= 0 || tiles >= kCUs || nkt <= 0) return 1;
-  const double c_m = 10.0 + 0.3 * (double)tiles;
-  long S = (long)(std::sqrt(1.7 * (double)nkt / c_m) + 0.5);
+  long S = (long)(std::sqrt(2.1 * (double)nkt / 5.0) + 0.5);
   if (S > kCUs / tiles) S = kCUs / tiles;
   if (S > 16) S = 16;
   return S < 1 ? 1 : (int)S;
@@ -219,7 +217,6 @@ void run_layout(long R, long NC, int& L, int& RPB, int& nruns) {
 }
 struct SplitWs {
   float* part = nullptr;
-  int* cnt = nullptr;
   int S = 1;
   long tiles = 0;
 };
@@ -228,19 +225,25 @@ SplitWs take_split(C& c, bool eligible, long tiles, long nkt) {
   SplitWs sw;
   sw.S = eligible ? split_count(tiles, nkt) : 1;
   sw.tiles = tiles;
-  if (sw.S > 1) {
-    sw.part = c.template take<float>((size_t)tiles * sw.S * kSplitFloats * 4);
-    sw.cnt = c.template take<int>((size_t)tiles * 4);
-  }
+  if (sw.S > 1) sw.part = c.template take<float>((size_t)tiles * sw.S * kSplitFloats * 4);
   return sw;
 }
-// Counter reset before a split launch; the kernels' SplitK argument.
-int split_prepare(const SplitWs& sw, hipStream_t st, SplitK& sk) {
+// The kernels' SplitK argument (partial pass first).
+void split_setup(const SplitWs& sw, SplitK& sk) {
   sk.part = sw.part;
-  sk.cnt = sw.cnt;
   sk.S = sw.S;
-  if (sw.S <= 1) return LORA_OK;
-  return launch(11, k_split_zero, dim3((unsigned)cdiv(sw.tiles, 256)), dim3(256), st, sw.cnt, (int)sw.tiles);
+  sk.pass = 0;
+}
+// Both passes of a split linear forward, or the one launch of an unsplit one.
+template <class T>
+hipError_t launch_linear_fwd_passes(bool fast, const LinearArgs& a, hipStream_t st) {
+  hipError_t e = launch_linear_fwd<T>(fast, a, dim3(a.R * a.NC * a.sk.S), st);
+  if (e == hipSuccess && a.sk.S > 1) {
+    LinearArgs m = a;
+    m.sk.pass = 1;
+    e = launch_linear_fwd<T>(fast, m, dim3(a.R * a.NC), st);
+  }
+  return e;
 }
 
 // Column ranges of the backward prologue (grid R x NCR, CPC chunks of BK
@@ -460,12 +463,8 @@ int mlp_fwd_impl(const lora_mlp_desc_t& d, const void* X, const lora_proj_t& g, 
     a.R = R; a.NC = (int)cdiv(h, kBN);
     const bool fast = fast_ok(DT<T>::code, i, N, {w.H, dn.W, dn.A}) && i % 64 == 0;
     a.sk.S = 1;
-    if (sizeof(T) == 2 && fast) {
-      const int rc = split_prepare(w.split, st, a.sk);
-      if (rc) return rc;
-    }
-    const dim3 grid(a.R * a.NC * a.sk.S);
-    const int rc = launch_call(1, st, [&]() { return launch_linear_fwd<T>(fast, a, grid, st); });
+    if (sizeof(T) == 2 && fast) split_setup(w.split, a.sk);
+    const int rc = launch_call(1, st, [&]() { return launch_linear_fwd_passes<T>(fast, a, st); });
     if (rc) return rc;
   }
   return ok();
@@ -560,16 +559,12 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       const bool fast = fast_ok(DT<T>::code, i, N, {w.dG, w.dU, g.W, u.W, g.B, u.B}) && h % 8 == 0 && r == 16 &&
                         i % 64 == 0 && x_buf_ok(a.vecO, N, h);
       a.sk.S = 1;
-      if (sizeof(T) == 2 && fast) {
-        const int rc = split_prepare(w.split, st, a.sk);
-        if (rc) return rc;
-      }
+      if (sizeof(T) == 2 && fast) split_setup(w.split, a.sk);
       int rc = LORA_OK;
       bool split = false;
       if constexpr (sizeof(T) == 2) {
         if (a.sk.S > 1) {                          // set only on the bf16 fast path
-          const dim3 grid(a.R * a.NC * a.sk.S);
-          rc = launch_call(6, st, [&]() { return launch_mlp_dx_split_bf16(a, grid, st); });
+          rc = launch_call(6, st, [&]() { return launch_mlp_dx_split_bf16(a, st); });
           split = true;
         }
       }
@@ -794,12 +789,8 @@ int linear_fwd_impl(const lora_linear_desc_t& d, const void* X, const lora_proj_
   a.R = (int)cdiv(N, kBM); a.NC = (int)cdiv(out, kBN);
   const bool fast = fast_ok(DT<T>::code, in, N, {X, p.W, p.A}) && in % 64 == 0;
   a.sk.S = 1;
-  if (sizeof(T) == 2 && fast) {
-    const int rc = split_prepare(w.split, st, a.sk);
-    if (rc) return rc;
-  }
-  const dim3 grid(a.R * a.NC * a.sk.S);
-  const int rc = launch_call(1, st, [&]() { return launch_linear_fwd<T>(fast, a, grid, st); });
+  if (sizeof(T) == 2 && fast) split_setup(w.split, a.sk);
+  const int rc = launch_call(1, st, [&]() { return launch_linear_fwd_passes<T>(fast, a, st); });
   if (rc) return rc;
   return ok();
 }
