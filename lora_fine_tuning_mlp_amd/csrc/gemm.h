@@ -680,20 +680,27 @@ __device__ __forceinline__ void split_load(const SplitK& sk, int tile, f32x4 (&a
     for (int mb = 0; mb < kMB; ++mb) sacc[sb][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   if (flush)
     for (int e = tid; e < kSplitFlush; e += kGemmThreads) flush[e] = 0.f;
+  // Accumulators: four at a time from up to four partials at once (16 loads
+  // in flight), added in split order.
+  const f32x4* p0 = reinterpret_cast<const f32x4*>(sk.part + (long)tile * sk.S * kSplitFloats);
+  for (int sp0 = 0; sp0 < sk.S; sp0 += 4) {
+#pragma unroll
+    for (int i0 = 0; i0 < kSplitAcc; i0 += 4) {
+      f32x4 t[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)   // (past the last partial: reload it, discarded below)
+          t[u][k] = p0[min(sp0 + u, sk.S - 1) * (kSplitFloats / 4) + (i0 + k) * kGemmThreads + tid];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (sp0 + u < sk.S) acc[(i0 + k) >> 3][(i0 + k) & 7] += t[u][k];
+    }
+  }
   for (int sp = 0; sp < sk.S; ++sp) {
     const f32x4* pp = reinterpret_cast<const f32x4*>(sk.part + ((long)tile * sk.S + sp) * kSplitFloats);
-    // Eight loads in flight at a time (one at a time when each add follows
-    // its load in the same registers).
-#pragma unroll
-    for (int i0 = 0; i0 < kSplitAcc; i0 += 8) {
-      f32x4 t[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) t[k] = pp[(i0 + k) * kGemmThreads + tid];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) asm volatile("" : "+v"(t[k]));
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[(i0 + k) >> 3][(i0 + k) & 7] += t[k];
-    }
 #pragma unroll
     for (int sb = 0; sb < NS; ++sb)
 #pragma unroll
