@@ -96,7 +96,23 @@ def _per_kernel(path: str, counter: str):
     return vals, copies
 
 
-def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str, out_md: str, cmds) -> None:
+def _trace_avg_us(stats_csv: str):
+    """Average duration (us) per kernel from a kernel_stats.csv (with the
+    recorder names of base_name)."""
+    out = {}
+    for r in csv.DictReader(open(stats_csv)):
+        k = base_name(r["Name"])
+        n, tot = int(r["Calls"]), float(r["TotalDurationNs"])
+        pn, pt = out.get(k, (0, 0.0))
+        out[k] = (pn + n, pt + tot)
+    return {k: t / n / 1e3 for k, (n, t) in out.items() if n}
+
+
+def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: str, out_md: str, cmds,
+                    stats_csv=None, note=None) -> None:
+    """Bytes per launch from FETCH_SIZE / WRITE_SIZE runs (out_json "-": no
+    JSON); with stats_csv (a kernel trace of the same program) also the
+    achieved rate of those bytes over the traced average duration."""
     fv, fcopy = _per_kernel(fetch_csv, "FETCH_SIZE")
     wv, wcopy = _per_kernel(write_csv, "WRITE_SIZE")
     if not fcopy or not wcopy:
@@ -110,8 +126,15 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: s
     for c in cmds:
         lines += ["```", c, "```", ""]
     lines += [f"Calibration: a device copy of {copy_bytes} bytes reads FETCH_SIZE {max(fcopy):.0f} KiB and "
-              f"WRITE_SIZE {max(wcopy):.0f} KiB; scale factors {f_scale:.4f} (fetch), {w_scale:.4f} (write).", "",
-              "| kernel | dispatches | fetch MB | write MB | total MB |", "|---|---:|---:|---:|---:|"]
+              f"WRITE_SIZE {max(wcopy):.0f} KiB; scale factors {f_scale:.4f} (fetch), {w_scale:.4f} (write).", ""]
+    if note:
+        lines += [note, ""]
+    avg = _trace_avg_us(stats_csv) if stats_csv else {}
+    if avg:
+        lines += ["| kernel | dispatches | fetch MB | write MB | total MB | avg us (trace) | GB/s | of 8 TB/s |",
+                  "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    else:
+        lines += ["| kernel | dispatches | fetch MB | write MB | total MB |", "|---|---:|---:|---:|---:|"]
     for k in sorted(fv):
         if not k.startswith("k_"):
             continue
@@ -119,9 +142,15 @@ def traffic_summary(fetch_csv: str, write_csv: str, copy_bytes: int, out_json: s
         wb = (sum(wv[k]) / len(wv[k]) * 1024.0 * w_scale) if wv.get(k) else 0.0
         res[k] = {"fetch_bytes": fb, "write_bytes": wb, "bytes_per_launch": fb + wb, "dispatches": len(fv[k]),
                   "source_hash": sh}
-        lines.append(f"| `{k}` | {len(fv[k])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |")
+        row = f"| `{k}` | {len(fv[k])} | {fb / 1e6:.1f} | {wb / 1e6:.1f} | {(fb + wb) / 1e6:.1f} |"
+        if avg:
+            us = avg.get(k)
+            row += (f" {us:.1f} | {(fb + wb) / (us * 1e-6) / 1e9:.0f} | {(fb + wb) / (us * 1e-6) / 8e12:.2f} |"
+                    if us else " | | |")
+        lines.append(row)
     lines += ["", f"HIP sources hash: `{sh}`"]
-    json.dump(res, open(out_json, "w"), indent=1)
+    if out_json != "-":
+        json.dump(res, open(out_json, "w"), indent=1)
     open(out_md, "w").write("\n".join(lines) + "\n")
 
 
@@ -160,7 +189,7 @@ STALL_RATIOS = [
     ("wait_any", "SQ_WAIT_ANY"),           # waiting on anything else: s_waitcnt, barrier
     ("wait_lds", "SQ_WAIT_INST_LDS"),      # waiting to issue an LDS instruction
     ("valu", "SQ_ACTIVE_INST_VALU"),       # issue split by instruction type (VALU includes MFMA)
-    ("vmem", "SQ_ACTIVE_INST_VMEM"),       # buffer instructions (global_* loads are FLAT-encoded)
+    ("vmem", "SQ_ACTIVE_INST_VMEM"),
     ("flat", "SQ_ACTIVE_INST_FLAT"),
     ("lds", "SQ_ACTIVE_INST_LDS"),
     ("salu", "SQ_ACTIVE_INST_SCA"),
@@ -241,6 +270,8 @@ def main():
     t.add_argument("out_json")
     t.add_argument("out_md")
     t.add_argument("--cmd", action="append", default=[])
+    t.add_argument("--stats", default=None, help="kernel_stats.csv of a trace of the same program (adds GB/s)")
+    t.add_argument("--note", default=None)
     c = sub.add_parser("counters")
     c.add_argument("csv")
     c.add_argument("out")
@@ -266,7 +297,7 @@ def main():
     elif a.what == "stalls":
         stalls_summary(a.csv, a.out, a.cmd)
     else:
-        traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.out_json, a.out_md, a.cmd)
+        traffic_summary(a.fetch_csv, a.write_csv, a.copy_bytes, a.out_json, a.out_md, a.cmd, a.stats, a.note)
 
 
 if __name__ == "__main__":
