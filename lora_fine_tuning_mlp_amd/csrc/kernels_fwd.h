@@ -190,7 +190,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
     f32x4 sacc[2][kMB];
     zero_acc(acc);
     zero_side(sacc);
-    kloop2<2>(smem, nkt, ld, acc, sacc, 0, !first);
+    if (first) {
+      kloop2<2>(smem, nkt, ld, acc, sacc, 0, false);
+    } else {
+      // Later tiles of the run carry no side product: the loop without it.
+      f32x4 snone[1][kMB];
+      kloop2<0>(smem, nkt, ld, acc, snone, 0, true);
+    }
     if (cb + 1 < cb1) {                 // the next tile's first K tile, into stage 0
       set_cols(cb + 1);
       ld.smask = 0u;
