@@ -144,6 +144,108 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
 // T_g, T_u of the row block are computed in the run's first tile only (the
 // later tiles skip the side loads and MFMAs) and folded into every tile from
 // the run's fold operand in LDS.
+// Whole-tile ping-pong K-loop for a gate/up tile without side product: the
+// wave groups 0-3 (rows 0-127) and 4-7 (rows 128-255) run one phase apart.
+// In its read phase a group reads all 24 fragments of the K tile (and issues
+// the global loads of the next one: each group its 128 A rows, group 0 all
+// 256 B rows); in its MFMA phase it issues the tile's 64 MFMAs, while the
+// other group reads.  Barriers separate the phases; group 1 starts one
+// barrier late and group 0 ends one barrier late, so every wave passes the
+// same number.  Needs whole B rows (j0 + 128 <= i); the two stages and the
+// stage-1 side-row area (the run's fold operand) are as in kloop2.
+__device__ __forceinline__ void gateup_kloop_pp(char* smem, int nkt, const bf16* X, long h, long N, long m0,
+                                                const bf16* Wg, const bf16* Wu, int j0, f32x4 (&acc)[kMB][8]) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int grp = w >> 2, wl = w & 3;
+  const WaveId q = wave_id();
+  const int L = threadIdx.x & 63;
+  const int chunk = (L & 7) ^ (L >> 3);
+  int aoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    long row = m0 + 8 * (grp * 16 + wl + 4 * it) + (L >> 3);
+    if (row > N - 1) row = N - 1;
+    aoff[it] = (int)(row * h) + chunk * 8;
+  }
+  // B block wl + 4 it (LDS rows 8 (wl + 4 it) + L / 8), by gateup_row: up
+  // for it % 4 >= 2, column j = 64 [it >= 4] + 4 c + ((b0 + 2 (it & 1)) & 3)
+  // with x = 8 wl + L / 8, c = x % 16, b0 = x / 16.  So a lane needs two
+  // offsets; the rest is uniform.
+  const int x = 8 * wl + (L >> 3);
+  int boff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) boff[p] = (4 * (x & 15) + (((x >> 4) + 2 * p) & 3)) * (int)h + chunk * 8;
+  const bf16* Wg0 = Wg + (long)j0 * h;
+  const bf16* Wu0 = Wu + (long)j0 * h;
+  const long half = 64 * h;
+  // The lane offsets pass through an empty asm each time, so the compiler
+  // cannot hoist 64-bit addresses out of the loop (they would be spilled).
+  auto issue = [&](int kt, char* S) {
+    const int k = kt * 64;
+    int ao[4] = {aoff[0], aoff[1], aoff[2], aoff[3]};
+    asm volatile("" : "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]), "+v"(ao[3]));
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(X + ao[it] + k, S + (grp * 16 + wl + 4 * it) * 1024);
+    if (grp == 0) {
+      int bo[2] = {boff[0], boff[1]};
+      asm volatile("" : "+v"(bo[0]), "+v"(bo[1]));
+#pragma unroll
+      for (int it = 0; it < 8; ++it) {
+        const bf16* base = ((it & 3) >= 2 ? Wu0 : Wg0) + (it >= 4 ? half : 0);
+        g2lds16(base + bo[it & 1] + k, S + kStage2A + (wl + 4 * it) * 1024);
+      }
+    }
+  };
+  auto bar = [] { asm volatile("s_barrier" ::: "memory"); };
+  auto stage = [&](int kt) { return smem + (kt & 1) * kStage2; };
+  issue(0, stage(0));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  bar();
+  if (grp == 1) bar();
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const char* S = stage(kt);
+    if (kt + 1 < nkt) issue(kt + 1, stage(kt + 1));
+    u32x4 av[2][kMB], bv[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) av[ks][mb] = rd128(S + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) bv[ks][nb] = rd128(S + kStage2A + lds_off2(q.wn * 128 + nb * 16 + q.r16, ks * 4 + q.g));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) tie<0>(av[ks][mb]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) tie<0>(bv[ks][nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        Frag<bf16> bfr;
+        bfr.v = bv[ks][nb];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+          Frag<bf16> af;
+          af.v = av[ks][mb];
+          acc[mb][nb] = mma(acc[mb][nb], af, bfr);
+        }
+      }
+    if (kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (grp == 0) bar();
+}
+
 template <int ACT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
   __shared__ __align__(16) char smem[kRunLds];
@@ -158,24 +260,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
   const bf16* Bg = static_cast<const bf16*>(a.Bg);
   const bf16* Bu = static_cast<const bf16*>(a.Bu);
 
-  NKPairLoader<2> ld;
-  ld.init_a(X, a.h, a.N, m0);
-  ld.bfallback = Wg;
-  auto set_cols = [&](int cb) {
+  // The loader of a kloop2 tile (X rows, B rows of column block cb, side
+  // rows when smask != 0); built where it is used, so nothing of it lives
+  // through the ping-pong tiles.
+  auto make_ld = [&](int cb, unsigned smask) {
+    NKPairLoader<2> ld;
+    ld.init_a(X, a.h, a.N, m0);
+    ld.bfallback = Wg;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       int up, j;
       gateup_row(ld.row_of(it), cb * 128, up, j);
       ld.brow[it] = (j < a.i) ? (up ? Wu : Wg) + (long)j * a.h : nullptr;
     }
-  };
-  set_cols(cb0);
-  ld.smask = 3u;
-  ld.srow = Ag;
-  {
+    ld.smask = smask;
+    ld.srow = Ag;
     const int sr = ld.side_row();
     if (sr >= 0) ld.srow = ld.side_ptr((sr >> 4) == 0 ? Ag : Au, sr & 15, a.r, a.h, Ag);
-  }
+    return ld;
+  };
   const float fs[kMaxSide] = {a.sg, a.su, 0.f};
   char* FA = smem + kRunFAOff;
   bf16* Go = static_cast<bf16*>(a.G);
@@ -190,17 +293,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
     f32x4 sacc[2][kMB];
     zero_acc(acc);
     zero_side(sacc);
+    // Later tiles of the run carry no side product: whole tiles take the
+    // ping-pong loop, a ragged last tile the plain loop without side work.
     if (first) {
+      const NKPairLoader<2> ld = make_ld(cb, 3u);
       kloop2<2>(smem, nkt, ld, acc, sacc, 0, false);
+    } else if (j0 + 128 <= a.i) {
+      gateup_kloop_pp(smem, nkt, X, a.h, a.N, m0, Wg, Wu, j0, acc);
     } else {
-      // Later tiles of the run carry no side product: the loop without it.
+      const NKPairLoader<2> ld = make_ld(cb, 0u);
       f32x4 snone[1][kMB];
-      kloop2<0>(smem, nkt, ld, acc, snone, 0, true);
-    }
-    if (cb + 1 < cb1) {                 // the next tile's first K tile, into stage 0
-      set_cols(cb + 1);
-      ld.smask = 0u;
-      ld.issue(0, smem, smem + kStage2A);
+      kloop2<0>(smem, nkt, ld, acc, snone, 0, false);
     }
     const WaveId q = wave_id_opaque();   // everything after the K-loop derives from this
     if (first) {
