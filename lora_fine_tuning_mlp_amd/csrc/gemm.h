@@ -613,6 +613,108 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
 
 
 
+// Whole-tile ping-pong form of kloop2tr without side block.  Wave groups
+// 0-3 (rows 0-127) and 4-7 (rows 128-255) run one phase apart: in its read
+// phase a group reads every fragment of the K tile it needs (8 A reads, 32
+// transpose reads) and issues the next tile's loads (each group its own 128
+// A rows, group 0 the whole B tile); in its MFMA phase it issues the tile's
+// 64 MFMAs while the other group reads.  Barriers separate the phases; group
+// 1 starts one barrier late and group 0 ends one barrier late, so every wave
+// passes the same number.  Operands and stages as kloop2tr (A split along K
+// at K0, krow(k) the B row of K row k, every K tile inside one segment).
+template <class KRow>
+__device__ __forceinline__ void kloop2tr_pp(char* smem, int nkt, const bf16* A0, const bf16* A1, long K0,
+                                            const KRow& krow, long lda, long M, long m0, long ldb, long n0,
+                                            long N, f32x4 (&acc)[kMB][8]) {
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int grp = w >> 2, wl = w & 3;
+  const WaveId q = wave_id();
+  const int L = threadIdx.x & 63;
+  if (A1 == nullptr) { A1 = A0; K0 = 1L << 40; }
+  int aoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    long row = m0 + 8 * (grp * 16 + wl + 4 * it) + (L >> 3);
+    if (row > M - 1) row = M - 1;
+    aoff[it] = (int)(row * lda) + direct2_chunk(L) * 8;
+  }
+  // B block wl + 4 it holds K rows 8 it + r0 (r0 = 2 wl + L / 32); its
+  // swizzle depends on it only through it & 1, so a lane keeps two offsets.
+  const int r0 = 2 * wl + (L >> 5);
+  int boff[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int lseg = (L & 31) ^ ftr(8 * p + r0);
+    boff[p] = (int)(r0 * ldb + min(n0 + lseg * 8, N - 8));
+  }
+  // The lane offsets pass through an empty asm at each use, so no 64-bit
+  // address is hoisted out of the loop (it would be spilled).
+  auto issue = [&](int kt, char* S) {
+    const long k = (long)kt * 64;
+    const bf16* ab = (k >= K0) ? A1 + (k - K0) : A0 + k;
+    int ao[4] = {aoff[0], aoff[1], aoff[2], aoff[3]};
+    asm volatile("" : "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]), "+v"(ao[3]));
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(ab + ao[it], S + (grp * 16 + wl + 4 * it) * 1024);
+    if (grp == 0) {
+      const bf16* bb = krow(k);
+      int bo[2] = {boff[0], boff[1]};
+      asm volatile("" : "+v"(bo[0]), "+v"(bo[1]));
+#pragma unroll
+      for (int it = 0; it < 8; ++it) g2lds16(bb + 8 * it * ldb + bo[it & 1], S + kStage2A + (wl + 4 * it) * 1024);
+    }
+  };
+  auto bar = [] { asm volatile("s_barrier" ::: "memory"); };
+  auto stage = [&](int kt) { return smem + (kt & 1) * kStage2Tr; };
+  if (nkt <= 0) return;
+  issue(0, stage(0));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  bar();
+  if (grp == 1) bar();
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const char* S = stage(kt);
+    if (kt + 1 < nkt) issue(kt + 1, stage(kt + 1));
+    u32x4 av[2][kMB];
+    u32x2 lo[2][8], hi[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) av[ks][mb] = rd128(S + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) tr_issue(S + kStage2A + ks * 32 * 512, nb, q, lo[ks][nb], hi[ks][nb]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) tie<0>(av[ks][mb]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) lgkm_tie0(lo[ks][nb], hi[ks][nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const Frag<bf16> bfr = tr_make(lo[ks][nb], hi[ks][nb]);
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+          Frag<bf16> af;
+          af.v = av[ks][mb];
+          acc[mb][nb] = mma(acc[mb][nb], af, bfr);
+        }
+      }
+    if (kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (grp == 0) bar();
+}
+
 // ---------------------------------------------------------------------------
 // Split K.  When a call has fewer output tiles than the chip has CUs, each
 // tile's K range is cut into S pieces, in two launches of the same kernel.

@@ -864,10 +864,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
   const int nkt = (a.h + ET<T>::BK - 1) / ET<T>::BK;
   if constexpr (FAST) {
     static_assert(TR, "the fast path is bf16");
-    KNPairLoader<KRow1<bf16>, SRowNone<bf16>, 0> ld;      // h % 64 == 0
-    ld.krow.W = Wd; ld.krow.K = h; ld.krow.ld = ni;
-    ld.init(dY, nullptr, h, h, a.N, m0, ni, n0, ni, 0);
-    kloop2tr<0>(smem, (int)(h / 64), ld, acc, sacc);
+    KRow1<bf16> kr;                                       // h % 64 == 0
+    kr.W = Wd; kr.K = h; kr.ld = ni;
+    kloop2tr_pp(smem, (int)(h / 64), dY, nullptr, h, kr, h, a.N, m0, ni, n0, ni, acc);
   } else if constexpr (TR) {
     KNTrLoader<RowsA<T>, KRow1<T>, SRowNone<T>, SMaskNone, 0> ld;
     ld.a.init(dY, nullptr, h, 0, h, a.N, m0, a.vecA);
@@ -1277,10 +1276,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_proj_dx_bwd(ProjDxArgs a) {
   const int nkt = (a.O + ET<T>::BK - 1) / ET<T>::BK;
   if constexpr (FAST) {
     static_assert(TR, "the fast path is bf16");
-    KNPairLoader<KRow3<bf16>, SRowNone<bf16>, 0> ld;      // O % 64 == 0
-    ld.krow = kr;
-    ld.init(dP, nullptr, a.O, a.O, a.N, m0, h, n0, h, 0);
-    kloop2tr<0>(smem, a.O / 64, ld, acc, sacc);
+    // O % 64 == 0
+    kloop2tr_pp(smem, a.O / 64, reinterpret_cast<const bf16*>(dP), nullptr, a.O, kr, a.O, a.N, m0, h, n0, h, acc);
   } else if constexpr (TR) {
     KNTrLoader<RowsA<T>, KRow3<T>, SRowNone<T>, SMaskNone, 0> ld;
     ld.a.init(dP, nullptr, a.O, 0, a.O, a.N, m0, a.vecA);
