@@ -626,10 +626,12 @@ template <class KRow>
 __device__ __forceinline__ void kloop2tr_pp(char* smem, int nkt, const bf16* A0, const bf16* A1, long K0,
                                             const KRow& krow, long lda, long M, long m0, long ldb, long n0,
                                             long N, f32x4 (&acc)[kMB][8]) {
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  // Lane values from an opaque thread id: nothing is shared with (or kept
+  // live from) code around the loop, e.g. the tiles of a run.
+  const WaveId q = wave_id_opaque();
+  const int w = __builtin_amdgcn_readfirstlane(q.w);
   const int grp = w >> 2, wl = w & 3;
-  const WaveId q = wave_id();
-  const int L = threadIdx.x & 63;
+  const int L = q.lane;
   if (A1 == nullptr) { A1 = A0; K0 = 1L << 40; }
   int aoff[4];
 #pragma unroll

@@ -561,14 +561,18 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
       a.sk.S = 1;
       if (sizeof(T) == 2 && fast) split_setup(w.split, a.sk);
       int rc = LORA_OK;
-      bool split = false;
+      bool done = false;
       if constexpr (sizeof(T) == 2) {
         if (a.sk.S > 1) {                          // set only on the bf16 fast path
           rc = launch_call(6, st, [&]() { return launch_mlp_dx_split_bf16(a, st); });
-          split = true;
+          done = true;
+        } else if (fast) {                         // runs of column tiles
+          run_layout(a.R, a.NC, a.L, a.RPB, a.nruns);
+          rc = launch(6, k_mlp_dx_run<T>, dim3(a.nruns), dim3(kGemmThreads), st, a);
+          done = true;
         }
       }
-      if (!split)
+      if (!done)
         rc = LORA_LAUNCH_FAST(6, fast, (k_mlp_dx_bwd<T, true>), (k_mlp_dx_bwd<T, false>), dim3(a.R * a.NC),
                               dim3(kGemmThreads), st, a);
       if (rc) return rc;

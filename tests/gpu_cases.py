@@ -52,6 +52,9 @@ MLP_CASES = [
     # few output tiles, long K: the down projection and dX split their K range
     S.MLPConfig("mlp_bf16_splitk", 64, 512, 2048, 16, 2.0, "swiglu", "bf16"),
     S.MLPConfig("mlp_bf16_splitk_cross", 100, 256, 1472, 16, 2.0, "geglu_tanh", "bf16"),
+    # more dX tiles than CUs (17 x 17): runs of two column tiles, a last run of
+    # one, a ragged last row block and a 64-wide last column tile
+    S.MLPConfig("mlp_bf16_dx_runs_ragged", 4200, 4160, 128, 16, 2.0, "swiglu", "bf16"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),

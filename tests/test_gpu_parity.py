@@ -201,7 +201,9 @@ def test_rope_position_zero_identity_on_device():
 
 
 def test_determinism():
-    for cfg in (gc.MLP_CASES[1], gc.QKV_CASES[0], gc.LINEAR_CASES[0], gc.MLP_CASES[-1], gc.LINEAR_CASES[-1]):
+    mlp = {c.name: c for c in gc.MLP_CASES}
+    for cfg in (gc.MLP_CASES[1], gc.QKV_CASES[0], gc.LINEAR_CASES[0], mlp["mlp_bf16_splitk_cross"],
+                mlp["mlp_bf16_dx_runs_ragged"], gc.LINEAR_CASES[-1]):
         if isinstance(cfg, S.MLPConfig):
             t = S.mlp_inputs(cfg, 3)
             a, b = gc.run_mlp_gpu(cfg, t), gc.run_mlp_gpu(cfg, t)
