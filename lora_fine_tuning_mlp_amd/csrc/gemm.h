@@ -613,6 +613,96 @@ __device__ __forceinline__ void kloop2tr(char* smem, int nkt, const Loader& ld, 
 
 
 
+// Whole-tile ping-pong K-loop over [N][K] operands (the kloop2 layout)
+// without side rows.  Wave groups 0-3 (rows 0-127) and 4-7 (rows 128-255)
+// run one phase apart: in its read phase a group reads all 24 fragments of
+// the K tile (and issues the global loads of the next one: each group its
+// 128 A rows, group 0 all 256 B rows); in its MFMA phase it issues the
+// tile's 64 MFMAs while the other group reads.  Barriers separate the
+// phases; group 1 starts one barrier late and group 0 ends one barrier late,
+// so every wave passes the same number.  B block wl + 4 it (it = 0..7, LDS
+// rows 8 (wl + 4 it) + L / 8) comes from bp.base(it) + bp.off[bp.sel(it)]:
+// a uniform pointer plus one of the lane's two offsets (whole B rows only).
+template <class BP>
+__device__ __forceinline__ void nk_kloop_pp(char* smem, int nkt, const bf16* X, long lda, long M, long m0,
+                                            const BP& bp, f32x4 (&acc)[kMB][8]) {
+  const WaveId q = wave_id_opaque();
+  const int w = __builtin_amdgcn_readfirstlane(q.w);
+  const int grp = w >> 2, wl = w & 3;
+  const int L = q.lane;
+  int aoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    long row = m0 + 8 * (grp * 16 + wl + 4 * it) + (L >> 3);
+    if (row > M - 1) row = M - 1;
+    aoff[it] = (int)(row * lda) + direct2_chunk(L) * 8;
+  }
+  // The lane offsets pass through an empty asm at each use, so no 64-bit
+  // address is hoisted out of the loop (it would be spilled).
+  auto issue = [&](int kt, char* S) {
+    const int k = kt * 64;
+    int ao[4] = {aoff[0], aoff[1], aoff[2], aoff[3]};
+    asm volatile("" : "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]), "+v"(ao[3]));
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(X + ao[it] + k, S + (grp * 16 + wl + 4 * it) * 1024);
+    if (grp == 0) {
+      int bo[2] = {bp.off[0], bp.off[1]};
+      asm volatile("" : "+v"(bo[0]), "+v"(bo[1]));
+#pragma unroll
+      for (int it = 0; it < 8; ++it) g2lds16(bp.base(it) + bo[bp.sel(it)] + k, S + kStage2A + (wl + 4 * it) * 1024);
+    }
+  };
+  auto bar = [] { asm volatile("s_barrier" ::: "memory"); };
+  auto stage = [&](int kt) { return smem + (kt & 1) * kStage2; };
+  if (nkt <= 0) return;
+  issue(0, stage(0));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  bar();
+  if (grp == 1) bar();
+  __builtin_amdgcn_sched_barrier(0);
+  for (int kt = 0; kt < nkt; ++kt) {
+    const char* S = stage(kt);
+    if (kt + 1 < nkt) issue(kt + 1, stage(kt + 1));
+    u32x4 av[2][kMB], bv[2][8];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) av[ks][mb] = rd128(S + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) bv[ks][nb] = rd128(S + kStage2A + lds_off2(q.wn * 128 + nb * 16 + q.r16, ks * 4 + q.g));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < kMB; ++mb) tie<0>(av[ks][mb]);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) tie<0>(bv[ks][nb]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        Frag<bf16> bfr;
+        bfr.v = bv[ks][nb];
+#pragma unroll
+        for (int mb = 0; mb < kMB; ++mb) {
+          Frag<bf16> af;
+          af.v = av[ks][mb];
+          acc[mb][nb] = mma(acc[mb][nb], af, bfr);
+        }
+      }
+    if (kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    bar();
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (grp == 0) bar();
+}
+
 // Whole-tile ping-pong form of kloop2tr without side block.  Wave groups
 // 0-3 (rows 0-127) and 4-7 (rows 128-255) run one phase apart: in its read
 // phase a group reads every fragment of the K tile it needs (8 A reads, 32

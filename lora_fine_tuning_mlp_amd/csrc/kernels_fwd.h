@@ -144,107 +144,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
 // T_g, T_u of the row block are computed in the run's first tile only (the
 // later tiles skip the side loads and MFMAs) and folded into every tile from
 // the run's fold operand in LDS.
-// Whole-tile ping-pong K-loop for a gate/up tile without side product: the
-// wave groups 0-3 (rows 0-127) and 4-7 (rows 128-255) run one phase apart.
-// In its read phase a group reads all 24 fragments of the K tile (and issues
-// the global loads of the next one: each group its 128 A rows, group 0 all
-// 256 B rows); in its MFMA phase it issues the tile's 64 MFMAs, while the
-// other group reads.  Barriers separate the phases; group 1 starts one
-// barrier late and group 0 ends one barrier late, so every wave passes the
-// same number.  Needs whole B rows (j0 + 128 <= i); the two stages and the
-// stage-1 side-row area (the run's fold operand) are as in kloop2.
-__device__ __forceinline__ void gateup_kloop_pp(char* smem, int nkt, const bf16* X, long h, long N, long m0,
-                                                const bf16* Wg, const bf16* Wu, int j0, f32x4 (&acc)[kMB][8]) {
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int grp = w >> 2, wl = w & 3;
-  const WaveId q = wave_id();
-  const int L = threadIdx.x & 63;
-  const int chunk = (L & 7) ^ (L >> 3);
-  int aoff[4];
+// B rows of a gate/up tile for nk_kloop_pp: block wl + 4 it holds LDS rows
+// 8 (wl + 4 it) + L / 8, by gateup_row up for it % 4 >= 2 and intermediate
+// column j0 + 64 [it >= 4] + 4 c + ((b0 + 2 (it & 1)) & 3) with x = 8 wl +
+// L / 8, c = x % 16, b0 = x / 16: two lane offsets, the rest uniform.
+struct GateUpPP {
+  const bf16* Wg0; const bf16* Wu0; long half;
+  int off[2];
+  __device__ __forceinline__ GateUpPP(const bf16* Wg, const bf16* Wu, long h, int j0, int wl, int L) {
+    Wg0 = Wg + (long)j0 * h;
+    Wu0 = Wu + (long)j0 * h;
+    half = 64 * h;
+    const int x = 8 * wl + (L >> 3), chunk = direct2_chunk(L);
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    long row = m0 + 8 * (grp * 16 + wl + 4 * it) + (L >> 3);
-    if (row > N - 1) row = N - 1;
-    aoff[it] = (int)(row * h) + chunk * 8;
+    for (int p = 0; p < 2; ++p) off[p] = (4 * (x & 15) + (((x >> 4) + 2 * p) & 3)) * (int)h + chunk * 8;
   }
-  // B block wl + 4 it (LDS rows 8 (wl + 4 it) + L / 8), by gateup_row: up
-  // for it % 4 >= 2, column j = 64 [it >= 4] + 4 c + ((b0 + 2 (it & 1)) & 3)
-  // with x = 8 wl + L / 8, c = x % 16, b0 = x / 16.  So a lane needs two
-  // offsets; the rest is uniform.
-  const int x = 8 * wl + (L >> 3);
-  int boff[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) boff[p] = (4 * (x & 15) + (((x >> 4) + 2 * p) & 3)) * (int)h + chunk * 8;
-  const bf16* Wg0 = Wg + (long)j0 * h;
-  const bf16* Wu0 = Wu + (long)j0 * h;
-  const long half = 64 * h;
-  // The lane offsets pass through an empty asm each time, so the compiler
-  // cannot hoist 64-bit addresses out of the loop (they would be spilled).
-  auto issue = [&](int kt, char* S) {
-    const int k = kt * 64;
-    int ao[4] = {aoff[0], aoff[1], aoff[2], aoff[3]};
-    asm volatile("" : "+v"(ao[0]), "+v"(ao[1]), "+v"(ao[2]), "+v"(ao[3]));
-#pragma unroll
-    for (int it = 0; it < 4; ++it) g2lds16(X + ao[it] + k, S + (grp * 16 + wl + 4 * it) * 1024);
-    if (grp == 0) {
-      int bo[2] = {boff[0], boff[1]};
-      asm volatile("" : "+v"(bo[0]), "+v"(bo[1]));
-#pragma unroll
-      for (int it = 0; it < 8; ++it) {
-        const bf16* base = ((it & 3) >= 2 ? Wu0 : Wg0) + (it >= 4 ? half : 0);
-        g2lds16(base + bo[it & 1] + k, S + kStage2A + (wl + 4 * it) * 1024);
-      }
-    }
-  };
-  auto bar = [] { asm volatile("s_barrier" ::: "memory"); };
-  auto stage = [&](int kt) { return smem + (kt & 1) * kStage2; };
-  issue(0, stage(0));
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  bar();
-  if (grp == 1) bar();
-  __builtin_amdgcn_sched_barrier(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    const char* S = stage(kt);
-    if (kt + 1 < nkt) issue(kt + 1, stage(kt + 1));
-    u32x4 av[2][kMB], bv[2][8];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) av[ks][mb] = rd128(S + lds_off2(q.wm * 64 + mb * 16 + q.r16, ks * 4 + q.g));
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) bv[ks][nb] = rd128(S + kStage2A + lds_off2(q.wn * 128 + nb * 16 + q.r16, ks * 4 + q.g));
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < kMB; ++mb) tie<0>(av[ks][mb]);
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) tie<0>(bv[ks][nb]);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    bar();
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        Frag<bf16> bfr;
-        bfr.v = bv[ks][nb];
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          Frag<bf16> af;
-          af.v = av[ks][mb];
-          acc[mb][nb] = mma(acc[mb][nb], af, bfr);
-        }
-      }
-    if (kt + 1 < nkt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    bar();
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (grp == 0) bar();
-}
+  __device__ __forceinline__ const bf16* base(int it) const { return ((it & 3) >= 2 ? Wu0 : Wg0) + (it >= 4 ? half : 0); }
+  __device__ __forceinline__ static int sel(int it) { return it & 1; }
+};
 
 template <int ACT>
 __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
@@ -286,39 +203,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
   bf16* Ho = static_cast<bf16*>(a.H);
   const int nkt = a.h / 64;
 
-  for (int cb = cb0; cb < cb1; ++cb) {
-    const bool first = cb == cb0;
-    const int j0 = cb * 128;
-    f32x4 acc[kMB][8];
-    f32x4 sacc[2][kMB];
-    zero_acc(acc);
-    zero_side(sacc);
-    // Later tiles of the run carry no side product: whole tiles take the
-    // ping-pong loop, a ragged last tile the plain loop without side work.
-    if (first) {
-      const NKPairLoader<2> ld = make_ld(cb, 3u);
-      kloop2<2>(smem, nkt, ld, acc, sacc, 0, false);
-    } else if (j0 + 128 <= a.i) {
-      gateup_kloop_pp(smem, nkt, X, a.h, a.N, m0, Wg, Wu, j0, acc);
-    } else {
-      const NKPairLoader<2> ld = make_ld(cb, 0u);
-      f32x4 snone[1][kMB];
-      kloop2<0>(smem, nkt, ld, acc, snone, 0, false);
-    }
+  // Fold and the GLU epilogue (registers only) of the tile at column block
+  // cb: the lane holds gate (blocks 0..3) and up (blocks 4..7) of the same 4
+  // consecutive intermediate columns.
+  auto finish = [&](int cb, f32x4 (&acc)[kMB][8]) {
     const WaveId q = wave_id_opaque();   // everything after the K-loop derives from this
-    if (first) {
-      side_reduce<bf16, 2>(smem + kRunTsOff, sacc);
-      const float* Ts = ts_ptr(smem + kRunTsOff);
-      if (cb0 == 0 && q.tid < kBM) {    // T_g, T_u are saved once per row block
-        const long row = m0 + q.tid;
-        if (row < a.N)
-          for (int t = 0; t < a.r; ++t) {
-            a.Tg[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
-            a.Tu[row * a.r + t] = Ts[ts_idx(1, q.tid, t)];
-          }
-      }
-      build_fold_a(FA, Ts, 2, fs);
-    }
+    const int j0 = cb * 128;
     auto fb = [&](int R, int slot, int t0, float* v) {
       int up, j;
       gateup_row(R, j0, up, j);
@@ -327,9 +217,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
       load_rank<bf16, 8>(src, 1, t0, a.r, v);
     };
     fold_run(FA, smem + kRunFBOff, acc, fb);
-
-    // GLU epilogue (registers only): the lane holds gate (blocks 0..3) and
-    // up (blocks 4..7) of the same 4 consecutive intermediate columns.
     const int jj = j0 + q.wn * 64 + 4 * q.r16;
     const int nvalid = min(4, a.i - jj);
 #pragma unroll
@@ -350,6 +237,48 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
         gstore<bf16, 4>(Uo + off, uv, nvalid, a.vecO);
         gstore<bf16, 4>(Ho + off, hv, nvalid, a.vecO);
       }
+  };
+
+  {
+    // First tile: T_g, T_u ride the K-loop.
+    f32x4 acc[kMB][8];
+    f32x4 sacc[2][kMB];
+    zero_acc(acc);
+    zero_side(sacc);
+    {
+      const NKPairLoader<2> ld = make_ld(cb0, 3u);
+      kloop2<2>(smem, nkt, ld, acc, sacc, 0, false);
+    }
+    const WaveId q = wave_id_opaque();
+    side_reduce<bf16, 2>(smem + kRunTsOff, sacc);
+    const float* Ts = ts_ptr(smem + kRunTsOff);
+    if (cb0 == 0 && q.tid < kBM) {      // T_g, T_u are saved once per row block
+      const long row = m0 + q.tid;
+      if (row < a.N)
+        for (int t = 0; t < a.r; ++t) {
+          a.Tg[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
+          a.Tu[row * a.r + t] = Ts[ts_idx(1, q.tid, t)];
+        }
+    }
+    build_fold_a(FA, Ts, 2, fs);
+    finish(cb0, acc);
+  }
+  // Later tiles carry no side product: whole tiles take the ping-pong loop,
+  // a ragged last tile the plain loop without side work.
+  for (int cb = cb0 + 1; cb < cb1; ++cb) {
+    const int j0 = cb * 128;
+    f32x4 acc[kMB][8];
+    zero_acc(acc);
+    if (j0 + 128 <= a.i) {
+      const WaveId qo = wave_id_opaque();
+      const GateUpPP bp(Wg, Wu, a.h, j0, __builtin_amdgcn_readfirstlane(qo.w) & 3, qo.lane);
+      nk_kloop_pp(smem, nkt, X, a.h, a.N, m0, bp, acc);
+    } else {
+      const NKPairLoader<2> ld = make_ld(cb, 0u);
+      f32x4 snone[1][kMB];
+      kloop2<0>(smem, nkt, ld, acc, snone, 0, false);
+    }
+    finish(cb, acc);
   }
 }
 
@@ -365,6 +294,7 @@ struct LinearArgs {
   int vecA, vecW, vecS, vecO;
   int R, NC;
   SplitK sk;           // fast path only; sk.S == 1: no split
+  int L, RPB, nruns;   // run kernel: run length, runs per row block, runs
 };
 
 template <class T, bool FAST>
@@ -464,6 +394,127 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_linear_fwd(LinearArgs a) {
       for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j] + bv[nb];
       store_row8<T>(Y + row * a.O + c0, v, nvalid, a.vecO);
     }
+}
+
+// B rows of a linear tile for nk_kloop_pp (columns in perm_col(0, ..)
+// order): block wl + 4 it holds output column n0 + 128 (it / 4) + 2 (it % 4)
+// + 8 (x % 16) + x / 16 with x = 8 wl + L / 8: one lane offset.
+struct LinearPP {
+  const bf16* W0; long K;
+  int off[2];
+  __device__ __forceinline__ LinearPP(const bf16* W, long Kd, long n0, int wl, int L) {
+    W0 = W + n0 * Kd;
+    K = Kd;
+    const int x = 8 * wl + (L >> 3);
+    off[0] = off[1] = (8 * (x & 15) + (x >> 4)) * (int)Kd + direct2_chunk(L) * 8;
+  }
+  __device__ __forceinline__ const bf16* base(int it) const { return W0 + (128 * (it >> 2) + 2 * (it & 3)) * K; }
+  __device__ __forceinline__ static int sel(int) { return 0; }
+};
+
+// Fast path without split K as runs of column tiles (k_gateup_run's layout
+// and LDS): the run's first tile computes T = Z A^T in its K-loop and builds
+// the fold operand s T (bf16); whole later tiles take the ping-pong K-loop,
+// a ragged last one the plain loop, neither with side work.
+template <class T>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_linear_run(LinearArgs a) {
+  static_assert(sizeof(T) == 2, "the run kernel is bf16");
+  __shared__ __align__(16) char smem[kRunLds];
+  int rb, cb0, cb1;
+  run_coords(a.nruns, a.RPB, a.L, a.NC, rb, cb0, cb1);
+  const long m0 = (long)rb * kBM;
+  const bf16* Z = static_cast<const bf16*>(a.Z);
+  const bf16* W = static_cast<const bf16*>(a.W);
+  const bf16* A = static_cast<const bf16*>(a.A);
+  const bf16* B = static_cast<const bf16*>(a.B);
+  char* FA = smem + kRunFAOff;
+  const float fs[kMaxSide] = {a.s, 0.f, 0.f};
+  const int nkt = a.K / 64;
+
+  // The kloop2 loader of the tile at n0 (side rows when smask != 0).
+  auto make_ld = [&](long n0, unsigned smask) {
+    NKPairLoader<1> ld;
+    ld.init_a(Z, a.K, a.N, m0);
+    ld.bfallback = W;
+    ld.smask = smask;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const long n = n0 + lds_row_col(0, ld.row_of(it));
+      ld.brow[it] = (n < a.O) ? W + n * a.K : nullptr;
+    }
+    ld.srow = A;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = ld.side_ptr(A, sr, a.r, a.K, A);
+    return ld;
+  };
+
+  // Fold and store the tile at column n0 (bias added).
+  auto finish = [&](long n0, f32x4 (&acc)[kMB][8]) {
+    const WaveId q = wave_id_opaque();   // everything after the K-loop derives from this
+    auto fb = [&](int R, int slot, int t0, float* v) {
+      const long n = n0 + lds_row_col(0, R);
+      if (slot != 0 || n >= a.O) return;
+      load_rank<bf16, 8>(B + n * a.r, 1, t0, a.r, v);
+    };
+    fold_run(FA, smem + kRunFBOff, acc, fb);
+    bf16* Y = static_cast<bf16*>(a.Y);
+    const long c0 = n0 + q.wn * 128 + 8 * q.r16;
+    const int nvalid = (int)min(8L, a.O - c0);
+    float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (a.bias) {
+      const bf16* bp = static_cast<const bf16*>(a.bias) + c0;
+      for (int nb = 0; nb < nvalid; ++nb) bv[nb] = to_f<bf16>(bp[nb]);
+    }
+#pragma unroll
+    for (int mb = 0; mb < kMB; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long row = m0 + acc_row(q, mb, j);
+        if (row >= a.N || nvalid <= 0) continue;
+        float v[8];
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) v[nb] = acc[mb][nb][j] + bv[nb];
+        store_row8<bf16>(Y + row * a.O + c0, v, nvalid, a.vecO);
+      }
+  };
+
+  {
+    // First tile: T rides the K-loop.
+    const long n0 = (long)cb0 * kBN;
+    f32x4 acc[kMB][8];
+    f32x4 sacc[1][kMB];
+    zero_acc(acc);
+    zero_side(sacc);
+    {
+      const NKPairLoader<1> ld = make_ld(n0, 1u);
+      kloop2<1>(smem, nkt, ld, acc, sacc, 0, false);
+    }
+    const WaveId q = wave_id_opaque();
+    side_reduce<bf16, 1>(smem + kRunTsOff, sacc);
+    const float* Ts = ts_ptr(smem + kRunTsOff);
+    if (cb0 == 0 && q.tid < kBM) {      // T is saved once per row block
+      const long row = m0 + q.tid;
+      if (row < a.N)
+        for (int t = 0; t < a.r; ++t) a.T[row * a.r + t] = Ts[ts_idx(0, q.tid, t)];
+    }
+    build_fold_a(FA, Ts, 1, fs);
+    finish(n0, acc);
+  }
+  for (int cb = cb0 + 1; cb < cb1; ++cb) {
+    const long n0 = (long)cb * kBN;
+    f32x4 acc[kMB][8];
+    zero_acc(acc);
+    if (n0 + kBN <= a.O) {
+      const WaveId qo = wave_id_opaque();
+      const LinearPP bp(W, a.K, n0, __builtin_amdgcn_readfirstlane(qo.w) & 3, qo.lane);
+      nk_kloop_pp(smem, nkt, Z, a.K, a.N, m0, bp, acc);
+    } else {
+      const NKPairLoader<1> ld = make_ld(n0, 0u);
+      f32x4 snone[1][kMB];
+      kloop2<0>(smem, nkt, ld, acc, snone, 0, false);
+    }
+    finish(n0, acc);
+  }
 }
 
 // ===========================================================================

@@ -25,6 +25,7 @@ namespace lora {
 // Defined in kernels_default_sched.hip (a translation unit of its own,
 // compiled with the default instruction scheduling).
 hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, hipStream_t st);
+hipError_t launch_linear_run_bf16(const LinearArgs& a, hipStream_t st);
 template <class T>
 hipError_t launch_linear_fwd(bool fast, const LinearArgs& a, dim3 grid, hipStream_t st);
 template <class T>
@@ -237,6 +238,13 @@ void split_setup(const SplitWs& sw, SplitK& sk) {
 // Both passes of a split linear forward, or the one launch of an unsplit one.
 template <class T>
 hipError_t launch_linear_fwd_passes(bool fast, const LinearArgs& a, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (fast && a.sk.S == 1) {                   // runs of column tiles
+      LinearArgs r = a;
+      run_layout(r.R, r.NC, r.L, r.RPB, r.nruns);
+      return launch_linear_run_bf16(r, st);
+    }
+  }
   hipError_t e = launch_linear_fwd<T>(fast, a, dim3(a.R * a.NC * a.sk.S), st);
   if (e == hipSuccess && a.sk.S > 1) {
     LinearArgs m = a;

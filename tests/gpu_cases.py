@@ -55,6 +55,8 @@ MLP_CASES = [
     # more dX tiles than CUs (17 x 17): runs of two column tiles, a last run of
     # one, a ragged last row block and a 64-wide last column tile
     S.MLPConfig("mlp_bf16_dx_runs_ragged", 4200, 4160, 128, 16, 2.0, "swiglu", "bf16"),
+    # 17 x 16 dX tiles: the 64-wide last column tile is the second of its run
+    S.MLPConfig("mlp_bf16_dx_runs_ragged_tile", 4200, 3904, 128, 16, 2.0, "geglu_tanh", "bf16"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
@@ -87,6 +89,10 @@ LINEAR_CASES = [
     S.LinearConfig("linear_bf16_bias", 520, 512, 384, 16, 2.0, "bf16", bias=True),
     S.LinearConfig("linear_f32_bias_ragged", 90, 40, 70, 4, 2.0, "f32", bias=True),
     S.LinearConfig("linear_bf16_splitk_uneven", 200, 1600, 256, 16, 2.0, "bf16", bias=True),
+    # more output tiles than CUs (17 x 16, 17 x 17): runs of two column tiles
+    # with a 64-wide last tile inside a run, or a last run of one tile
+    S.LinearConfig("linear_bf16_runs_ragged", 4200, 192, 3904, 16, 2.0, "bf16", bias=True),
+    S.LinearConfig("linear_bf16_runs_of_one", 4200, 128, 4160, 8, 2.0, "bf16"),
 ]
 
 
