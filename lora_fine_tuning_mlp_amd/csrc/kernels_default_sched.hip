@@ -33,6 +33,12 @@ hipError_t launch_linear_run_bf16(const LinearArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// The head_dim-128 QKV forward as runs of column tiles (a.L, a.RPB, a.nruns set).
+hipError_t launch_qkv_run_bf16(const QKVFwdArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k_qkv_run<bf16>), dim3(a.nruns), dim3(kGemmThreads), 0, st, a);
+  return hipGetLastError();
+}
+
 template <class T>
 hipError_t launch_linear_fwd(bool fast, const LinearArgs& a, dim3 grid, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {

@@ -552,6 +552,7 @@ struct QKVFwdArgs {
   int off[4];          // column offsets: 0, Oq, Oq+Ok, O
   int vecA, vecW, vecS, vecO;
   int R, NC;
+  int L, RPB, nruns;   // run kernel: run length, runs per row block, runs
 };
 
 // LG = log2(256 / head_dim): 1 for d = 128, 2 for d = 64 (RoPE pairs share a lane).
@@ -615,121 +616,14 @@ struct QKVRowLoader {
   }
 };
 
-template <class T, int LG, bool FAST, int NS>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
-  __shared__ __align__(16) char smem[kGemmLds];
-  const WaveId q = wave_id();
-  int rb, cb;
-  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
-  const long m0 = (long)rb * kBM;
-  const int n0 = cb * kBN;
+// RoPE + split of a QKV tile after its fold (rows m0.., columns n0..): the
+// bias, the optional q/k RMSNorm, the rotation of q and k, and the stores
+// into the [B][heads][S][d] outputs.  qe: the wave id after the K-loop.
+template <class T, int LG>
+__device__ __forceinline__ void qkv_rope_store(QKVFwdArgs a, f32x4 (&acc)[kMB][8], long m0, int n0,
+                                               const WaveId& qe) {
   const int O = a.off[3];
-  const T* X = static_cast<const T*>(a.X);
-
-  // Projections overlapping this tile -> fold / side slots.  The projections
-  // are contiguous column ranges, so the tile overlaps a contiguous run of
-  // them: slot sl holds projection pfirst + sl, sl < nslot (plain arithmetic,
-  // no runtime-indexed array, which would live in scratch memory).
-  const int hi = min(n0 + kBN, O);
-  const int ov0 = (a.off[0] < hi && a.off[1] > n0) ? 1 : 0;
-  const int ov1 = (a.off[1] < hi && a.off[2] > n0) ? 1 : 0;
-  const int ov2 = (a.off[2] < hi && a.off[3] > n0) ? 1 : 0;
-  const int nslot = ov0 + ov1 + ov2;
-  const int pfirst = ov0 ? 0 : (ov1 ? 1 : 2);
   auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
-  auto slot_of = [&](int p) { return p - pfirst; };
-
-  auto brow_of = [&](int R) -> const T* {
-    const int o = n0 + lds_row_col(LG, R);
-    if (o >= O) return nullptr;
-    const int p = proj_of(o);
-    return static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
-  };
-  auto side_base = [&](int sl) -> const T* {        // side block sl: adapter of projection pfirst + sl
-    if (sl >= nslot) return nullptr;
-    const int pj = pfirst + sl;
-    return static_cast<const T*>(pj == 0 ? a.A[0] : (pj == 1 ? a.A[1] : a.A[2]));
-  };
-  const T* afall = static_cast<const T*>(pfirst == 0 ? a.A[0] : (pfirst == 1 ? a.A[1] : a.A[2]));
-
-  f32x4 acc[kMB][8];
-  f32x4 sacc[NS][kMB];
-  zero_acc(acc);
-  zero_side(sacc);
-  if constexpr (FAST && LG == 1) {
-    // head_dim 128: the per-lane row pointers fit in registers through the loop.
-    NKPairLoader<NS> ld;
-    ld.init_a(X, a.h, a.N, m0);
-    ld.bfallback = static_cast<const T*>(a.W[0]);
-    ld.smask = (1u << nslot) - 1u;
-#pragma unroll
-    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
-    ld.srow = afall;
-    const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
-    if (sr >= 0) ld.srow = ld.side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
-    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
-  } else if constexpr (FAST) {
-    // head_dim 64: the row pointers are derived inside the loop.
-    QKVRowLoader<NS, LG> ld;
-    ld.X = X;
-    ld.W0 = static_cast<const T*>(a.W[0]);
-    ld.W1 = static_cast<const T*>(a.W[1]);
-    ld.W2 = static_cast<const T*>(a.W[2]);
-    ld.S0 = side_base(0);
-    ld.S1 = side_base(1);
-    ld.S2 = side_base(2);
-    ld.afall = afall;
-    ld.N = a.N; ld.m0 = m0; ld.h = a.h; ld.n0 = n0; ld.r = a.r;
-    ld.off1 = a.off[1]; ld.off2 = a.off[2]; ld.off3 = a.off[3];
-    ld.smask = (1u << nslot) - 1u;
-    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
-  } else {
-    NKLoader<T, RowsA<T>, NS> ld;
-    ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
-    ld.bfallback = static_cast<const T*>(a.W[0]);
-    ld.K = a.h;
-    ld.vecB = a.vecW;
-    ld.vecS = a.vecS;
-    ld.smask = (1u << nslot) - 1u;
-#pragma unroll
-    for (int qq = 0; qq < 2; ++qq) ld.brow[qq] = brow_of(ld.row_of(qq));
-    ld.srow = nullptr;
-    const int sr = ld.side_row();
-    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
-    kloop<T, NS>(smem, (a.h + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
-  }
-  side_reduce<T, NS>(smem, sacc);
-  // A fresh (opaque) wave id for everything after the K-loop: the one above
-  // dies with the loader set-up instead of staying live through the loop.
-  const WaveId qe = wave_id();
-
-  // T_p is saved by the tile holding projection p's first column.
-  if (qe.tid < kBM) {
-    const float* Ts = ts_ptr(smem);
-    const long row = m0 + qe.tid;
-    for (int sl = 0; sl < nslot; ++sl) {
-      const int p = pfirst + sl;
-      if (a.off[p] >= n0 && a.off[p] < n0 + kBN && row < a.N)
-        for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, qe.tid, t)];
-    }
-  }
-
-  auto fb = [&](int R, int slot, int t0, float* v) {
-    const int o = n0 + lds_row_col(LG, R);
-    if (o >= O) return;
-    const int p = proj_of(o);
-    if (slot_of(p) != slot) return;
-    const T* src = static_cast<const T*>(a.B[p]) + (long)(o - a.off[p]) * a.r;
-    load_rank<T, ET<T>::VEC>(src, 1, t0, a.r, v);
-  };
-  float fs[kMaxSide];
-#pragma unroll
-  for (int sl = 0; sl < kMaxSide; ++sl) {
-    const int p = min(pfirst + sl, 2);
-    fs[sl] = (p == 0) ? a.s[0] : ((p == 1) ? a.s[1] : a.s[2]);
-  }
-  fold<T>(smem, acc, nslot, fs, fb);
-
   // RoPE + split.  Groups alternate first half / second half of a head, so
   // block b (first half) pairs with block b + cw in the same lane.  Per
   // m-block the lane first fetches the cos / sin of its four rows (cw
@@ -924,6 +818,257 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
         gstore<T, cw>(dst + half, y2, cw, a.vecO);
       }
     }
+  }
+}
+
+template <class T, int LG, bool FAST, int NS>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
+  __shared__ __align__(16) char smem[kGemmLds];
+  const WaveId q = wave_id();
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const int n0 = cb * kBN;
+  const int O = a.off[3];
+  const T* X = static_cast<const T*>(a.X);
+
+  // Projections overlapping this tile -> fold / side slots.  The projections
+  // are contiguous column ranges, so the tile overlaps a contiguous run of
+  // them: slot sl holds projection pfirst + sl, sl < nslot (plain arithmetic,
+  // no runtime-indexed array, which would live in scratch memory).
+  const int hi = min(n0 + kBN, O);
+  const int ov0 = (a.off[0] < hi && a.off[1] > n0) ? 1 : 0;
+  const int ov1 = (a.off[1] < hi && a.off[2] > n0) ? 1 : 0;
+  const int ov2 = (a.off[2] < hi && a.off[3] > n0) ? 1 : 0;
+  const int nslot = ov0 + ov1 + ov2;
+  const int pfirst = ov0 ? 0 : (ov1 ? 1 : 2);
+  auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
+  auto slot_of = [&](int p) { return p - pfirst; };
+
+  auto brow_of = [&](int R) -> const T* {
+    const int o = n0 + lds_row_col(LG, R);
+    if (o >= O) return nullptr;
+    const int p = proj_of(o);
+    return static_cast<const T*>(a.W[p]) + (long)(o - a.off[p]) * a.h;
+  };
+  auto side_base = [&](int sl) -> const T* {        // side block sl: adapter of projection pfirst + sl
+    if (sl >= nslot) return nullptr;
+    const int pj = pfirst + sl;
+    return static_cast<const T*>(pj == 0 ? a.A[0] : (pj == 1 ? a.A[1] : a.A[2]));
+  };
+  const T* afall = static_cast<const T*>(pfirst == 0 ? a.A[0] : (pfirst == 1 ? a.A[1] : a.A[2]));
+
+  f32x4 acc[kMB][8];
+  f32x4 sacc[NS][kMB];
+  zero_acc(acc);
+  zero_side(sacc);
+  if constexpr (FAST && LG == 1) {
+    // head_dim 128: the per-lane row pointers fit in registers through the loop.
+    NKPairLoader<NS> ld;
+    ld.init_a(X, a.h, a.N, m0);
+    ld.bfallback = static_cast<const T*>(a.W[0]);
+    ld.smask = (1u << nslot) - 1u;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) ld.brow[it] = brow_of(ld.row_of(it));
+    ld.srow = afall;
+    const int sr = ld.side_row();              // side row: slot sr/16, rank sr%16
+    if (sr >= 0) ld.srow = ld.side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
+    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
+  } else if constexpr (FAST) {
+    // head_dim 64: the row pointers are derived inside the loop.
+    QKVRowLoader<NS, LG> ld;
+    ld.X = X;
+    ld.W0 = static_cast<const T*>(a.W[0]);
+    ld.W1 = static_cast<const T*>(a.W[1]);
+    ld.W2 = static_cast<const T*>(a.W[2]);
+    ld.S0 = side_base(0);
+    ld.S1 = side_base(1);
+    ld.S2 = side_base(2);
+    ld.afall = afall;
+    ld.N = a.N; ld.m0 = m0; ld.h = a.h; ld.n0 = n0; ld.r = a.r;
+    ld.off1 = a.off[1]; ld.off2 = a.off[2]; ld.off3 = a.off[3];
+    ld.smask = (1u << nslot) - 1u;
+    kloop2<NS>(smem, a.h / 64, ld, acc, sacc);
+  } else {
+    NKLoader<T, RowsA<T>, NS> ld;
+    ld.a.init(X, nullptr, a.h, 0, a.h, a.N, m0, a.vecA);
+    ld.bfallback = static_cast<const T*>(a.W[0]);
+    ld.K = a.h;
+    ld.vecB = a.vecW;
+    ld.vecS = a.vecS;
+    ld.smask = (1u << nslot) - 1u;
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) ld.brow[qq] = brow_of(ld.row_of(qq));
+    ld.srow = nullptr;
+    const int sr = ld.side_row();
+    if (sr >= 0) ld.srow = decltype(ld)::side_ptr(side_base(sr >> 4), sr & 15, a.r, a.h, afall);
+    kloop<T, NS>(smem, (a.h + ET<T>::BK - 1) / ET<T>::BK, ld, acc, sacc);
+  }
+  side_reduce<T, NS>(smem, sacc);
+  // A fresh (opaque) wave id for everything after the K-loop: the one above
+  // dies with the loader set-up instead of staying live through the loop.
+  const WaveId qe = wave_id();
+
+  // T_p is saved by the tile holding projection p's first column.
+  if (qe.tid < kBM) {
+    const float* Ts = ts_ptr(smem);
+    const long row = m0 + qe.tid;
+    for (int sl = 0; sl < nslot; ++sl) {
+      const int p = pfirst + sl;
+      if (a.off[p] >= n0 && a.off[p] < n0 + kBN && row < a.N)
+        for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, qe.tid, t)];
+    }
+  }
+
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const int o = n0 + lds_row_col(LG, R);
+    if (o >= O) return;
+    const int p = proj_of(o);
+    if (slot_of(p) != slot) return;
+    const T* src = static_cast<const T*>(a.B[p]) + (long)(o - a.off[p]) * a.r;
+    load_rank<T, ET<T>::VEC>(src, 1, t0, a.r, v);
+  };
+  float fs[kMaxSide];
+#pragma unroll
+  for (int sl = 0; sl < kMaxSide; ++sl) {
+    const int p = min(pfirst + sl, 2);
+    fs[sl] = (p == 0) ? a.s[0] : ((p == 1) ? a.s[1] : a.s[2]);
+  }
+  fold<T>(smem, acc, nslot, fs, fb);
+
+  qkv_rope_store<T, LG>(a, acc, m0, n0, qe);
+}
+
+// B rows of a head_dim-128 QKV tile inside one projection p for
+// nk_kloop_pp (columns in perm_col(1, ..) order): block wl + 4 it holds tile
+// column 128 (it / 4) + 64 ((it / 2) % 2) + 2 (it % 2) + 4 (x % 16) + x / 16
+// with x = 8 wl + L / 8: one lane offset.
+struct QkvPP {
+  const bf16* W0; long h;
+  int off[2];
+  __device__ __forceinline__ QkvPP(const bf16* Wp, long hd, long c0, int wl, int L) {
+    W0 = Wp + c0 * hd;
+    h = hd;
+    const int x = 8 * wl + (L >> 3);
+    off[0] = off[1] = (4 * (x & 15) + (x >> 4)) * (int)hd + direct2_chunk(L) * 8;
+  }
+  __device__ __forceinline__ const bf16* base(int it) const {
+    return W0 + (128 * (it >> 2) + 64 * ((it >> 1) & 1) + 2 * (it & 1)) * h;
+  }
+  __device__ __forceinline__ static int sel(int) { return 0; }
+};
+
+// head_dim 128, bf16 fast path, as runs of column tiles (k_gateup_run's
+// layout and LDS), for calls whose every run overlaps at most two
+// projections: the run's first tile computes T_p of those projections in its
+// K-loop and builds the fold operand (s_p T_p, bf16); later tiles inside one
+// projection take the ping-pong K-loop, others the plain loop, neither with
+// side work.  T_p is saved by the run holding projection p's first column.
+template <class T>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_run(QKVFwdArgs a) {
+  static_assert(sizeof(T) == 2, "the run kernel is bf16");
+  constexpr int LG = 1;
+  __shared__ __align__(16) char smem[kRunLds];
+  int rb, cb0, cb1;
+  run_coords(a.nruns, a.RPB, a.L, a.NC, rb, cb0, cb1);
+  const long m0 = (long)rb * kBM;
+  const int O = a.off[3];
+  const bf16* X = static_cast<const bf16*>(a.X);
+  char* FA = smem + kRunFAOff;
+  const int nkt = a.h / 64;
+  auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
+  auto wp = [&](int p) { return static_cast<const bf16*>(p == 0 ? a.W[0] : (p == 1 ? a.W[1] : a.W[2])); };
+  // Projections overlapping the run's columns: slots 0 .. rns - 1 hold
+  // projection rpf + slot.
+  const int lo = cb0 * kBN, hi = min(cb1 * kBN, O);
+  const int ov0 = (a.off[0] < hi && a.off[1] > lo) ? 1 : 0;
+  const int ov1 = (a.off[1] < hi && a.off[2] > lo) ? 1 : 0;
+  const int ov2 = (a.off[2] < hi && a.off[3] > lo) ? 1 : 0;
+  const int rns = ov0 + ov1 + ov2;
+  const int rpf = ov0 ? 0 : (ov1 ? 1 : 2);
+
+  // The kloop2 loader of the tile at n0 (side rows when smask != 0).
+  auto make_ld = [&](int n0, unsigned smask) {
+    NKPairLoader<2> ld;
+    ld.init_a(X, a.h, a.N, m0);
+    ld.bfallback = wp(0);
+    ld.smask = smask;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int o = n0 + lds_row_col(LG, ld.row_of(it));
+      const int p = proj_of(min(o, O - 1));
+      ld.brow[it] = (o < O) ? wp(p) + (long)(o - a.off[p]) * a.h : nullptr;
+    }
+    const bf16* afall = static_cast<const bf16*>(rpf == 0 ? a.A[0] : (rpf == 1 ? a.A[1] : a.A[2]));
+    ld.srow = afall;
+    const int sr = ld.side_row();              // side row: slot sr / 16, rank sr % 16
+    if (sr >= 0) {
+      const int sl = sr >> 4, pj = rpf + sl;
+      const bf16* base = (sl < rns) ? static_cast<const bf16*>(pj == 0 ? a.A[0] : (pj == 1 ? a.A[1] : a.A[2]))
+                                    : nullptr;
+      ld.srow = ld.side_ptr(base, sr & 15, a.r, a.h, afall);
+    }
+    return ld;
+  };
+
+  // Fold with the run's operand, then RoPE, split and stores.
+  auto finish = [&](int n0, f32x4 (&acc)[kMB][8]) {
+    const WaveId qe = wave_id_opaque();
+    auto fb = [&](int R, int slot, int t0, float* v) {
+      const int o = n0 + lds_row_col(LG, R);
+      if (o >= O) return;
+      const int p = proj_of(o);
+      if (p - rpf != slot) return;
+      const bf16* src = static_cast<const bf16*>(p == 0 ? a.B[0] : (p == 1 ? a.B[1] : a.B[2])) +
+                        (long)(o - a.off[p]) * a.r;
+      load_rank<bf16, 8>(src, 1, t0, a.r, v);
+    };
+    fold_run(FA, smem + kRunFBOff, acc, fb);
+    qkv_rope_store<bf16, LG>(a, acc, m0, n0, qe);
+  };
+
+  {
+    // First tile: the run's T_p ride the K-loop.
+    const int n0 = cb0 * kBN;
+    f32x4 acc[kMB][8];
+    f32x4 sacc[2][kMB];
+    zero_acc(acc);
+    zero_side(sacc);
+    {
+      const NKPairLoader<2> ld = make_ld(n0, (1u << rns) - 1u);
+      kloop2<2>(smem, nkt, ld, acc, sacc, 0, false);
+    }
+    const WaveId q = wave_id_opaque();
+    side_reduce<bf16, 2>(smem + kRunTsOff, sacc);
+    const float* Ts = ts_ptr(smem + kRunTsOff);
+    if (q.tid < kBM) {
+      const long row = m0 + q.tid;
+      for (int sl = 0; sl < rns; ++sl) {
+        const int p = rpf + sl;
+        if (a.off[p] >= lo && a.off[p] < hi && row < a.N)
+          for (int t = 0; t < a.r; ++t) a.T[p][row * a.r + t] = Ts[ts_idx(sl, q.tid, t)];
+      }
+    }
+    const float fs[kMaxSide] = {rpf == 0 ? a.s[0] : (rpf == 1 ? a.s[1] : a.s[2]),
+                                rpf == 0 ? a.s[1] : a.s[2], 0.f};
+    build_fold_a(FA, Ts, rns, fs);
+    finish(n0, acc);
+  }
+  for (int cb = cb0 + 1; cb < cb1; ++cb) {
+    const int n0 = cb * kBN;
+    f32x4 acc[kMB][8];
+    zero_acc(acc);
+    const int p = proj_of(n0);
+    if (n0 + kBN <= a.off[p + 1]) {
+      const WaveId qo = wave_id_opaque();
+      const QkvPP bp(wp(p), a.h, n0 - a.off[p], __builtin_amdgcn_readfirstlane(qo.w) & 3, qo.lane);
+      nk_kloop_pp(smem, nkt, X, a.h, a.N, m0, bp, acc);
+    } else {
+      const NKPairLoader<2> ld = make_ld(n0, 0u);
+      f32x4 snone[1][kMB];
+      kloop2<0>(smem, nkt, ld, acc, snone, 0, false);
+    }
+    finish(n0, acc);
   }
 }
 

@@ -26,6 +26,7 @@ namespace lora {
 // compiled with the default instruction scheduling).
 hipError_t launch_mlp_dx_split_bf16(const MlpDxArgs& a, hipStream_t st);
 hipError_t launch_linear_run_bf16(const LinearArgs& a, hipStream_t st);
+hipError_t launch_qkv_run_bf16(const QKVFwdArgs& a, hipStream_t st);
 template <class T>
 hipError_t launch_linear_fwd(bool fast, const LinearArgs& a, dim3 grid, hipStream_t st);
 template <class T>
@@ -671,6 +672,24 @@ int qkv_fwd_impl(const lora_qkv_desc_t& d, const void* X, const lora_proj_t* con
     for (int p = 0; p < 3; ++p)
       if (a.off[p] < std::min((cb + 1) * kBN, a.off[3]) && a.off[p + 1] > cb * kBN) ++c;
     ns = std::max(ns, c);
+  }
+  if constexpr (sizeof(T) == 2) {
+    // Runs of column tiles (head_dim 128, more tiles than CUs, every run
+    // over at most two projections).
+    run_layout(a.R, a.NC, a.L, a.RPB, a.nruns);
+    bool runs = fast && d.head_dim == 128 && a.L > 1;
+    for (int u = 0; runs && u < a.RPB; ++u) {
+      const int lo = u * a.L * kBN, hi = std::min((u + 1) * a.L * kBN, a.off[3]);
+      int c = 0;
+      for (int p = 0; p < 3; ++p)
+        if (a.off[p] < hi && a.off[p + 1] > lo) ++c;
+      runs = c <= 2;
+    }
+    if (runs) {
+      rc = launch_call(3, st, [&]() { return launch_qkv_run_bf16(a, st); });
+      if (rc) return rc;
+      return ok();
+    }
   }
   const dim3 grid(a.R * a.NC);
   rc = launch_call(3, st, [&]() { return launch_qkv_fwd<T>(fast, d.head_dim, ns, a, grid, st); });

@@ -76,6 +76,11 @@ QKV_CASES = [
     # v 256 columns) and with q, k and v all in one 256-column tile
     S.QKVConfig("qkv_bf16_d64_one_proj_per_tile", 2, 130, 128, 8, 4, 64, 16, 2.0, 1.0e4, "bf16"),
     S.QKVConfig("qkv_bf16_d64_three_proj_tile", 1, 300, 256, 2, 1, 64, 8, 2.0, 1.0e6, "bf16", bias=True),
+    # head_dim 128 with more tiles than CUs (24 x 11): runs of two column
+    # tiles, a later tile over q and k (plain loop), a later tile inside v
+    # (ping-pong loop), a last run of one 128-wide tile, a ragged row block
+    S.QKVConfig("qkv_bf16_d128_runs_ragged", 2, 3022, 128, 15, 3, 128, 16, 2.0, 1.0e4, "bf16", bias=True),
+    S.QKVConfig("qkv_bf16_d128_runs_norm", 2, 3022, 128, 15, 3, 128, 8, 2.0, 1.0e6, "bf16", qk_norm=True),
 ]
 
 

@@ -204,7 +204,8 @@ def test_determinism():
     mlp = {c.name: c for c in gc.MLP_CASES}
     lin = {c.name: c for c in gc.LINEAR_CASES}
     for cfg in (gc.MLP_CASES[1], gc.QKV_CASES[0], gc.LINEAR_CASES[0], mlp["mlp_bf16_splitk_cross"],
-                mlp["mlp_bf16_dx_runs_ragged"], lin["linear_bf16_splitk_uneven"], lin["linear_bf16_runs_ragged"]):
+                mlp["mlp_bf16_dx_runs_ragged"], lin["linear_bf16_splitk_uneven"], lin["linear_bf16_runs_ragged"],
+                [c for c in gc.QKV_CASES if c.name == "qkv_bf16_d128_runs_ragged"][0]):
         if isinstance(cfg, S.MLPConfig):
             t = S.mlp_inputs(cfg, 3)
             a, b = gc.run_mlp_gpu(cfg, t), gc.run_mlp_gpu(cfg, t)
