@@ -1137,6 +1137,7 @@ struct MlpDxArgs {
   int R, NC;
   SplitK sk;                      // fast path only; sk.S == 1: no split
   int L, RPB, nruns;              // run kernel: run length, runs per row block, runs
+  const float* dT;                // k_mlp_dx_pp: [2][N][16] dT_g, dT_u (summed k_mlp_dt partials)
 };
 
 // SPLIT (fast path only): the K range is split over a.sk.S workgroups per
@@ -1351,6 +1352,146 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_run(MlpDxArgs a) {
     kloop2tr_pp(smem, 2 * nk0, dG, dU, ni, kr, ni, a.N, m0, h, n0, h, acc);
     finish(n0, acc);
   }
+}
+
+// dT_g = dG B_g and dT_u = dU B_u ([N][16] each) on their own: a streaming
+// pass over [dG | dU] (K = 2i in chunks of 64 columns, grid row blocks x KS
+// K splits), so that the dX GEMM needs no side product.  Each workgroup
+// keeps three chunks in flight in a ring of four LDS stages (direct loads:
+// the token rows in the GEMM's 128-byte layout, the 64 B rows of the chunk
+// as [64 k][16 t]); wave w multiplies rows 32 w .. 32 w + 31.  Partials
+// [KS][3][N][16] (slots 0, 1), summed in a fixed order by k_dt_sum.
+struct MlpDtArgs {
+  const void* dG; const void* dU;  // [N][i]
+  const void* Bg; const void* Bu;  // [i][16]
+  float* part;                     // [KS][3][N][16]
+  long N; int i, KS;
+};
+constexpr int kDtStage = kStage2A + 64 * 32;
+constexpr int kDtStages = 4;
+
+template <class T>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dt(MlpDtArgs a) {
+  static_assert(sizeof(T) == 2, "bf16, i % 64 == 0, r == 16");
+  __shared__ __align__(16) char smem[kDtStages * kDtStage];
+  const WaveId q = wave_id();
+  const int L = q.lane, w = __builtin_amdgcn_readfirstlane(q.w);
+  const long m0 = (long)blockIdx.x * kBM;
+  const int nk0 = a.i / 64;
+  int cb, ce;
+  split_range(2 * nk0, a.KS, (int)blockIdx.y, cb, ce);
+  const bf16* dG = static_cast<const bf16*>(a.dG);
+  const bf16* dU = static_cast<const bf16*>(a.dU);
+  const bf16* Bg = static_cast<const bf16*>(a.Bg);
+  const bf16* Bu = static_cast<const bf16*>(a.Bu);
+  int aoff[4];
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    long row = m0 + direct2_row(it);
+    if (row > a.N - 1) row = a.N - 1;
+    aoff[it] = (int)(row * a.i) + direct2_chunk(L) * 8;
+  }
+  const int ci = 16 * w + L;                       // B chunk (lanes < 16): k row ci / 2, half ci % 2
+  const int soff = (ci >> 1) * 16 + 8 * (ci & 1);
+  auto issue = [&](int c) {
+    char* S = smem + (c & (kDtStages - 1)) * kDtStage;
+    const bool up = c >= nk0;
+    const long k = (long)(c - (up ? nk0 : 0)) * 64;
+    const bf16* A = (up ? dU : dG) + k;
+#pragma unroll
+    for (int it = 0; it < 4; ++it) g2lds16(A + aoff[it], S + direct_blk(it) * 1024);
+    if (L < 16) g2lds16((up ? Bu : Bg) + k * 16 + soff, S + kStage2A + 256 * w);
+  };
+  f32x4 acc[2][2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) acc[sl][mb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < kDtStages - 1; ++j)
+    if (cb + j < ce) issue(cb + j);
+  for (int c = cb; c < ce; ++c) {
+    // Chunk c has landed once at most the later chunks' loads (5 per chunk
+    // and wave, retired in order) are outstanding.
+    if (c + 2 < ce) vm_wait<10>();
+    else if (c + 1 < ce) vm_wait<5>();
+    else vm_wait<0>();
+    asm volatile("s_barrier" ::: "memory");
+    // The stage refilled here was read in the previous iteration by every
+    // wave, before the barrier.
+    if (c + kDtStages - 1 < ce) issue(c + kDtStages - 1);
+    const char* S = smem + (c & (kDtStages - 1)) * kDtStage;
+    u32x4 av[2][2];
+    u32x2 lo[2], hi[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) av[ks][mb] = rd128(S + lds_off2(32 * w + 16 * mb + q.r16, ks * 4 + q.g));
+      tr_side_issue(S + kStage2A + ks * 1024, q, lo[ks], hi[ks]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) tie<0>(av[ks][mb]);
+      lgkm_tie0(lo[ks], hi[ks]);
+    }
+    const bool up = c >= nk0;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const Frag<bf16> bfr = tr_make(lo[ks], hi[ks]);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        Frag<bf16> af;
+        af.v = av[ks][mb];
+        if (up) acc[1][mb] = mma(acc[1][mb], af, bfr);
+        else acc[0][mb] = mma(acc[0][mb], af, bfr);
+      }
+    }
+  }
+  // C layout: lane (t = r16, g) holds rows 4 g + j of each m-block.
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const long row = m0 + 32 * w + 16 * mb + 4 * q.g + j;
+        if (row < a.N) a.part[(((long)blockIdx.y * 3 + sl) * a.N + row) * 16 + q.r16] = acc[sl][mb][j];
+      }
+}
+
+// Fast path without split K when dT_g, dT_u come precomputed (k_mlp_dt):
+// the ping-pong K-loop over [dG | dU] [W_g; W_u] without side work, then the
+// fold and the dX epilogue as in k_mlp_dx_bwd.
+template <class T>
+__global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_pp(MlpDxArgs a) {
+  static_assert(sizeof(T) == 2, "bf16 fast path");
+  __shared__ __align__(16) char smem[kGemmLds];
+  int rb, cb;
+  tile_coords(a.R * a.NC, a.R, a.NC, 8, rb, cb);
+  const long m0 = (long)rb * kBM;
+  const long n0 = (long)cb * kBN;
+  const long h = a.h, ni = a.i;
+  f32x4 acc[kMB][8];
+  zero_acc(acc);
+  KRow2<bf16> kr;
+  kr.W0 = static_cast<const bf16*>(a.Wg); kr.W1 = static_cast<const bf16*>(a.Wu);
+  kr.K0 = ni; kr.K1 = ni; kr.ld = h;
+  kloop2tr_pp(smem, (int)(2 * ni / 64), static_cast<const bf16*>(a.dG), static_cast<const bf16*>(a.dU), ni, kr, ni,
+              a.N, m0, h, n0, h, acc);
+  load_dT(smem, a.dT, a.N, m0, 2);
+  const bf16* Ag = static_cast<const bf16*>(a.Ag);
+  const bf16* Au = static_cast<const bf16*>(a.Au);
+  auto fb = [&](int R, int slot, int t0, float* v) {
+    const long n = n0 + R;
+    if (n >= h) return;
+    load_rank<bf16, 8>((slot == 0 ? Ag : Au) + n, h, t0, a.r, v);
+  };
+  const float fs[kMaxSide] = {a.sg, a.su, 0.f};
+  fold<bf16>(smem, acc, 2, fs, fb);
+  float* const parts[2] = {a.pA_g + (long)rb * h * 16, a.pA_u + (long)rb * h * 16};
+  dx_epilogue<bf16, 2, true, true>(smem, acc, fs, static_cast<const bf16*>(a.X), static_cast<bf16*>(a.dX), parts,
+                                   a.N, h, m0, n0, a.vecO);
 }
 
 // ===========================================================================

@@ -65,7 +65,7 @@ int ok() {
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd",  "k_linear_fwd", "k_rope_table", "k_qkv_fwd",
                         "k_bwd_prologue", "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd",
-                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd"};
+                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd", "k_mlp_dt"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -280,6 +280,7 @@ struct MlpWs {
   float *dT_part, *dT, *pA_d, *pB_g, *pB_u, *pA_g, *pA_u, *pB_d;
   SplitWs split;    // forward: down projection; backward: MLP dX
   int NCR, NCH, CPC;
+  int KS;           // backward: K splits of k_mlp_dt
   size_t bytes;
 };
 MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
@@ -299,7 +300,9 @@ MlpWs mlp_ws(const lora_mlp_desc_t& d, int pass, void* base) {
     w.split = take_split(c, bf && i % 64 == 0 && d.rank == 16, R * cdiv(h, kBN), 2 * i / 64);
     w.dG = c.take<void>(N * i * es);
     w.dU = c.take<void>(N * i * es);
-    w.dT_part = c.take<float>((size_t)w.NCR * 3 * N * 16 * 4);
+    // k_mlp_dt: about one workgroup per CU over the row blocks x K splits.
+    w.KS = (int)std::max(1L, std::min(cdiv(kCUs, std::max(1L, R)), std::max(1L, 2 * i / 64)));
+    w.dT_part = c.take<float>((size_t)std::max(w.NCR, w.KS) * 3 * N * 16 * 4);
     w.dT = c.take<float>((size_t)3 * N * 16 * 4);
     w.pA_d = c.take<float>(R * i * 16 * 4);
     w.pB_g = c.take<float>(R * i * 16 * 4);
@@ -575,9 +578,20 @@ int mlp_bwd_impl(const lora_mlp_desc_t& d, const void* dY, const void* X, const 
         if (a.sk.S > 1) {                          // set only on the bf16 fast path
           rc = launch_call(6, st, [&]() { return launch_mlp_dx_split_bf16(a, st); });
           done = true;
-        } else if (fast) {                         // runs of column tiles
-          run_layout(a.R, a.NC, a.L, a.RPB, a.nruns);
-          rc = launch(6, k_mlp_dx_run<T>, dim3(a.nruns), dim3(kGemmThreads), st, a);
+        } else if (fast) {
+          // dT_g, dT_u by a streaming pass of their own, then the dX GEMM
+          // without side work.
+          MlpDtArgs t{};
+          t.dG = w.dG; t.dU = w.dU; t.Bg = g.B; t.Bu = u.B;
+          t.part = w.dT_part;
+          t.N = N; t.i = i; t.KS = w.KS;
+          rc = launch(11, k_mlp_dt<T>, dim3(R, w.KS), dim3(kGemmThreads), st, t);
+          if (rc) return rc;
+          rc = launch(9, k_dt_sum, dim3((unsigned)cdiv(N * 4, 256), 2), dim3(256), st, (const float*)w.dT_part, w.dT,
+                      w.KS, N);
+          if (rc) return rc;
+          a.dT = w.dT;
+          rc = launch(6, k_mlp_dx_pp<T>, dim3(a.R * a.NC), dim3(kGemmThreads), st, a);
           done = true;
         }
       }
