@@ -1029,30 +1029,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_down_bwd(DownBwdArgs a) {
 // ===========================================================================
 constexpr int kParkOff = kTsBytes;
 
-// The same A operand as ts_frag4 from a built fold operand FA[m][16 s + t]
-// = bf16(scale_s Ts[s][m][t]) (64-byte rows, lds_off): the identical bf16
-// values, read back instead of recomputed.
-__device__ __forceinline__ Frag4<bf16> fa_frag4(const char* FA, int slot, const WaveId& q, int mb) {
-  const int k = 16 * slot + q.r16;
-  unsigned u[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    u[j] = *reinterpret_cast<const unsigned short*>(FA + lds_off(acc_row(q, mb, j), k >> 3) + (k & 7) * 2);
-  Frag4<bf16> f;
-  f.v = (u32x2){u[0] | (u[1] << 16), u[2] | (u[3] << 16)};
-  return f;
-}
-
 // BUFX (bf16; X rows aligned, X at most 2 GB): X rows come by raw buffer
 // loads, branch-free, so a fetch stays in flight across the previous block.
-// FA (bf16): the dA operands come from the fold operand at `fa` instead of
-// the fp32 side products.
-template <class T, int NA, bool TR, bool BUFX = false, bool FA = false>
+template <class T, int NA, bool TR, bool BUFX = false>
 __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], const float (&escale)[kMaxSide],
                                             const T* X, T* dX, float* const (&parts)[NA], long N, long h, long m0,
-                                            long n0, bool vecO, const char* fa = nullptr) {
-  static_assert(!FA || sizeof(T) == 2, "bf16 fold operand");
-  const WaveId q = FA ? wave_id_opaque() : wave_id();
+                                            long n0, bool vecO) {
+  const WaveId q = wave_id();
   const float* Ts = ts_ptr(smem);
   const long c0 = n0 + q.wn * 128 + 8 * q.r16;
   const int nvalid = (int)min(8L, h - c0);
@@ -1104,10 +1087,7 @@ __device__ __forceinline__ void dx_epilogue(char* smem, f32x4 (&acc)[kMB][8], co
     }
     Frag4<T> adT[NA];
 #pragma unroll
-    for (int o = 0; o < NA; ++o) {
-      if constexpr (FA) adT[o] = fa_frag4(fa, o, q, mb);
-      else adT[o] = ts_frag4<T>(Ts, o, escale[o], q, mb);
-    }
+    for (int o = 0; o < NA; ++o) adT[o] = ts_frag4<T>(Ts, o, escale[o], q, mb);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
       const float b[4] = {xv[0][nb], xv[1][nb], xv[2][nb], xv[3][nb]};
@@ -1136,7 +1116,6 @@ struct MlpDxArgs {
   int vecA, vecW, vecS, vecO;
   int R, NC;
   SplitK sk;                      // fast path only; sk.S == 1: no split
-  int L, RPB, nruns;              // run kernel: run length, runs per row block, runs
   const float* dT;                // k_mlp_dx_pp: [2][N][16] dT_g, dT_u (summed k_mlp_dt partials)
 };
 
@@ -1257,101 +1236,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
   float* const parts[2] = {a.pA_g + (long)rb * h * 16, a.pA_u + (long)rb * h * 16};
   dx_epilogue<T, 2, TR, FAST>(smem, acc, fs, static_cast<const T*>(a.X), static_cast<T*>(a.dX), parts, a.N, h, m0, n0,
                         a.vecO);
-}
-
-// Fast path without split K as runs of column tiles (k_gateup_run's layout):
-// the run's first tile computes dT_g, dT_u in its K-loop (as k_mlp_dx_bwd)
-// and builds the fold operand s dT (bf16) past the K-loop stages, where it
-// stays for the run; the later tiles take the ping-pong K-loop without side
-// work.  Every tile folds with that operand and forms its dA partials from
-// it (the same bf16 values k_mlp_dx_bwd computes per tile).
-constexpr int kDxRunFAOff = 2 * kStage2Tr;
-static_assert(kDxRunFAOff + kBM * kRowBytes <= kGemmLdsX, "run fold operand");
-static_assert(kRedOff + kRedBytes <= kDxRunFAOff && kParkOff + 8 * 4096 <= kDxRunFAOff, "epilogue scratch");
-
-template <class T>
-__global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_run(MlpDxArgs a) {
-  static_assert(sizeof(T) == 2, "the run kernel is bf16");
-  __shared__ __align__(16) char smem[kGemmLdsX];
-  int rb, cb0, cb1;
-  run_coords(a.nruns, a.RPB, a.L, a.NC, rb, cb0, cb1);
-  const long m0 = (long)rb * kBM;
-  const long h = a.h, ni = a.i, r = a.r;
-  const bf16* Wg = static_cast<const bf16*>(a.Wg);
-  const bf16* Wu = static_cast<const bf16*>(a.Wu);
-  const bf16* dG = static_cast<const bf16*>(a.dG);
-  const bf16* dU = static_cast<const bf16*>(a.dU);
-  const float fs[kMaxSide] = {a.sg, a.su, 0.f};
-  char* FA = smem + kDxRunFAOff;
-  const int nk0 = (int)(ni / 64);
-
-  // Fold, dX and the dA partials of the tile at column n0.
-  auto finish = [&](long n0, f32x4 (&acc)[kMB][8]) {
-    const bf16* Ag = static_cast<const bf16*>(a.Ag);
-    const bf16* Au = static_cast<const bf16*>(a.Au);
-    auto fb = [&](int R, int slot, int t0, float* v) {
-      const long n = n0 + R;
-      if (n >= h) return;
-      load_rank<bf16, 8>((slot == 0 ? Ag : Au) + n, h, t0, a.r, v);
-    };
-    fold_run(FA, smem + kFBOff, acc, fb);
-    __syncthreads();                                   // FB is read; the park area overlaps it
-    float* const parts[2] = {a.pA_g + (long)rb * h * 16, a.pA_u + (long)rb * h * 16};
-    dx_epilogue<bf16, 2, true, true, true>(smem, acc, fs, static_cast<const bf16*>(a.X), static_cast<bf16*>(a.dX),
-                                           parts, a.N, h, m0, n0, a.vecO, FA);
-  };
-
-  {
-    // First tile: dT_g, dT_u ride the K-loop (as in k_mlp_dx_bwd).
-    const long n0 = (long)cb0 * kBN;
-    f32x4 acc[kMB][8];
-    f32x4 sacc[1][kMB];
-    zero_acc(acc);
-    KNPairLoader<KRow2<bf16>, SRowLin<bf16>, 1> ld;
-    ld.krow.W0 = Wg; ld.krow.W1 = Wu; ld.krow.K0 = ni; ld.krow.K1 = ni; ld.krow.ld = h;
-    ld.srow.B = static_cast<const bf16*>(a.Bg); ld.srow.kb = 0; ld.srow.ld = r;   // phase 1: B_g rows
-    ld.init(dG, dU, ni, ni, a.N, m0, h, n0, h, r);
-    zero_side(sacc);
-    kloop2tr<1>(smem, nk0, ld, acc, sacc, 0);
-    {
-      const WaveId q = wave_id();
-      float* fl = reinterpret_cast<float*>(smem + kFlushOff);
-      if (q.wn == 0)
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] = sacc[0][mb][j];
-      __syncthreads();
-      if (q.wn == 1)
-#pragma unroll
-        for (int mb = 0; mb < kMB; ++mb)
-#pragma unroll
-          for (int j = 0; j < 4; ++j) fl[acc_row(q, mb, j) * kSlot + q.r16] += sacc[0][mb][j];
-    }
-    zero_side(sacc);
-    ld.srow.B = static_cast<const bf16*>(a.Bu);        // phase 2: B_u rows
-    ld.srow.kb = ni;
-    kloop2tr<1>(smem, 2 * nk0, ld, acc, sacc, nk0);
-    side_reduce<bf16, 1>(smem, sacc, 1);               // dT_u -> slot 1
-    {
-      float* Ts = ts_ptr(smem);
-      const float* fl = reinterpret_cast<const float*>(smem + kFlushOff);
-      for (int e = threadIdx.x; e < kBM * kSlot; e += kGemmThreads) Ts[e] = fl[e];   // dT_g -> slot 0
-      __syncthreads();
-      build_fold_a(FA, Ts, 2, fs);                     // over the flush slot, now copied
-    }
-    finish(n0, acc);
-  }
-  KRow2<bf16> kr;
-  kr.W0 = Wg; kr.W1 = Wu; kr.K0 = ni; kr.K1 = ni; kr.ld = h;
-  for (int cb = cb0 + 1; cb < cb1; ++cb) {
-    const long n0 = (long)cb * kBN;
-    f32x4 acc[kMB][8];
-    zero_acc(acc);
-    __syncthreads();                                   // the last tile's epilogue scratch is stage 0
-    kloop2tr_pp(smem, 2 * nk0, dG, dU, ni, kr, ni, a.N, m0, h, n0, h, acc);
-    finish(n0, acc);
-  }
 }
 
 // dT_g = dG B_g and dT_u = dU B_u ([N][16] each) on their own: a streaming
