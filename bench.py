@@ -47,7 +47,8 @@ def kernel_flops(qkv, mlp):
         "k_linear_fwd": 2 * N * i * h + 2 * N * i * r + 2 * N * r * h,
         "k_qkv_fwd": 2 * Nq * hq * O + 6 * Nq * hq * rq + 2 * Nq * rq * O,
         "k_down_bwd": 2 * N * h * i + 8 * N * r * i,
-        "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h,
+        "k_mlp_dt": 4 * N * i * r,
+        "k_mlp_dx_bwd": 4 * N * i * h + 8 * N * r * h,
         "k_proj_dx_bwd": 2 * Nq * O * hq + 12 * Nq * rq * hq,
     }
 
@@ -197,7 +198,8 @@ def mlp_kernel_flops(cfg):
     return {"k_gateup_fwd": 4 * N * h * i + 4 * N * h * r + 4 * N * r * i,
             "k_linear_fwd": 2 * N * i * h + 2 * N * i * r + 2 * N * r * h,
             "k_down_bwd": 2 * N * h * i + 8 * N * r * i,
-            "k_mlp_dx_bwd": 4 * N * i * h + 4 * N * i * r + 8 * N * r * h}
+            "k_mlp_dt": 4 * N * i * r,
+            "k_mlp_dx_bwd": 4 * N * i * h + 8 * N * r * h}
 
 
 def bench_mlp(cfg, steps: int, warmup: int, flush=None):
