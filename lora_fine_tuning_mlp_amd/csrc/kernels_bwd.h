@@ -99,30 +99,27 @@ constexpr int kProPc = 32768;                   // tiles [BK cols][BK tokens] x 
 constexpr int kProBt = 65536;                   // [16 t][BK]       B_p^T chunk
 constexpr int kProTT = 65536 + 2048;            // per adapter tiles [16 t][BK tokens] x (256/BK)
 constexpr int kProLds = kProTT + 3 * 16384;     // 116736
-// BUF layout (no column-major copy; bf16 T^T tiles of 8 KB): 58 KB.
+// Layout of the buffer-load prologue (no column-major copy; bf16 T^T tiles of
+// 8 KB): 58 KB.
 constexpr int kProBtBuf = 32768;
 constexpr int kProTTBuf = kProBtBuf + 2048;
 constexpr int kProLdsBuf = kProTTBuf + 3 * 8192;   // 59392
 
-// BUF (bf16, every source under 4 GB, 16-byte aligned rows): the tile loads
-// are raw buffer loads, which read zero past the end instead of needing a
-// branch, so all of a thread's loads go out together, and the next chunk's
-// are issued before the current chunk is processed.
-template <class T, bool BUF = false>
+// Register-staged prologue (fp32, or bf16 calls the buffer-load version
+// below cannot take).
+template <class T>
 __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
   constexpr int VEC = PT<T>::VEC, BK = PT<T>::BK, KSUB = PT<T>::KSUB, HW = BK / 2;
   constexpr int NKB = kBM / BK;                 // token tiles per 256 rows
   constexpr int TTB = 16 * kPRowBytes * NKB;     // bytes of one adapter's T^T
-  static_assert(!BUF || sizeof(T) == 2, "buffer-load prologue is bf16");
-  static_assert(!BUF || TTB == 8192, "bf16 T^T tiles");
-  __shared__ __align__(16) char smem[BUF ? kProLdsBuf : kProLds];
+  __shared__ __align__(16) char smem[kProLds];
   const WaveId q = wave_id();
   const int rb = blockIdx.x, cr = blockIdx.y;
   const long m0 = (long)rb * kBM;
   char* Pr = smem + kProPr;
-  char* Pc = smem + kProPc;                      // (not used with BUF)
-  char* Bt = smem + (BUF ? kProBtBuf : kProBt);
-  char* TT = smem + (BUF ? kProTTBuf : kProTT);
+  char* Pc = smem + kProPc;
+  char* Bt = smem + kProBt;
+  char* TT = smem + kProTT;
 
   // (s_p T_p)^T for this row block, once: TT_p tile kb, row t, element row % BK.
   for (int p = 0; p < a.nadp; ++p) {
@@ -269,215 +266,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
     __syncthreads();
   };
 
-  // The same for BUF (bf16) without the column-major copy: B rows go to LDS
-  // as loaded ([64 kk][16 t], 32-byte rows) and both MFMA operands that need
-  // a transposed view (B_p^T for dT, P^T for dB) are read with
-  // ds_read_b64_tr_b16, which hands a lane four rows of one column.
-  auto process_tr = [&](const CMap& m, const u32x4 (&lo)[4], const u32x4 (&hi)[4], const u32x4& bv) {
-    const int p = m.p;
+  for (int ch = ch_beg; ch < ch_end; ++ch) {
+    const CMap m = cmap(ch);
+    const int p = m.p, hd = m.hd;
+    // 1. P tile: 4 rows x (chunk pc, chunk pc+4) per thread.
+    u32x4 lo[4], hi[4];
+    const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4*>(Pr + p_off(4 * rg4 + i, pc)) = lo[i];
-      *reinterpret_cast<u32x4*>(Pr + p_off(4 * rg4 + i, pc + 4)) = hi[i];
-    }
-    if (q.tid < 128) *reinterpret_cast<u32x4*>(Bt + bkk * 32 + bt0 * 2) = bv;
-    __syncthreads();
-    const int s = q.r16, g = q.g;
-    // 4. dT_p[rows][t] += P[rows][chunk] . B_p[chunk][t]: B operand lane s:
-    // t = s, K slots kk = 32 ks + 8 g .. +7.
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kr = ks * 32 + 8 * g + (s >> 2);
-      u32x2 b0 = tr16(lds_addr(Bt + kr * 32 + 8 * (s & 3)));
-      u32x2 b1 = tr16(lds_addr(Bt + (kr + 4) * 32 + 8 * (s & 3)));
-      lgkm_tie0(b0, b1);
-      PFrag<bf16> bf;
-      bf.v = (u32x4){b0.x, b0.y, b1.x, b1.y};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const PFrag<bf16> af = p_frag<bf16>(Pr, (4 * q.w + i) * 16 + q.r16, ks, q.g);
-        if (p == 0) dT[0][i] = p_mma(dT[0][i], af, bf);
-        else if (p == 1) dT[1][i] = p_mma(dT[1][i], af, bf);
-        else dT[2][i] = p_mma(dT[2][i], af, bf);
-      }
-    }
-    // 5. dB_p[col][t] = P[rows][col]^T . (s_p T_p)[rows][t]: wave w takes
-    // columns 16 w .. +15; A operand lane s: column 16 w + s, K slots rows
-    // 64 kb + 32 ks + 8 g .. +7.
-    {
-      f32x4 db = (f32x4){0.f, 0.f, 0.f, 0.f};
-      const int col = q.w * 16 + 4 * (s & 3);
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int row = kb * 64 + ks * 32 + 8 * g + (s >> 2);
-          u32x2 a0 = tr16(lds_addr(Pr + p_off(row, col >> 3) + (col & 7) * 2));
-          u32x2 a1 = tr16(lds_addr(Pr + p_off(row + 4, col >> 3) + (col & 7) * 2));
-          lgkm_tie0(a0, a1);
-          PFrag<bf16> af;
-          af.v = (u32x4){a0.x, a0.y, a1.x, a1.y};
-          const PFrag<bf16> bf = p_frag<bf16>(TT + p * TTB + kb * (16 * kPRowBytes), q.r16, ks, q.g);
-          db = p_mma(db, af, bf);
-        }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int kk = q.w * 16 + 4 * q.g + j;
-        const long c = (kk < HW) ? m.base_lo + kk : m.base_hi + (kk - HW);
-        if (c < a.O) a.dB_part[((long)rb * a.O + c) * 16 + q.r16] = db[j];
-      }
-    }
-    __syncthreads();
-  };
-
-  if constexpr (BUF) {
-    // Raw 16-byte chunks of a chunk's rows (plus, for rotated q/k chunks,
-    // the cos / sin of the row's position at its 8 columns).
-    struct Raw {
-      u32x4 xl[4], xh[4];
-      f32x4 c[4][2], sn[4][2];
-      u32x4 bv;
-    };
-    auto fetch = [&](const CMap& m, Raw& w) {
-      const int p = m.p;
-      const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
-      {
-        // B_p rows [off_p+1 - off_p][r]: zero past the adapter's columns or r.
-        const long col = (bkk < HW) ? m.base_lo + bkk : m.base_hi + (bkk - HW);
-        const long rows = (long)a.off[p + 1] - a.off[p];
-        const __amdgpu_buffer_rsrc_t rb2 = buf_rsrc(a.Bp[p], (unsigned)(rows * a.r * 2));
-        const bool ok = q.tid < 128 && col < a.off[p + 1] && bt0 < a.r;
-        const unsigned off = ok ? (unsigned)(((col - a.off[p]) * a.r + bt0) * 2) : kBufOut;
-        w.bv = buf_load16(rb2, off);
-      }
+      const long n = m0 + 4 * rg4 + i;
+      if (n >= a.N) { lo[i] = zero4(); hi[i] = zero4(); continue; }
       if (a.qkv) {
-        const unsigned bytes = (unsigned)(a.N * a.nh[p] * a.d * 2);
-        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.src[p], bytes);
-        const int jlo = (int)(clo - a.off[p] - (long)m.hd * a.d);   // index within the head, < d/2
+        const int s = (int)(n % a.S);
+        const long b = n / a.S;
+        const int jlo = (int)(clo - a.off[p] - (long)hd * a.d);   // index within the head, < d/2
+        const T* src = static_cast<const T*>(a.src[p]) + ((b * a.nh[p] + hd) * a.S + s) * (long)a.d;
+        const u32x4 xl = gload<T>(src, jlo, a.d, a.vecP);
+        const u32x4 xh = gload<T>(src, jlo + a.d / 2, a.d, a.vecP);
+        if (p < 2) {
+          float vl[VEC], vh[VEC], yl[VEC], yh[VEC];
+          unpack(xl, vl);
+          unpack(xh, vh);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long n = m0 + 4 * rg4 + i;
-          const long nn = n < a.N ? n : 0;
-          const int s = (int)(nn % a.S);
-          const long b = nn / a.S;
-          const long e0 = ((b * a.nh[p] + m.hd) * a.S + s) * (long)a.d + jlo;
-          const unsigned off = n < a.N ? (unsigned)(e0 * 2) : kBufOut;
-          w.xl[i] = buf_load16(rs, off);
-          w.xh[i] = buf_load16(rs, off + (unsigned)a.d);
-          if (p < 2) {
-            const f32x4* cs4 = reinterpret_cast<const f32x4*>(a.cs + (long)s * (a.d / 2) + jlo);
-            const f32x4* sn4 = reinterpret_cast<const f32x4*>(a.sn + (long)s * (a.d / 2) + jlo);
-            w.c[i][0] = cs4[0];
-            w.c[i][1] = cs4[1];
-            w.sn[i][0] = sn4[0];
-            w.sn[i][1] = sn4[1];
+          for (int e = 0; e < VEC; ++e) {
+            const float c = a.cs[(long)s * (a.d / 2) + jlo + e], sn = a.sn[(long)s * (a.d / 2) + jlo + e];
+            yl[e] = vl[e] * c + vh[e] * sn;      // R^T: rotate by -angle
+            yh[e] = vh[e] * c - vl[e] * sn;
           }
-        }
-      } else {
-        const unsigned bytes = (unsigned)(a.N * a.O * 2);
-        const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.P, bytes);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long n = m0 + 4 * rg4 + i;
-          const bool live = n < a.N;
-          const unsigned ol = (live && clo < a.O) ? (unsigned)((n * a.O + clo) * 2) : kBufOut;
-          const unsigned oh = (live && chi < a.O) ? (unsigned)((n * a.O + chi) * 2) : kBufOut;
-          w.xl[i] = buf_load16(rs, ol);
-          w.xh[i] = buf_load16(rs, oh);
-        }
-      }
-    };
-    // The thread's rows of chunk ch are taken out of nx (rotated, and stored
-    // to dP, for q/k chunks) before chunk ch + 1 is fetched into it, so the
-    // fetch is in flight while chunk ch is processed.
-    Raw nx;
-    if (ch_beg < ch_end) fetch(cmap(ch_beg), nx);
-    for (int ch = ch_beg; ch < ch_end; ++ch) {
-      const CMap m = cmap(ch);
-      u32x4 lo[4], hi[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        lo[i] = nx.xl[i];
-        hi[i] = nx.xh[i];
-      }
-      if (a.qkv) {
-        if (m.p < 2) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            float vl[VEC], vh[VEC], yl[VEC], yh[VEC];
-            unpack(nx.xl[i], vl);
-            unpack(nx.xh[i], vh);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const float c = nx.c[i][e >> 2][e & 3], sv = nx.sn[i][e >> 2][e & 3];
-              yl[e] = vl[e] * c + vh[e] * sv;      // R^T: rotate by -angle
-              yh[e] = vh[e] * c - vl[e] * sv;
-            }
-            lo[i] = pack(yl);
-            hi[i] = pack(yh);
-          }
-        }
-        const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const long n = m0 + 4 * rg4 + i;
-          if (n < a.N) {
-            T* dp = static_cast<T*>(a.dP) + n * a.O;
-            *reinterpret_cast<u32x4*>(dp + clo) = lo[i];
-            *reinterpret_cast<u32x4*>(dp + chi) = hi[i];
-          }
-        }
-      }
-      const u32x4 bv = nx.bv;
-      if (ch + 1 < ch_end) fetch(cmap(ch + 1), nx);
-      process_tr(m, lo, hi, bv);
-    }
-  } else {
-    for (int ch = ch_beg; ch < ch_end; ++ch) {
-      const CMap m = cmap(ch);
-      const int p = m.p, hd = m.hd;
-      // 1. P tile: 4 rows x (chunk pc, chunk pc+4) per thread.
-      u32x4 lo[4], hi[4];
-      const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long n = m0 + 4 * rg4 + i;
-        if (n >= a.N) { lo[i] = zero4(); hi[i] = zero4(); continue; }
-        if (a.qkv) {
-          const int s = (int)(n % a.S);
-          const long b = n / a.S;
-          const int jlo = (int)(clo - a.off[p] - (long)hd * a.d);   // index within the head, < d/2
-          const T* src = static_cast<const T*>(a.src[p]) + ((b * a.nh[p] + hd) * a.S + s) * (long)a.d;
-          const u32x4 xl = gload<T>(src, jlo, a.d, a.vecP);
-          const u32x4 xh = gload<T>(src, jlo + a.d / 2, a.d, a.vecP);
-          if (p < 2) {
-            float vl[VEC], vh[VEC], yl[VEC], yh[VEC];
-            unpack(xl, vl);
-            unpack(xh, vh);
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) {
-              const float c = a.cs[(long)s * (a.d / 2) + jlo + e], sn = a.sn[(long)s * (a.d / 2) + jlo + e];
-              yl[e] = vl[e] * c + vh[e] * sn;      // R^T: rotate by -angle
-              yh[e] = vh[e] * c - vl[e] * sn;
-            }
-            lo[i] = pack(yl);
-            hi[i] = pack(yh);
-          } else {
-            lo[i] = xl;
-            hi[i] = xh;
-          }
-          T* dp = static_cast<T*>(a.dP) + n * a.O;
-          *reinterpret_cast<u32x4*>(dp + clo) = lo[i];
-          *reinterpret_cast<u32x4*>(dp + chi) = hi[i];
+          lo[i] = pack(yl);
+          hi[i] = pack(yh);
         } else {
-          const T* row = static_cast<const T*>(a.P) + n * a.O;
-          lo[i] = gload<T>(row, clo, a.O, a.vecP);
-          hi[i] = gload<T>(row, chi, a.O, a.vecP);
+          lo[i] = xl;
+          hi[i] = xh;
         }
+        T* dp = static_cast<T*>(a.dP) + n * a.O;
+        *reinterpret_cast<u32x4*>(dp + clo) = lo[i];
+        *reinterpret_cast<u32x4*>(dp + chi) = hi[i];
+      } else {
+        const T* row = static_cast<const T*>(a.P) + n * a.O;
+        lo[i] = gload<T>(row, clo, a.O, a.vecP);
+        hi[i] = gload<T>(row, chi, a.O, a.vecP);
       }
-      const u32x4 bv = q.tid < 128 ? bload(m) : zero4();
-      process(m, lo, hi, bv);
     }
+    const u32x4 bv = q.tid < 128 ? bload(m) : zero4();
+    process(m, lo, hi, bv);
   }
 
   // dT partial of this column range for the call's adapters (zeros for
@@ -492,6 +324,263 @@ __global__ __launch_bounds__(kThreads, 1) void k_bwd_prologue(ProArgs a) {
           const long n = m0 + (4 * q.w + i) * 16 + 4 * q.g + j;
           if (n < a.N) a.dT_part[(((long)cr * 3 + p) * a.N + n) * 16 + q.r16] = a.s[p] * dT[p][i][j];
         }
+}
+
+// The bf16 buffer-load prologue with eight waves (512 threads): a thread
+// holds 2 of a chunk's 256 rows (16-byte pieces pc and pc + 4 of each), so
+// twice as many waves keep loads in flight and each does half the per-row
+// work; the rows' (sequence, position) split is computed once.  After the
+// chunk is in LDS, waves 0-3 form dT (4 m-blocks each) while waves 4-7 form
+// the dB partial (one 16-column block each), both with the transpose reads
+// of the four-wave version.  Same arguments, grid and results as
+// k_bwd_prologue<bf16, true>.
+template <class T>
+__global__ __launch_bounds__(512, 1) void k_bwd_prologue8(ProArgs a) {
+  static_assert(sizeof(T) == 2, "bf16");
+  constexpr int VEC = 8, BK = 64, HW = 32, NKB = kBM / BK, TTB = 8192;
+  __shared__ __align__(16) char smem[kProLdsBuf];
+  const WaveId q = wave_id();
+  const int w = __builtin_amdgcn_readfirstlane(q.w);
+  const int rb = blockIdx.x, cr = blockIdx.y;
+  const long m0 = (long)rb * kBM;
+  char* Pr = smem + kProPr;
+  char* Bt = smem + kProBtBuf;
+  char* TT = smem + kProTTBuf;
+
+  // (s_p T_p)^T for this row block, once (threads 0..255: one row each).
+  if (q.tid < kBM) {
+    for (int p = 0; p < a.nadp; ++p) {
+      const int row = q.tid;
+      const long n = m0 + row;
+      float v[16];
+      load_rank<float, 16>(a.Tp[p] + min(n, a.N - 1) * a.r, 1, 0, a.r, v);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        char* dst = TT + p * TTB + (row / BK) * (16 * kPRowBytes) + p_off(t, (row % BK) / VEC) + (row % VEC) * 2;
+        *reinterpret_cast<T*>(dst) = from_f<T>(n < a.N ? a.s[p] * v[t] : 0.f);
+      }
+    }
+  }
+
+  f32x4 dT[3][4];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dT[p][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  const int pc = q.tid & 3, rg = q.tid >> 2;    // pieces (pc, pc + 4) of rows 2 rg, 2 rg + 1
+  const int ch_beg = cr * a.CPC, ch_end = min(a.NCH, (cr + 1) * a.CPC);
+  // qkv: (batch, position) of the thread's rows.
+  long rbat[2];
+  int rpos[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const long n = m0 + 2 * rg + i;
+    const long nn = (a.qkv && n < a.N) ? n : 0;
+    rpos[i] = a.qkv ? (int)(nn % a.S) : 0;
+    rbat[i] = a.qkv ? nn / a.S : 0;
+  }
+
+  struct CMap {
+    int p, hd;
+    long base_lo, base_hi;
+  };
+  auto cmap = [&](int ch) {
+    CMap m;
+    m.p = 0;
+    m.hd = 0;
+    if (a.qkv) {
+      const int cph = a.d / BK;
+      const int gh = ch / cph, qq = ch % cph;
+      m.p = (gh < a.nh[0]) ? 0 : ((gh < a.nh[0] + a.nh[1]) ? 1 : 2);
+      m.hd = gh - ((m.p == 0) ? 0 : ((m.p == 1) ? a.nh[0] : a.nh[0] + a.nh[1]));
+      m.base_lo = a.off[m.p] + (long)m.hd * a.d + qq * HW;
+      m.base_hi = m.base_lo + a.d / 2;
+    } else {
+      m.base_lo = (long)ch * BK;
+      m.base_hi = m.base_lo + HW;
+      m.p = (a.nadp > 1 && m.base_lo >= a.off[1]) ? ((a.nadp > 2 && m.base_lo >= a.off[2]) ? 2 : 1) : 0;
+    }
+    return m;
+  };
+  // B_p chunk rows: thread tid < 128 supplies ranks bt0 .. bt0+7 of row bkk.
+  const int bkk = q.tid >> 1, bt0 = (q.tid & 1) * VEC;
+
+  struct Raw {
+    u32x4 xl[2], xh[2];
+    u32x4 bv;
+  };
+  struct Rot {
+    f32x4 c[2][2], sn[2][2];
+  };
+  auto fetch = [&](const CMap& m, Raw& r) {
+    const int p = m.p;
+    {
+      const long col = (bkk < HW) ? m.base_lo + bkk : m.base_hi + (bkk - HW);
+      const long rows = (long)a.off[p + 1] - a.off[p];
+      const __amdgpu_buffer_rsrc_t rb2 = buf_rsrc(a.Bp[p], (unsigned)(rows * a.r * 2));
+      const bool ok = q.tid < 128 && col < a.off[p + 1] && bt0 < a.r;
+      r.bv = buf_load16(rb2, ok ? (unsigned)(((col - a.off[p]) * a.r + bt0) * 2) : kBufOut);
+    }
+    if (a.qkv) {
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.src[p], (unsigned)(a.N * a.nh[p] * a.d * 2));
+      const int jlo = (int)(m.base_lo + pc * VEC - a.off[p] - (long)m.hd * a.d);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const long n = m0 + 2 * rg + i;
+        const long e0 = ((rbat[i] * a.nh[p] + m.hd) * a.S + rpos[i]) * (long)a.d + jlo;
+        const unsigned off = n < a.N ? (unsigned)(e0 * 2) : kBufOut;
+        r.xl[i] = buf_load16(rs, off);
+        r.xh[i] = buf_load16(rs, off + (unsigned)a.d);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.P, (unsigned)(a.N * a.O * 2));
+      const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const long n = m0 + 2 * rg + i;
+        const bool live = n < a.N;
+        r.xl[i] = buf_load16(rs, (live && clo < a.O) ? (unsigned)((n * a.O + clo) * 2) : kBufOut);
+        r.xh[i] = buf_load16(rs, (live && chi < a.O) ? (unsigned)((n * a.O + chi) * 2) : kBufOut);
+      }
+    }
+  };
+  auto fetch_rot = [&](const CMap& m, Rot& r) {
+    if (!a.qkv || m.p >= 2) return;
+    const int jlo = (int)(m.base_lo + pc * VEC - a.off[m.p] - (long)m.hd * a.d);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const f32x4* cs4 = reinterpret_cast<const f32x4*>(a.cs + (long)rpos[i] * (a.d / 2) + jlo);
+      const f32x4* sn4 = reinterpret_cast<const f32x4*>(a.sn + (long)rpos[i] * (a.d / 2) + jlo);
+      r.c[i][0] = cs4[0];
+      r.c[i][1] = cs4[1];
+      r.sn[i][0] = sn4[0];
+      r.sn[i][1] = sn4[1];
+    }
+  };
+
+  auto process = [&](const CMap& m, const u32x4 (&lo)[2], const u32x4 (&hi)[2], const u32x4& bv) {
+    const int p = m.p;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      *reinterpret_cast<u32x4*>(Pr + p_off(2 * rg + i, pc)) = lo[i];
+      *reinterpret_cast<u32x4*>(Pr + p_off(2 * rg + i, pc + 4)) = hi[i];
+    }
+    if (q.tid < 128) *reinterpret_cast<u32x4*>(Bt + bkk * 32 + bt0 * 2) = bv;
+    __syncthreads();
+    const int sl = q.r16, g = q.g;
+    if (w < 4) {
+      // dT_p[rows][t] += P[rows][chunk] . B_p[chunk][t]; wave w: m-blocks 4w .. 4w+3.
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kr = ks * 32 + 8 * g + (sl >> 2);
+        u32x2 b0 = tr16(lds_addr(Bt + kr * 32 + 8 * (sl & 3)));
+        u32x2 b1 = tr16(lds_addr(Bt + (kr + 4) * 32 + 8 * (sl & 3)));
+        lgkm_tie0(b0, b1);
+        PFrag<bf16> bf;
+        bf.v = (u32x4){b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const PFrag<bf16> af = p_frag<bf16>(Pr, (4 * w + i) * 16 + q.r16, ks, q.g);
+          if (p == 0) dT[0][i] = p_mma(dT[0][i], af, bf);
+          else if (p == 1) dT[1][i] = p_mma(dT[1][i], af, bf);
+          else dT[2][i] = p_mma(dT[2][i], af, bf);
+        }
+      }
+    } else {
+      // dB_p[col][t] = P[rows][col]^T . (s_p T_p)[rows][t]; wave w: columns
+      // 16 (w - 4) .. +15.
+      f32x4 db = (f32x4){0.f, 0.f, 0.f, 0.f};
+      const int col = (w - 4) * 16 + 4 * (sl & 3);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int row = kb * 64 + ks * 32 + 8 * g + (sl >> 2);
+          u32x2 a0 = tr16(lds_addr(Pr + p_off(row, col >> 3) + (col & 7) * 2));
+          u32x2 a1 = tr16(lds_addr(Pr + p_off(row + 4, col >> 3) + (col & 7) * 2));
+          lgkm_tie0(a0, a1);
+          PFrag<bf16> af;
+          af.v = (u32x4){a0.x, a0.y, a1.x, a1.y};
+          const PFrag<bf16> bf = p_frag<bf16>(TT + p * TTB + kb * (16 * kPRowBytes), q.r16, ks, q.g);
+          db = p_mma(db, af, bf);
+        }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = (w - 4) * 16 + 4 * q.g + j;
+        const long c = (kk < HW) ? m.base_lo + kk : m.base_hi + (kk - HW);
+        if (c < a.O) a.dB_part[((long)rb * a.O + c) * 16 + q.r16] = db[j];
+      }
+    }
+    __syncthreads();
+  };
+
+  // One chunk in flight while one is processed; the rotation of a q/k chunk
+  // is fetched one chunk ahead.
+  Raw nx;
+  Rot rot;
+  if (ch_beg < ch_end) {
+    fetch(cmap(ch_beg), nx);
+    fetch_rot(cmap(ch_beg), rot);
+  }
+  for (int ch = ch_beg; ch < ch_end; ++ch) {
+    const CMap m = cmap(ch);
+    u32x4 lo[2], hi[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lo[i] = nx.xl[i];
+      hi[i] = nx.xh[i];
+    }
+    if (a.qkv) {
+      if (m.p < 2) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          float vl[VEC], vh[VEC], yl[VEC], yh[VEC];
+          unpack(nx.xl[i], vl);
+          unpack(nx.xh[i], vh);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float c = rot.c[i][e >> 2][e & 3], sv = rot.sn[i][e >> 2][e & 3];
+            yl[e] = vl[e] * c + vh[e] * sv;      // R^T: rotate by -angle
+            yh[e] = vh[e] * c - vl[e] * sv;
+          }
+          lo[i] = pack(yl);
+          hi[i] = pack(yh);
+        }
+      }
+      const long clo = m.base_lo + pc * VEC, chi = m.base_hi + pc * VEC;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const long n = m0 + 2 * rg + i;
+        if (n < a.N) {
+          T* dp = static_cast<T*>(a.dP) + n * a.O;
+          *reinterpret_cast<u32x4*>(dp + clo) = lo[i];
+          *reinterpret_cast<u32x4*>(dp + chi) = hi[i];
+        }
+      }
+    }
+    const u32x4 bv = nx.bv;
+    if (ch + 1 < ch_end) {
+      const CMap mn = cmap(ch + 1);
+      fetch(mn, nx);
+      fetch_rot(mn, rot);
+    }
+    process(m, lo, hi, bv);
+  }
+
+  // dT partial of this column range for the call's adapters (waves 0-3).
+  if (w < 4) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      if (p < a.nadp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const long n = m0 + (4 * w + i) * 16 + 4 * q.g + j;
+            if (n < a.N) a.dT_part[(((long)cr * 3 + p) * a.N + n) * 16 + q.r16] = a.s[p] * dT[p][i][j];
+          }
+  }
 }
 
 // ===========================================================================
