@@ -57,6 +57,9 @@ MLP_CASES = [
     S.MLPConfig("mlp_bf16_dx_runs_ragged", 4200, 4160, 128, 16, 2.0, "swiglu", "bf16"),
     # 17 x 16 dX tiles: the 64-wide last column tile is the second of its run
     S.MLPConfig("mlp_bf16_dx_runs_ragged_tile", 4200, 3904, 128, 16, 2.0, "geglu_tanh", "bf16"),
+    # 40 x 7 dX tiles: the separate dT pass runs 7 K splits of 2 chunks over
+    # the 14 chunks of [dG | dU], one of them across the dG / dU seam
+    S.MLPConfig("mlp_bf16_dt_split_over_seam", 10240, 1792, 448, 16, 2.0, "swiglu", "bf16"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
