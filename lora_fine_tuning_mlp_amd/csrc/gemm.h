@@ -682,16 +682,19 @@ __device__ __forceinline__ void nk_kloop_pp(char* smem, int nkt, const bf16* X, 
     __builtin_amdgcn_sched_barrier(0);
     bar();
     __builtin_amdgcn_sched_barrier(0);
+    // MFMA phase, A fragment outer: eight MFMAs in a row share their A
+    // operand (measured a little faster under the power limit than sharing
+    // the B operand four at a time; each accumulator's sum is unchanged).
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        Frag<bf16> bfr;
-        bfr.v = bv[ks][nb];
+      for (int mb = 0; mb < kMB; ++mb) {
+        Frag<bf16> af;
+        af.v = av[ks][mb];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          Frag<bf16> af;
-          af.v = av[ks][mb];
+        for (int nb = 0; nb < 8; ++nb) {
+          Frag<bf16> bfr;
+          bfr.v = bv[ks][nb];
           acc[mb][nb] = mma(acc[mb][nb], af, bfr);
         }
       }
@@ -790,12 +793,12 @@ __device__ __forceinline__ void kloop2tr_pp(char* smem, int nkt, const bf16* A0,
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        const Frag<bf16> bfr = tr_make(lo[ks][nb], hi[ks][nb]);
+      for (int mb = 0; mb < kMB; ++mb) {
+        Frag<bf16> af;
+        af.v = av[ks][mb];
 #pragma unroll
-        for (int mb = 0; mb < kMB; ++mb) {
-          Frag<bf16> af;
-          af.v = av[ks][mb];
+        for (int nb = 0; nb < 8; ++nb) {
+          const Frag<bf16> bfr = tr_make(lo[ks][nb], hi[ks][nb]);
           acc[mb][nb] = mma(acc[mb][nb], af, bfr);
         }
       }
