@@ -583,6 +583,215 @@ __global__ __launch_bounds__(512, 1) void k_bwd_prologue8(ProArgs a) {
   }
 }
 
+// Direct buffer -> LDS load (gfx950 buffer_load_dwordx4 ... lds): lane l
+// writes 16 bytes at LDS base + 16 l; an offset at or past the resource's
+// end writes zeros and never faults.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, unsigned off, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_wave_base, 16, off, 0, 0,
+                                           0);
+}
+// Barrier after this wave's LDS traffic has completed, as one asm statement
+// (the compiler adds no wait for the direct loads still in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The bf16 backward prologue over a token-major P (dY of the MLP down
+// projection or of one LoRA linear) as a ring of LDS stages filled by direct
+// buffer loads, NS - 1 chunks in flight.  The waves split the work:
+//   waves 0-3  issue every direct load (the 256 x 64 P tile of a chunk and
+//              its B_p rows), wait for them, and form dT = P . B_p;
+//   waves 4-7  build (s_p T_p)^T once and form the dB partials.
+// Same arguments, grid and results (up to the order of the dT sums) as
+// k_bwd_prologue8 with qkv = 0.  (The QKV prologue also un-rotates and stores
+// dP; in this form each of its chunks waited for its own stores before the
+// next rotation values could be used, and it ran slower than k_bwd_prologue8.)
+constexpr int kPrStage = 32768 + 2048;             // P tile [256][128 B] + B_p chunk [64 kk][16 t]
+template <int NS>
+constexpr int pr_lds_bytes() { return NS * kPrStage + 3 * 8192; }
+
+template <class T, int NS>
+__global__ __launch_bounds__(512, 1) void k_bwd_prologue_ring(ProArgs a) {
+  static_assert(sizeof(T) == 2, "bf16");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  constexpr int HW = 32, NKB = kBM / 64, TTB = 8192, LPC = 9;   // LPC: direct loads per chunk and loader wave
+  __shared__ __align__(16) char smem[pr_lds_bytes<NS>()];
+  const WaveId q = wave_id();
+  const int w = __builtin_amdgcn_readfirstlane(q.w);
+  const int L = q.lane;
+  const int rb = blockIdx.x, cr = blockIdx.y;
+  const long m0 = (long)rb * kBM;
+  char* TT = smem + NS * kPrStage;
+  const int cb = cr * a.CPC, ce = min(a.NCH, (cr + 1) * a.CPC);
+  const int nch = max(0, ce - cb);
+  // Adapter of chunk ch by column range (ranges are whole chunks).
+  auto adapter = [&](int ch) {
+    const int base = ch * 64;
+    return (a.nadp > 1 && base >= a.off[1]) ? ((a.nadp > 2 && base >= a.off[2]) ? 2 : 1) : 0;
+  };
+
+  // (s_p T_p)^T for this row block, once (waves 4-7: one row each), before
+  // any direct load is in flight.
+  if (w >= 4) {
+    const int row = q.tid - 256;
+    const long n = m0 + row;
+    for (int p = 0; p < a.nadp; ++p) {
+      float v[16];
+      load_rank<float, 16>(a.Tp[p] + min(n, a.N - 1) * a.r, 1, 0, a.r, v);
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        char* dst = TT + p * TTB + (row / 64) * (16 * kPRowBytes) + p_off(t, (row % 64) / 8) + (row % 8) * 2;
+        *reinterpret_cast<T*>(dst) = from_f<T>(n < a.N ? a.s[p] * v[t] : 0.f);
+      }
+    }
+  }
+
+  // Loader waves: rows 8 (w + 4 it) + L / 8 of the tile, 16-byte piece lc
+  // (the LDS rows are 128 bytes, pieces XOR-swizzled with row & 7).
+  const int lc = (L & 7) ^ (L >> 3);
+  int lrow[8];                                     // n * O of a live row, -1 past N
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const long n = m0 + 8 * ((w & 3) + 4 * it) + (L >> 3);
+    lrow[it] = n < a.N ? (int)(n * a.O) : -1;
+  }
+  const __amdgpu_buffer_rsrc_t prs = buf_rsrc(a.P, (unsigned)(a.N * a.O * 2));
+  auto issue = [&](int c, char* S) {
+    const int ch = cb + c, p = adapter(ch), base = ch * 64;
+    {
+      // B_p chunk: lanes < 32 of the loader waves, rank entries bt0 .. bt0+7 of chunk column bkk.
+      const int tid = w * 32 + L, bkk = tid >> 1, bt0 = (tid & 1) * 8;
+      const int col = base + bkk;
+      const int rows = a.off[p + 1] - a.off[p];
+      const __amdgpu_buffer_rsrc_t rs = buf_rsrc(a.Bp[p], (unsigned)(rows * a.r * 2));
+      const bool ok = col < a.off[p + 1] && bt0 < a.r;
+      if (L < 32) buf2lds16(rs, ok ? (unsigned)(((col - a.off[p]) * a.r + bt0) * 2) : kBufOut, S + 32768 + w * 512);
+    }
+    const int col = base + lc * 8;
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const bool ok = lrow[it] >= 0 && col < a.O;
+      buf2lds16(prs, ok ? (unsigned)((lrow[it] + col) * 2) : kBufOut, S + ((w & 3) + 4 * it) * 1024);
+    }
+  };
+
+  f32x4 dT[3][4];
+#pragma unroll
+  for (int p = 0; p < 3; ++p)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dT[p][i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  if (w < 4) {
+#pragma unroll
+    for (int j = 0; j < NS - 1; ++j)
+      if (j < nch) issue(j, smem + j * kPrStage);
+  }
+  int st = 0;                                      // stage of chunk c
+  for (int c = 0; c < nch; ++c) {
+    char* const S = smem + st * kPrStage;
+    if (w < 4) {
+      // Chunk c has landed once at most the later chunks' loads are outstanding.
+      const int later = min(nch - 1 - c, NS - 2);
+      if constexpr (NS >= 4) {
+        if (later >= 2) vm_wait<2 * LPC>();
+        else if (later == 1) vm_wait<LPC>();
+        else vm_wait<0>();
+      } else if constexpr (NS == 3) {
+        if (later >= 1) vm_wait<LPC>();
+        else vm_wait<0>();
+      } else {
+        vm_wait<0>();
+      }
+    }
+    lds_barrier();
+    // The stage refilled here was read in the previous iteration, before the barrier.
+    const int st_next = (st + NS - 1) % NS;
+    if (w < 4 && c + NS - 1 < nch) issue(c + NS - 1, smem + st_next * kPrStage);
+    const int ch = cb + c, p = adapter(ch), base = ch * 64;
+    const int sl = q.r16, g = q.g;
+    if (w < 4) {
+      // dT_p[rows][t] += P[rows][chunk] . B_p[chunk][t]; wave w: m-blocks 4w .. 4w+3.
+      const char* Bt = S + 32768;
+      u32x2 b0[2], b1[2];
+      u32x4 av[2][4];
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int kr = ks * 32 + 8 * g + (sl >> 2);
+        b0[ks] = tr16(lds_addr(Bt + kr * 32 + 8 * (sl & 3)));
+        b1[ks] = tr16(lds_addr(Bt + (kr + 4) * 32 + 8 * (sl & 3)));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[ks][i] = rd128(S + p_off((4 * w + i) * 16 + sl, ks * 4 + g));
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        lgkm_tie0(b0[ks], b1[ks]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) tie<0>(av[ks][i]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        PFrag<bf16> bf;
+        bf.v = (u32x4){b0[ks].x, b0[ks].y, b1[ks].x, b1[ks].y};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          PFrag<bf16> af;
+          af.v = av[ks][i];
+          if (p == 0) dT[0][i] = p_mma(dT[0][i], af, bf);
+          else if (p == 1) dT[1][i] = p_mma(dT[1][i], af, bf);
+          else dT[2][i] = p_mma(dT[2][i], af, bf);
+        }
+      }
+    } else {
+      // dB_p[col][t] = P[rows][col]^T . (s_p T_p)[rows][t]; wave w: columns
+      // 16 (w - 4) .. +15.
+      f32x4 db = (f32x4){0.f, 0.f, 0.f, 0.f};
+      const int col = (w - 4) * 16 + 4 * (sl & 3);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        u32x2 a0[2], a1[2];
+        u32x4 tv[2];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int row = kb * 64 + ks * 32 + 8 * g + (sl >> 2);
+          a0[ks] = tr16(lds_addr(S + p_off(row, col >> 3) + (col & 7) * 2));
+          a1[ks] = tr16(lds_addr(S + p_off(row + 4, col >> 3) + (col & 7) * 2));
+          tv[ks] = rd128(TT + p * TTB + kb * (16 * kPRowBytes) + p_off(sl, ks * 4 + g));
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          lgkm_tie0(a0[ks], a1[ks]);
+          tie<0>(tv[ks]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          PFrag<bf16> af, bf;
+          af.v = (u32x4){a0[ks].x, a0[ks].y, a1[ks].x, a1[ks].y};
+          bf.v = tv[ks];
+          db = p_mma(db, af, bf);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int cc = base + (w - 4) * 16 + 4 * g + j;
+        if (cc < a.O) a.dB_part[((long)rb * a.O + cc) * 16 + sl] = db[j];
+      }
+    }
+    st = (st + 1 == NS) ? 0 : st + 1;
+  }
+
+  // dT partial of this column range for the call's adapters (waves 0-3).
+  if (w < 4) {
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      if (p < a.nadp)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const long n = m0 + (4 * w + i) * 16 + 4 * q.g + j;
+            if (n < a.N) a.dT_part[(((long)cr * 3 + p) * a.N + n) * 16 + q.r16] = a.s[p] * dT[p][i][j];
+          }
+  }
+}
+
 // ===========================================================================
 // q/k norm backward: dP (token-major [N][O]) from dQ/dK/dV.  For q and k heads
 // g = R^T dQ is pulled back through the per-head RMSNorm,

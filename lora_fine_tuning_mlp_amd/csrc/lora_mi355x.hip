@@ -495,7 +495,10 @@ int launch_prologue(const ProArgs& a, dim3 grid, hipStream_t st) {
     } else {
       buf = buf && a.N * (long)a.O * 2 <= lim;
     }
-    if (buf) return launch(4, k_bwd_prologue8<T>, grid, dim3(512), st, a);
+    if (buf) {
+      if (a.qkv) return launch(4, k_bwd_prologue8<T>, grid, dim3(512), st, a);
+      return launch(4, k_bwd_prologue_ring<T, 3>, grid, dim3(512), st, a);
+    }
   }
   return launch(4, k_bwd_prologue<T>, grid, dim3(kThreads), st, a);
 }
