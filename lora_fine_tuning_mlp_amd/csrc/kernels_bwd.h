@@ -1542,7 +1542,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dx_bwd(MlpDxArgs a) {
 // keeps three chunks in flight in a ring of four LDS stages (direct loads:
 // the token rows in the GEMM's 128-byte layout, the 64 B rows of the chunk
 // as [64 k][16 t]); wave w multiplies rows 32 w .. 32 w + 31.  Partials
-// [KS][3][N][16] (slots 0, 1), summed in a fixed order by k_dt_sum.
+// [KS][3][N][16] (slots 0, 1), summed in a fixed order by k_dt_sum.  A
+// workgroup walks its K range from the top down: k_down_bwd writes each row
+// group's column tiles in ascending order, so the highest columns of a range
+// are the most recently written and the likeliest to be still in the 256 MB
+// MALL; read first, they are read before this pass's own misses evict them.
 struct MlpDtArgs {
   const void* dG; const void* dU;  // [N][i]
   const void* Bg; const void* Bu;  // [i][16]
@@ -1577,8 +1581,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dt(MlpDtArgs a) {
   const int soff = (ci >> 1) * 16 + 8 * (ci & 1);
   auto issue = [&](int c) {
     char* S = smem + (c & (kDtStages - 1)) * kDtStage;
-    const bool up = c >= nk0;
-    const long k = (long)(c - (up ? nk0 : 0)) * 64;
+    const int cid = cb + ce - 1 - c;
+    const bool up = cid >= nk0;
+    const long k = (long)(cid - (up ? nk0 : 0)) * 64;
     const bf16* A = (up ? dU : dG) + k;
 #pragma unroll
     for (int it = 0; it < 4; ++it) g2lds16(A + aoff[it], S + direct_blk(it) * 1024);
@@ -1617,7 +1622,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_mlp_dt(MlpDtArgs a) {
       for (int mb = 0; mb < 2; ++mb) tie<0>(av[ks][mb]);
       lgkm_tie0(lo[ks], hi[ks]);
     }
-    const bool up = c >= nk0;
+    const bool up = (cb + ce - 1 - c) >= nk0;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const Frag<bf16> bfr = tr_make(lo[ks], hi[ks]);
