@@ -65,7 +65,8 @@ int ok() {
 // ---- timing ---------------------------------------------------------------
 const char* kNames[] = {"k_gateup_fwd",  "k_linear_fwd", "k_rope_table", "k_qkv_fwd",
                         "k_bwd_prologue", "k_down_bwd",   "k_mlp_dx_bwd", "k_proj_dx_bwd",
-                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd", "k_mlp_dt"};
+                        "k_reduce",       "k_dt_sum",     "k_qk_norm_bwd", "k_mlp_dt",
+                        "k_bwd_prologue_ring"};
 constexpr int kNumNames = sizeof(kNames) / sizeof(kNames[0]);
 
 struct Rec {
@@ -497,7 +498,7 @@ int launch_prologue(const ProArgs& a, dim3 grid, hipStream_t st) {
     }
     if (buf) {
       if (a.qkv) return launch(4, k_bwd_prologue8<T>, grid, dim3(512), st, a);
-      return launch(4, k_bwd_prologue_ring<T, 3>, grid, dim3(512), st, a);
+      return launch(12, k_bwd_prologue_ring<T, 3>, grid, dim3(512), st, a);
     }
   }
   return launch(4, k_bwd_prologue<T>, grid, dim3(kThreads), st, a);

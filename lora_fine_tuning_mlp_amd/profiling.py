@@ -62,7 +62,7 @@ def short_name(name: str) -> str:
 # The library's per-launch recorder names a launch by the step it performs;
 # where a step has more than one kernel variant, the variant's own name (as
 # rocprofv3 reports it) maps to that step's name.
-RECORDER_NAME = {"k_gateup_run": "k_gateup_fwd", "k_bwd_prologue8": "k_bwd_prologue", "k_bwd_prologue_ring": "k_bwd_prologue", "k_mlp_dx_pp": "k_mlp_dx_bwd", "k_linear_run": "k_linear_fwd", "k_qkv_run": "k_qkv_fwd"}
+RECORDER_NAME = {"k_gateup_run": "k_gateup_fwd", "k_bwd_prologue8": "k_bwd_prologue", "k_mlp_dx_pp": "k_mlp_dx_bwd", "k_linear_run": "k_linear_fwd", "k_qkv_run": "k_qkv_fwd"}
 
 
 def base_name(name: str) -> str:
