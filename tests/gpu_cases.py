@@ -60,6 +60,9 @@ MLP_CASES = [
     # 40 x 7 dX tiles: the separate dT pass runs 7 K splits of 2 chunks over
     # the 14 chunks of [dG | dU], one of them across the dG / dU seam
     S.MLPConfig("mlp_bf16_dt_split_over_seam", 10240, 1792, 448, 16, 2.0, "swiglu", "bf16"),
+    # hidden 200 = 3 x 64 + 8: the backward prologue's last 64-column chunk
+    # holds 8 columns; rank 8 fills half of each 16-rank B row load
+    S.MLPConfig("mlp_bf16_ragged_hidden_r8", 333, 200, 384, 8, 2.0, "swiglu", "bf16"),
 ]
 QKV_CASES = [
     S.QKVConfig("qkv_bf16_d64", 2, 300, 384, 8, 2, 64, 8, 2.0, 1.0e4, "bf16"),
@@ -101,6 +104,8 @@ LINEAR_CASES = [
     # with a 64-wide last tile inside a run, or a last run of one tile
     S.LinearConfig("linear_bf16_runs_ragged", 4200, 192, 3904, 16, 2.0, "bf16", bias=True),
     S.LinearConfig("linear_bf16_runs_of_one", 4200, 128, 4160, 8, 2.0, "bf16"),
+    # 200 outputs = 3 x 64 + 8: a ragged last chunk in the backward prologue
+    S.LinearConfig("linear_bf16_ragged_chunk", 333, 256, 200, 16, 2.0, "bf16"),
 ]
 
 
