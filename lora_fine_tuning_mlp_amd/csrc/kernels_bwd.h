@@ -601,9 +601,9 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 //              its B_p rows), wait for them, and form dT = P . B_p;
 //   waves 4-7  build (s_p T_p)^T once and form the dB partials.
 // Same arguments, grid and results (up to the order of the dT sums) as
-// k_bwd_prologue8 with qkv = 0.  (The QKV prologue also un-rotates and stores
-// dP; in this form each of its chunks waited for its own stores before the
-// next rotation values could be used, and it ran slower than k_bwd_prologue8.)
+// k_bwd_prologue8 with qkv = 0.  (The QKV prologue, which also un-rotates and
+// stores dP, stays on k_bwd_prologue8: ring forms of it, with the rotation
+// on either half of the waves, measured slower.)
 constexpr int kPrStage = 32768 + 2048;             // P tile [256][128 B] + B_p chunk [64 kk][16 t]
 template <int NS>
 constexpr int pr_lds_bytes() { return NS * kPrStage + 3 * 8192; }
