@@ -18,6 +18,7 @@ import argparse
 import collections
 import csv
 import hashlib
+import re
 import json
 import os
 
@@ -25,13 +26,21 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "lora_fine_tuning_mlp_amd", "csrc")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed (the
+    sources hold no string literal with a comment marker in it)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources, so stored counter figures can be recognised as
-    stale once a kernel has changed."""
+    """Hash of the HIP sources' code (comments and layout ignored), so stored
+    counter figures can be recognised as stale once a kernel has changed."""
     h = hashlib.sha256()
     for f in sorted(os.listdir(CSRC)):
         if f.endswith((".h", ".hip")):
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+            h.update(_code_only(open(os.path.join(CSRC, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
