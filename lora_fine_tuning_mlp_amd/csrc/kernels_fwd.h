@@ -616,23 +616,48 @@ struct QKVRowLoader {
   }
 };
 
+// The cos / sin rows of a tile's 256 token rows ([256][d/2] fp32 each, cos
+// then sin, 2 KB x d/2 in all) into LDS by direct loads, all issued before
+// the tile's first output store and waited for once: a wave's loads and
+// stores share one completion counter, so a table load issued between the
+// stores of one m-block and the next would also wait for those stores.  Rows
+// past N take row N - 1's position (their outputs are not stored).
+static_assert(2 * kBM * 64 * 4 <= kGemmLds && 2 * kBM * 64 * 4 <= kRunFAOff, "RoPE slab (head_dim 128) in LDS");
+__device__ __forceinline__ void stage_rope_slab(char* slab, const float* cs, const float* sn, long m0, long N, int S,
+                                                int half) {
+  const int w = (int)(threadIdx.x >> 6), L = (int)(threadIdx.x & 63);
+  const int ppr = half >> 2;                       // 16-byte pieces per row
+  const int rpi = 64 / ppr;                        // rows per 1 KB load (4 or 8)
+  const int nins = kBM / rpi;
+  const int lr = L / ppr, lp = L - (L / ppr) * ppr;
+  const int r0 = (int)m0 + lr, rmax = (int)N - 1;  // token rows fit 31 bits
+  for (int i = w; i < nins; i += 8) {
+    const int e = (min(r0 + i * rpi, rmax) % S) * half + lp * 4;
+    g2lds16(cs + e, slab + i * 1024);
+    g2lds16(sn + e, slab + kBM * half * 4 + i * 1024);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
 // RoPE + split of a QKV tile after its fold (rows m0.., columns n0..): the
 // bias, the optional q/k RMSNorm, the rotation of q and k, and the stores
-// into the [B][heads][S][d] outputs.  qe: the wave id after the K-loop.
+// into the [B][heads][S][d] outputs.  qe: the wave id after the K-loop;
+// slab: the tile's cos / sin rows in LDS (stage_rope_slab).
 template <class T, int LG>
 __device__ __forceinline__ void qkv_rope_store(QKVFwdArgs a, f32x4 (&acc)[kMB][8], long m0, int n0,
-                                               const WaveId& qe) {
+                                               const WaveId& qe, const char* slab) {
   const int O = a.off[3];
   auto proj_of = [&](int o) { return (o < a.off[1]) ? 0 : ((o < a.off[2]) ? 1 : 2); };
   // RoPE + split.  Groups alternate first half / second half of a head, so
   // block b (first half) pairs with block b + cw in the same lane.  Per
-  // m-block the lane first fetches the cos / sin of its four rows (cw
-  // consecutive entries each, one vector load), then rotates and stores.
+  // m-block the lane first reads the cos / sin of its four rows (cw
+  // consecutive entries each, one LDS read), then rotates and stores.
   constexpr int cw = 8 >> LG;
   constexpr int NG = 8 / (2 * cw);                    // head-half pair groups per lane
   const int half = a.d >> 1;
-  const float* __restrict__ cs = a.cs;
-  const float* __restrict__ sn = a.sn;
+  const float* cs = reinterpret_cast<const float*>(slab);
+  const float* sn = cs + kBM * half;
   auto load_cw = [&](const float* ptr, float (&v)[cw]) {
     if constexpr (cw == 4) {
       const f32x4 t = *reinterpret_cast<const f32x4*>(ptr);
@@ -749,17 +774,16 @@ __device__ __forceinline__ void qkv_rope_store(QKVFwdArgs a, f32x4 (&acc)[kMB][8
     float cc[4][NG][cw], ss[4][NG][cw];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const long row = m0 + acc_row(qe, mb, j);
-      const int s = (int)(min(row, a.N - 1) % a.S);
+      const int rl = acc_row(qe, mb, j);            // tile row: slab row
 #pragma unroll
       for (int gi = 0; gi < NG; ++gi) {
         const int o1 = n0 + qe.wn * 128 + perm_col(LG, qe.r16, 2 * cw * gi);
-        // Every lane loads (clamped to a valid entry); the values are used
+        // Every lane reads (clamped to a valid entry); the values are used
         // only for rows < N, columns < O of q and k, as below.
         const int o1c = min(o1, O - 1);
         const int jj = min((o1c - a.off[proj_of(o1c)]) % a.d, half - cw);
-        load_cw(cs + (long)s * half + jj, cc[j][gi]);
-        load_cw(sn + (long)s * half + jj, ss[j][gi]);
+        load_cw(cs + rl * half + jj, cc[j][gi]);
+        load_cw(sn + rl * half + jj, ss[j][gi]);
       }
     }
 #pragma unroll
@@ -934,9 +958,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_fwd(QKVFwdArgs a) {
     const int p = min(pfirst + sl, 2);
     fs[sl] = (p == 0) ? a.s[0] : ((p == 1) ? a.s[1] : a.s[2]);
   }
-  fold<T>(smem, acc, nslot, fs, fb);
+  fold<T>(smem, acc, nslot, fs, fb);                // (ends with a barrier: LDS free)
 
-  qkv_rope_store<T, LG>(a, acc, m0, n0, qe);
+  stage_rope_slab(smem, a.cs, a.sn, m0, a.N, a.S, a.d >> 1);
+  qkv_rope_store<T, LG>(a, acc, m0, n0, qe, smem);
 }
 
 // B rows of a head_dim-128 QKV tile inside one projection p for
@@ -1024,7 +1049,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_qkv_run(QKVFwdArgs a) {
       load_rank<bf16, 8>(src, 1, t0, a.r, v);
     };
     fold_run(FA, smem + kRunFBOff, acc, fb);
-    qkv_rope_store<bf16, LG>(a, acc, m0, n0, qe);
+    // The slab covers the stages, the side products and the fold B tile
+    // (not the run's fold A operand): after every wave's fold reads, and
+    // read by all before the next tile's loads refill stage 0.
+    __syncthreads();
+    stage_rope_slab(smem, a.cs, a.sn, m0, a.N, a.S, a.d >> 1);
+    qkv_rope_store<bf16, LG>(a, acc, m0, n0, qe, smem);
+    __syncthreads();
   };
 
   {
