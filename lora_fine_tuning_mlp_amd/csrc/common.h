@@ -135,6 +135,23 @@ __device__ __forceinline__ void gstore(T* p, const float (&v)[NV], int n, bool v
     if (e < n) p[e] = from_f<T>(v[e]);
 }
 
+// gstore with non-temporal vector stores: for outputs no kernel of the same
+// call reads again, so they displace less of the L2 and MALL contents that
+// the next kernel does read.
+template <class T, int NV>
+__device__ __forceinline__ void gstore_nt(T* p, const float (&v)[NV], int n, bool vec) {
+  if constexpr (sizeof(T) == 2 && NV == 4) {
+    if (vec && n == NV) {
+      u32x2 c;
+      c.x = pack_bf2(v[0], v[1]);
+      c.y = pack_bf2(v[2], v[3]);
+      __builtin_nontemporal_store(c, reinterpret_cast<u32x2*>(p));
+      return;
+    }
+  }
+  gstore<T, NV>(p, v, n, vec);
+}
+
 // ---- MFMA fragments ----------------------------------------------------------
 // Main-loop fragment: one 16-byte chunk (8 bf16 or 4 fp32 K slots per lane).
 template <class T> struct Frag { u32x4 v; };

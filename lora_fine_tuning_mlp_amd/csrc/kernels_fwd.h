@@ -133,8 +133,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_fwd(GateUpArgs a) {
         hv[e] = act_fwd<ACT>(gv[e]) * uv[e];
       }
       const long off = row * a.i + jj;
-      gstore<T, 4>(Go + off, gv, nvalid, a.vecO);
-      gstore<T, 4>(Uo + off, uv, nvalid, a.vecO);
+      gstore_nt<T, 4>(Go + off, gv, nvalid, a.vecO);     // G, U: read again only by the backward
+      gstore_nt<T, 4>(Uo + off, uv, nvalid, a.vecO);
       gstore<T, 4>(Ho + off, hv, nvalid, a.vecO);
     }
 }
@@ -233,8 +233,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_gateup_run(GateUpArgs a) {
           hv[e] = act_fwd<ACT>(gv[e]) * uv[e];
         }
         const long off = row * a.i + jj;
-        gstore<bf16, 4>(Go + off, gv, nvalid, a.vecO);
-        gstore<bf16, 4>(Uo + off, uv, nvalid, a.vecO);
+        gstore_nt<bf16, 4>(Go + off, gv, nvalid, a.vecO);   // G, U: read again only by the backward
+        gstore_nt<bf16, 4>(Uo + off, uv, nvalid, a.vecO);
         gstore<bf16, 4>(Ho + off, hv, nvalid, a.vecO);
       }
   };
